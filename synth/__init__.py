@@ -1,0 +1,243 @@
+"""Seeded synthetic inputs for the sparse MoE FFN layer.
+
+This module only draws random numbers and stores them in the layer's input
+formats (fp32, bf16, MXFP4).  It holds none of the layer's arithmetic: it is
+the one module the oracle side and the HIP side share, so both see the same
+bytes.
+
+Workloads (the shapes of the serving deployments the pages discuss: decode
+batches of at most 8 rows -- "第 9 章 prefill：最大的瓶颈" §9.5 and §9.8 --
+and 8192-token prefill chunks -- the same chapter, §9.8):
+
+  c0  tiny fp32:  T=4, H=256, E=8, top-2, I=128
+  c1  decode T=1 bf16:  H=2048, E=128, top-8, I=768
+  c2  decode T=8 bf16, router bias ~ N(0, 0.5) so tokens share experts
+  c3  prefill T=8192 bf16, Zipf(1) expert popularity through the router bias
+  c4  MXFP4 experts (E2M1, 32-element blocks, E8M0 scales), bf16 activations:
+      H=4096, E=256, top-8, I=1024, at T=1, T=8 and T=4096
+
+Distributions: x ~ N(0,1); router W ~ N(0, 0.02); expert W ~ N(0, 1/sqrt(fan_in))
+with fan_in = H for gate/up and I for down (the second parameter is the
+standard deviation).  Draws are fp64 from numpy's PCG64, one independent
+stream per (seed, tensor, expert or batch index), then rounded to fp32 (RNE)
+and, for bf16 tensors, to bf16 (RNE); MXFP4 tensors are quantised from the
+fp32 draws (OCP MX: shared scale 2^(floor(log2 amax) - 2), elements rounded
+to nearest-even on the E2M1 grid, saturating at 6).  The stored bytes are the
+truth for both sides.
+"""
+from __future__ import annotations
+
+import math
+import os
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field
+from typing import Dict, Optional
+
+import numpy as np
+
+# tensor tags of the independent PCG64 streams
+_TAGS = {"x": 1, "wr": 2, "bias": 3, "wg": 4, "wu": 5, "wd": 6, "perm": 7}
+
+# Zipf temperature of the c3 router bias b[e] = beta * ln(p_e), p_e ~ rank_e^-1.
+# beta = 1 is the plain reading of "Zipf(s=1.0)"; at seed 0 it leaves no expert
+# empty, so beta is raised in 0.05 steps until one is (recorded, with the
+# histogram, by tests/golden/make_zipf_beta.py in tests/golden/zipf_beta.json).
+ZIPF_BETA = 1.05
+
+
+@dataclass(frozen=True)
+class Shape:
+    T: int
+    H: int
+    E: int
+    K: int
+    I: int
+    act: str          # "f32" | "bf16"
+    w: str            # "f32" | "bf16" | "mxfp4"
+    bias: str = "none"  # "none" | "normal" | "zipf"
+    renorm: bool = True
+
+
+CONFIGS: Dict[str, Shape] = {
+    "c0_tiny_f32": Shape(4, 256, 8, 2, 128, "f32", "f32"),
+    "c1_decode1_bf16": Shape(1, 2048, 128, 8, 768, "bf16", "bf16"),
+    "c2_decode8_bf16": Shape(8, 2048, 128, 8, 768, "bf16", "bf16", bias="normal"),
+    "c3_prefill8192_bf16": Shape(8192, 2048, 128, 8, 768, "bf16", "bf16", bias="zipf"),
+    "c4_mxfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "mxfp4"),
+    "c4_mxfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "mxfp4"),
+    "c4_mxfp4_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "mxfp4"),
+}
+
+
+def _rng(seed: int, tag: str, sub: int = 0) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([seed, _TAGS[tag], sub])))
+
+
+def normal(seed: int, tag: str, shape, sigma: float, sub: int = 0) -> np.ndarray:
+    """fp64 N(0, sigma) draws of one stream."""
+    return _rng(seed, tag, sub).standard_normal(shape) * sigma
+
+
+# ---- storage formats ---------------------------------------------------------
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 to bf16 (nearest, ties to even); returns the uint16 bit patterns."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# E2M1 grid magnitudes by code 0..7
+_E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float64)
+
+
+def _e2m1_code_rne(m: np.ndarray) -> np.ndarray:
+    """Magnitude (already divided by the block scale, >= 0) -> nearest E2M1 code, ties to the
+    even code, saturating at 6 (code 7)."""
+    m = np.minimum(m, 6.0)
+    # midpoints between consecutive grid values; at a midpoint choose the even code
+    lo = np.searchsorted(_E2M1_GRID, m, side="right") - 1          # grid[lo] <= m
+    lo = np.clip(lo, 0, 7)
+    hi = np.minimum(lo + 1, 7)
+    d_lo = m - _E2M1_GRID[lo]
+    d_hi = _E2M1_GRID[hi] - m
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
+    return np.where(pick_hi, hi, lo).astype(np.uint8)
+
+
+def mxfp4_quantize(w: np.ndarray):
+    """Quantise fp32 rows [R, C] (C % 32 == 0) to MXFP4 along C.
+
+    Returns (codes [R, C/2] uint8 with the even element in the low nibble,
+    scales [R, C/32] uint8 E8M0).  Block scale X = 2^(floor(log2 amax) - 2); an
+    all-zero block gets scale code 0 and zero codes.
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, C = w.shape
+    assert C % 32 == 0
+    blk = w.reshape(R, C // 32, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=2)
+    safe = np.where(amax > 0, amax, 1.0)
+    e = np.floor(np.log2(safe)).astype(np.int64) - 2
+    # guard floor(log2) against rounding at exact powers of two
+    e = np.where(np.ldexp(1.0, e + 2) > safe, e - 1, e)
+    e = np.where(np.ldexp(1.0, e + 3) <= safe, e + 1, e)
+    scale_code = np.where(amax > 0, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
+    X = np.ldexp(1.0, scale_code.astype(np.int64) - 127)[..., None]
+    mag = np.abs(blk) / X
+    code = _e2m1_code_rne(mag)
+    code = code | np.where(blk < 0, 8, 0).astype(np.uint8)
+    code = np.where(amax[..., None] > 0, code, 0).astype(np.uint8)
+    code = code.reshape(R, C)
+    packed = (code[:, 0::2] & 15) | ((code[:, 1::2] & 15) << 4)
+    return packed.astype(np.uint8), scale_code
+
+
+def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Inverse storage map used by tests on the quantiser: fp64 [R, C]."""
+    R = codes.shape[0]
+    c = np.empty((R, codes.shape[1] * 2), np.uint8)
+    c[:, 0::2] = codes & 15
+    c[:, 1::2] = codes >> 4
+    mag = _E2M1_GRID[c & 7]
+    val = np.where(c & 8, -mag, mag)
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return val * np.repeat(X, 32, axis=1)
+
+
+# ---- tensors of one layer ------------------------------------------------------
+
+@dataclass
+class LayerInputs:
+    shape: Shape
+    x: np.ndarray            # [T,H] float32 or uint16 (bf16 bits)
+    wr: np.ndarray           # [E,H]
+    bias: Optional[np.ndarray]
+    wg: np.ndarray
+    wu: np.ndarray
+    wd: np.ndarray
+    sg: Optional[np.ndarray] = None
+    su: Optional[np.ndarray] = None
+    sd: Optional[np.ndarray] = None
+    meta: dict = field(default_factory=dict)
+
+
+def _store(a64: np.ndarray, fmt: str) -> np.ndarray:
+    a32 = a64.astype(np.float32)
+    if fmt == "f32":
+        return a32
+    if fmt == "bf16":
+        return f32_to_bf16_bits(a32)
+    raise ValueError(fmt)
+
+
+def make_x(shape: Shape, seed: int = 0, batch: int = 0) -> np.ndarray:
+    return _store(normal(seed, "x", (shape.T, shape.H), 1.0, sub=batch), shape.act)
+
+
+def make_bias(shape: Shape, seed: int = 0, beta: Optional[float] = None) -> Optional[np.ndarray]:
+    if shape.bias == "none":
+        return None
+    if shape.bias == "normal":
+        return normal(seed, "bias", (shape.E,), 0.5).astype(np.float32)
+    if shape.bias == "zipf":
+        beta = ZIPF_BETA if beta is None else beta
+        ranks = _rng(seed, "perm").permutation(shape.E) + 1          # a seeded ranking 1..E
+        p = 1.0 / ranks
+        p = p / p.sum()
+        return (beta * np.log(p)).astype(np.float32)
+    raise ValueError(shape.bias)
+
+
+def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigma: float,
+                   threads: int):
+    E = shape.E
+    if shape.w == "mxfp4":
+        codes = np.empty((E, rows, cols // 2), np.uint8)
+        scales = np.empty((E, rows, cols // 32), np.uint8)
+    else:
+        out = np.empty((E, rows, cols), np.float32 if shape.w == "f32" else np.uint16)
+
+    def one(e):
+        a32 = normal(seed, tag, (rows, cols), sigma, sub=e).astype(np.float32)
+        if shape.w == "mxfp4":
+            codes[e], scales[e] = mxfp4_quantize(a32)
+        elif shape.w == "bf16":
+            out[e] = f32_to_bf16_bits(a32)
+        else:
+            out[e] = a32
+
+    if threads > 1 and E > 1:
+        with ThreadPoolExecutor(threads) as ex:
+            list(ex.map(one, range(E)))
+    else:
+        for e in range(E):
+            one(e)
+    if shape.w == "mxfp4":
+        return codes, scales
+    return out, None
+
+
+def make_layer(name_or_shape, seed: int = 0, batch: int = 0, threads: Optional[int] = None,
+               beta: Optional[float] = None, **overrides) -> LayerInputs:
+    """All tensors of one layer.  Expert and router weights depend only on (seed, shape
+    without T); x depends on (seed, batch, T)."""
+    shape = CONFIGS[name_or_shape] if isinstance(name_or_shape, str) else name_or_shape
+    if overrides:
+        shape = Shape(**{**shape.__dict__, **overrides})
+    if threads is None:
+        threads = min(16, os.cpu_count() or 1)
+    H, I = shape.H, shape.I
+    x = make_x(shape, seed, batch)
+    wr = _store(normal(seed, "wr", (shape.E, H), 0.02), shape.act)
+    bias = make_bias(shape, seed, beta)
+    wg, sg = _expert_tensor(shape, seed, "wg", I, H, 1.0 / math.sqrt(H), threads)
+    wu, su = _expert_tensor(shape, seed, "wu", I, H, 1.0 / math.sqrt(H), threads)
+    wd, sd = _expert_tensor(shape, seed, "wd", H, I, 1.0 / math.sqrt(I), threads)
+    meta = dict(seed=seed, batch=batch, zipf_beta=(ZIPF_BETA if beta is None else beta)
+                if shape.bias == "zipf" else None)
+    return LayerInputs(shape, x, wr, bias, wg, wu, wd, sg, su, sd, meta)
