@@ -1,0 +1,163 @@
+/*
+ * moe_router.h -- C ABI of the MI355X (gfx950) sparse Mixture-of-Experts FFN
+ * layer: router top-k softmax, token->expert grouping, grouped SwiGLU expert
+ * FFN and weighted combine, for decode batches of a few tokens and prefill
+ * chunks of thousands.
+ *
+ * The staged calls follow the four stages the fused MoE profiling plan times
+ * separately -- topk, expert kernel, activation, sum ("Decode 吞吐专项实验分析
+ * 报告", section "2026-07-14：解除强制 eager / custom all-reduce 禁用验证",
+ * subsection "下一步 profiling 方向").  moe_forward runs all of them on the
+ * device with no host round trip on the routing result, the per-layer
+ * stream synchronisation that "第 9 章 prefill：最大的瓶颈" §9.9 identifies as
+ * the serial point of its prefill path, and it never drops a token-expert
+ * entry, unlike the fixed 8-entries-per-group kernels of §9.5 there.
+ *
+ * Conventions shared by every call
+ *   - Pointers are device pointers unless stated otherwise; the caller owns
+ *     every buffer, including the workspace.  The library allocates nothing
+ *     and keeps no global state; calls on different workspaces may run
+ *     concurrently.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
+ *     default stream).  No call synchronises or reads device memory on the
+ *     host, except moe_check_device_error, which says so.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     call that returns an error has launched nothing.
+ *   - Layouts are row-major.  Weights are out-major with the contraction
+ *     index contiguous ([N][K]).  MXFP4 stores two E2M1 codes per byte (the
+ *     even element in the low nibble) with one E8M0 scale byte per 32
+ *     consecutive contraction elements.
+ *   - Device pointers must be 16-byte aligned.
+ *   - The workspace must be zero-filled before its first use.  Every call
+ *     leaves its control words zero again; only the sticky device error
+ *     word (cleared by moe_check_device_error) can remain set.
+ */
+#ifndef MOE_ROUTER_H
+#define MOE_ROUTER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,  /* null/misaligned pointer, bad size, k>E, ... */
+    MOE_ERR_UNSUPPORTED = -2,  /* legal but not implemented combination       */
+    MOE_ERR_WORKSPACE = -3,    /* workspace smaller than moe_workspace_size   */
+    MOE_ERR_HIP = -4,          /* a HIP launch or runtime call failed          */
+    MOE_ERR_DEVICE = -5        /* moe_check_device_error found a device error  */
+};
+
+/* element formats */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 };
+
+/* expert-FFN kernel family; AUTO picks DECODE for T <= 8 and GROUPED above */
+enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
+
+/* device error bits reported by moe_check_device_error */
+enum { MOE_DEVERR_BAD_EXPERT_ID = 1, MOE_DEVERR_TIMEOUT = 2 };
+
+typedef struct moe_shape {
+    int32_t num_tokens;    /* T >= 0; T == 0 is a no-op                       */
+    int32_t hidden;        /* H, multiple of 8 (of 32 for MXFP4), <= 8192      */
+    int32_t num_experts;   /* E, 1..1024                                       */
+    int32_t top_k;         /* k, 1..min(E, 32)                                 */
+    int32_t intermediate;  /* I, multiple of 8 (of 32 for MXFP4), <= 8192      */
+    int32_t renormalize;   /* nonzero: kept gate weights rescaled to sum 1     */
+    int32_t act_dtype;     /* x, router weight, y: MOE_F32 or MOE_BF16         */
+    int32_t weight_dtype;  /* experts: MOE_F32 (with F32 acts), MOE_BF16 or
+                              MOE_MXFP4 (with BF16 acts)                       */
+    int32_t path;          /* MOE_PATH_*                                        */
+} moe_shape;
+
+typedef struct moe_expert_weights {
+    const void *w_gate;    /* [E][I][H]   (MXFP4: [E][I][H/2] bytes)           */
+    const void *w_up;      /* [E][I][H]                                        */
+    const void *w_down;    /* [E][H][I]   (MXFP4: [E][H][I/2] bytes)           */
+    const uint8_t *s_gate; /* MXFP4 only: E8M0 scales [E][I][H/32]             */
+    const uint8_t *s_up;   /* [E][I][H/32]                                     */
+    const uint8_t *s_down; /* [E][H][I/32]                                     */
+} moe_expert_weights;
+
+/* Bytes of workspace every call below needs for `shape` (0 on bad shape). */
+size_t moe_workspace_size(const moe_shape *shape);
+
+/*
+ * Router gate + top-k ("gate" and "topk" stages of the profiling plan).
+ *   s[t,e]  = bias[e] + sum_h x[t,h] * w_router[e,h]          (fp32 accumulate)
+ *   kept    = the k largest s[t,.] by (score descending, expert id ascending)
+ *   topk_w  = softmax over all E of s[t,.], taken at the kept experts and,
+ *             when renormalize is set, divided by their sum
+ * x [T][H] and w_router [E][H] in act_dtype; bias [E] fp32 or NULL (zero).
+ * Outputs: topk_ids [T][k] int32 in ascending expert id, topk_w [T][k] fp32
+ * in the same order.
+ */
+moe_status moe_router_topk(const moe_shape *shape, const void *x, const void *w_router,
+                           const float *bias, int32_t *topk_ids, float *topk_w,
+                           void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Token->expert grouping on the device ("第 9 章" §9.9: the fused path groups
+ * by expert on the GPU instead of returning to the host every layer).
+ * Slot t*k+j is token t's j-th kept expert.  Outputs:
+ *   expert_offsets [E+1]: exclusive prefix of per-expert slot counts
+ *   sorted_slots [T*k]  : slots ordered by expert, ascending slot inside each
+ *                         expert (stable)
+ *   slot_pos [T*k]      : inverse map, sorted_slots[slot_pos[s]] == s
+ * An id outside [0, E) sets MOE_DEVERR_BAD_EXPERT_ID in the workspace error
+ * word; the slot is then left out of every group (offsets[E] < T*k) and
+ * nothing is written out of bounds.
+ */
+moe_status moe_group_tokens(const moe_shape *shape, const int32_t *topk_ids,
+                            int32_t *expert_offsets, int32_t *sorted_slots, int32_t *slot_pos,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Expert FFN ("expert kernel" and "activation" stages) for every grouped slot:
+ *   expert_out[p][n] = sum_i Wd[e][n][i] * a[i],
+ *   a[i] = silu(g[i]) * u[i], g = Wg[e] x_t, u = Wu[e] x_t, silu(z) = z/(1+e^-z)
+ * for p in [expert_offsets[e], expert_offsets[e+1]) and token t =
+ * sorted_slots[p] / k.  expert_out is [T*k][H] fp32 in sorted order.  With
+ * bf16/MXFP4 weights a is rounded to bf16 before the down projection.
+ */
+moe_status moe_expert_ffn(const moe_shape *shape, const void *x, const moe_expert_weights *w,
+                          const int32_t *expert_offsets, const int32_t *sorted_slots,
+                          float *expert_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Weighted combine ("sum" stage):
+ *   y[t][n] = sum_{j ascending} topk_w[t][j] * expert_out[slot_pos[t*k+j]][n]
+ * accumulated in fp32 and stored once in act_dtype (round to nearest even).
+ */
+moe_status moe_combine(const moe_shape *shape, const float *expert_out, const float *topk_w,
+                       const int32_t *slot_pos, void *y, void *stream);
+
+/*
+ * The whole layer (all stages above) on the device.  y [T][H] in act_dtype.
+ * topk_ids_out / topk_w_out may be NULL; when given they receive the
+ * routing exactly as moe_router_topk would.
+ */
+moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_router,
+                       const float *bias, const moe_expert_weights *w, void *y,
+                       int32_t *topk_ids_out, float *topk_w_out,
+                       void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Synchronises `stream`, reads the workspace's device error word into
+ * *err_bits (host pointer, MOE_DEVERR_* bits), clears it, and returns
+ * MOE_ERR_DEVICE when it was nonzero.
+ */
+moe_status moe_check_device_error(void *ws, int32_t *err_bits, void *stream);
+
+/* Static text for a status code. */
+const char *moe_status_string(moe_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_ROUTER_H */

@@ -1,0 +1,206 @@
+// moe_api.hip -- the C ABI (include/moe_router.h): host-side validation,
+// workspace layout and the launch sequence of every entry point.  Nothing
+// here touches device memory from the host or synchronises, except
+// moe_check_device_error.
+#include <algorithm>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int MAX_E = 1024;
+constexpr int MAX_K = 32;
+constexpr int MAX_DIM = 8192;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int weight_epc(int wdt) { return wdt == MOE_F32 ? 4 : wdt == MOE_BF16 ? 8 : 32; }
+
+// shape checks shared by all calls
+moe_status check_shape(const moe_shape *s) {
+    if (!s) return MOE_ERR_INVALID_ARG;
+    if (s->num_tokens < 0 || s->hidden <= 0 || s->intermediate <= 0 || s->num_experts <= 0) return MOE_ERR_INVALID_ARG;
+    if (s->top_k < 1 || s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
+    if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+    if (s->weight_dtype != MOE_F32 && s->weight_dtype != MOE_BF16 && s->weight_dtype != MOE_MXFP4)
+        return MOE_ERR_INVALID_ARG;
+    if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_GROUPED) return MOE_ERR_INVALID_ARG;
+    const int epc = weight_epc(s->weight_dtype);
+    if (s->hidden % 8 || s->intermediate % 8) return MOE_ERR_INVALID_ARG;
+    if (s->hidden % epc || s->intermediate % epc) return MOE_ERR_INVALID_ARG;
+    // supported element-format pairs
+    const bool ok_pair = (s->act_dtype == MOE_F32 && s->weight_dtype == MOE_F32) ||
+                         (s->act_dtype == MOE_BF16 && s->weight_dtype != MOE_F32);
+    if (!ok_pair) return MOE_ERR_UNSUPPORTED;
+    if (s->num_experts > MAX_E || s->top_k > MAX_K) return MOE_ERR_UNSUPPORTED;
+    if (s->hidden > MAX_DIM || s->intermediate > MAX_DIM) return MOE_ERR_UNSUPPORTED;
+    // fp32 rows: at most 16 chunks per lane
+    if (s->weight_dtype == MOE_F32 && (s->hidden > 4096 || s->intermediate > 4096)) return MOE_ERR_UNSUPPORTED;
+    if ((size_t)s->num_tokens * (size_t)s->top_k > (size_t)INT32_MAX / 2) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_shape *s, const void *ws, size_t ws_bytes) {
+    if (!ws || !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < ws_layout(*s).total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
+    if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down)) return MOE_ERR_INVALID_ARG;
+    if (s->weight_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status check_path(const moe_shape *s) {
+    // the grouped MFMA family covers bf16 / MXFP4 weights; fp32 runs on the decode family
+    if (s->path == MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+template <class T>
+T *at(void *ws, size_t off) {
+    return reinterpret_cast<T *>(static_cast<uint8_t *>(ws) + off);
+}
+
+#define MOE_TRY(expr)                                \
+    do {                                             \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+
+#define MOE_CHECK(expr)                  \
+    do {                                 \
+        const moe_status _st = (expr);   \
+        if (_st != MOE_OK) return _st;   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_shape *shape) {
+    if (check_shape(shape) != MOE_OK) return 0;
+    return ws_layout(*shape).total;
+}
+
+moe_status moe_router_topk(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                           int32_t *topk_ids, float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(topk_ids) || !aligned16(topk_w)) return MOE_ERR_INVALID_ARG;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return MOE_ERR_INVALID_ARG;
+    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(*shape);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    MOE_TRY(launch_router_logits(*shape, x, w_router, bias, at<float>(ws, L.logits), st));
+    MOE_TRY(launch_topk(*shape, at<float>(ws, L.logits), topk_ids, topk_w, st));
+    return MOE_OK;
+}
+
+moe_status moe_group_tokens(const moe_shape *shape, const int32_t *topk_ids, int32_t *expert_offsets,
+                            int32_t *sorted_slots, int32_t *slot_pos, void *ws, size_t ws_bytes, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    const bool any = shape->num_tokens > 0;  // slot arrays may be NULL when there are no slots
+    if (!expert_offsets || (any && (!topk_ids || !sorted_slots || !slot_pos))) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(topk_ids) || !aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(slot_pos))
+        return MOE_ERR_INVALID_ARG;
+    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(*shape);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // T == 0 still defines the offsets (all zero)
+    MOE_TRY(launch_group(*shape, topk_ids, expert_offsets, sorted_slots, slot_pos, at<int32_t>(ws, L.active),
+                         at<int32_t>(ws, L.ctrl), st));
+    return MOE_OK;
+}
+
+moe_status moe_expert_ffn(const moe_shape *shape, const void *x, const moe_expert_weights *w,
+                          const int32_t *expert_offsets, const int32_t *sorted_slots, float *expert_out, void *ws,
+                          size_t ws_bytes, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    MOE_CHECK(check_path(shape));
+    if (shape->num_tokens == 0) return MOE_OK;
+    MOE_CHECK(check_weights(shape, w));
+    if (!x || !expert_offsets || !sorted_slots || !expert_out) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(expert_out))
+        return MOE_ERR_INVALID_ARG;
+    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(*shape);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t *active = at<int32_t>(ws, L.active);
+    MOE_TRY(launch_active(*shape, expert_offsets, active, st));
+    MOE_TRY(launch_decode_gateup(*shape, x, *w, expert_offsets, sorted_slots, active, nullptr, at<void>(ws, L.h), st));
+    MOE_TRY(launch_decode_down(*shape, *w, expert_offsets, active, at<void>(ws, L.h), expert_out, st));
+    return MOE_OK;
+}
+
+moe_status moe_combine(const moe_shape *shape, const float *expert_out, const float *topk_w, const int32_t *slot_pos,
+                       void *y, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    if (shape->num_tokens == 0) return MOE_OK;
+    if (!expert_out || !topk_w || !slot_pos || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(expert_out) || !aligned16(topk_w) || !aligned16(slot_pos) || !aligned16(y))
+        return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_combine(*shape, expert_out, topk_w, slot_pos, y, static_cast<hipStream_t>(stream)));
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                       const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    MOE_CHECK(check_path(shape));
+    if (shape->num_tokens == 0) return MOE_OK;
+    MOE_CHECK(check_weights(shape, w));
+    if (!x || !w_router || !y) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(y)) return MOE_ERR_INVALID_ARG;
+    if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)))
+        return MOE_ERR_INVALID_ARG;
+    if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return MOE_ERR_INVALID_ARG;
+    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(*shape);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
+    float *wts = topk_w_out ? topk_w_out : at<float>(ws, L.wts);
+    int32_t *offsets = at<int32_t>(ws, L.offsets), *sorted = at<int32_t>(ws, L.sorted);
+    int32_t *slot_pos = at<int32_t>(ws, L.slot_pos), *active = at<int32_t>(ws, L.active);
+    MOE_TRY(launch_router_logits(*shape, x, w_router, bias, at<float>(ws, L.logits), st));
+    MOE_TRY(launch_topk(*shape, at<float>(ws, L.logits), ids, wts, st));
+    MOE_TRY(launch_group(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.ctrl), st));
+    MOE_TRY(launch_decode_gateup(*shape, x, *w, offsets, sorted, active, nullptr, at<void>(ws, L.h), st));
+    MOE_TRY(launch_decode_down(*shape, *w, offsets, active, at<void>(ws, L.h), at<float>(ws, L.o), st));
+    MOE_TRY(launch_combine(*shape, at<float>(ws, L.o), wts, slot_pos, y, st));
+    return MOE_OK;
+}
+
+moe_status moe_check_device_error(void *ws, int32_t *err_bits, void *stream) {
+    if (!ws || !aligned16(ws) || !err_bits) return MOE_ERR_INVALID_ARG;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    int32_t v = 0;
+    MOE_TRY(hipStreamSynchronize(st));
+    MOE_TRY(hipMemcpy(&v, ws, sizeof v, hipMemcpyDeviceToHost));
+    *err_bits = v;
+    if (v != 0) {
+        const int32_t zero = 0;
+        MOE_TRY(hipMemcpy(ws, &zero, sizeof zero, hipMemcpyHostToDevice));
+        return MOE_ERR_DEVICE;
+    }
+    return MOE_OK;
+}
+
+const char *moe_status_string(moe_status status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported shape or format combination";
+        case MOE_ERR_WORKSPACE: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP runtime error";
+        case MOE_ERR_DEVICE: return "device-side error reported";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

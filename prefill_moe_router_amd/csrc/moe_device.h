@@ -1,0 +1,127 @@
+// moe_device.h -- device-side helpers shared by the gfx950 kernels: element
+// formats (fp32, bf16, MXFP4), 16-byte chunk dot products, wave64 reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+
+constexpr int WAVE = 64;
+
+// ---- scalar conversions --------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+}
+
+// lo*lo' + hi*hi' + c on packed bf16 pairs, fp32 accumulate (v_dot2_f32_bf16)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// E8M0 scale code -> fp32 multiplier 2^(code-127) (code 0 maps to 0, 255 to inf)
+__device__ __forceinline__ float e8m0_to_f32(uint32_t code) { return __uint_as_float(code << 23); }
+
+// two E2M1 codes of byte `sel` of `packed` (low nibble first) times `scale`, as bf16x2
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t packed, float scale) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, SEL));
+}
+
+// silu(g) * u
+__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// ---- wave64 reductions -----------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
+    return v;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// ---- element formats -------------------------------------------------------------
+// A "chunk" is 16 bytes of a weight row: 4 fp32, 8 bf16 or 32 MXFP4 codes (one
+// scale block).  Dot products are taken chunk by chunk against the matching
+// activation elements.
+
+struct FmtF32 {  // fp32 weights with fp32 activations
+    static constexpr int EPC = 4;          // elements per 16-byte weight chunk
+    static constexpr int XB = 16;          // activation bytes per chunk
+    static constexpr bool SCALED = false;
+};
+struct FmtBF16 {  // bf16 weights with bf16 activations
+    static constexpr int EPC = 8;
+    static constexpr int XB = 16;
+    static constexpr bool SCALED = false;
+};
+struct FmtMX4 {  // MXFP4 weights with bf16 activations
+    static constexpr int EPC = 32;
+    static constexpr int XB = 64;
+    static constexpr bool SCALED = true;
+};
+
+// partial dot of one weight chunk with the activation chunk at xp (XB bytes)
+template <class F>
+__device__ __forceinline__ float chunk_dot(const uint4 &w, uint32_t scale_code, const uint8_t *xp, float acc);
+
+template <>
+__device__ __forceinline__ float chunk_dot<FmtF32>(const uint4 &w, uint32_t, const uint8_t *xp, float acc) {
+    const float4 xv = *reinterpret_cast<const float4 *>(xp);
+    acc = fmaf(__uint_as_float(w.x), xv.x, acc);
+    acc = fmaf(__uint_as_float(w.y), xv.y, acc);
+    acc = fmaf(__uint_as_float(w.z), xv.z, acc);
+    acc = fmaf(__uint_as_float(w.w), xv.w, acc);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<FmtBF16>(const uint4 &w, uint32_t, const uint8_t *xp, float acc) {
+    const uint4 xv = *reinterpret_cast<const uint4 *>(xp);
+    acc = dot2_bf16(w.x, xv.x, acc);
+    acc = dot2_bf16(w.y, xv.y, acc);
+    acc = dot2_bf16(w.z, xv.z, acc);
+    acc = dot2_bf16(w.w, xv.w, acc);
+    return acc;
+}
+
+__device__ __forceinline__ float mx4_word_dot(uint32_t codes, float s, const uint4 &xv, float acc) {
+    acc = dot2_bf16(fp4x2_to_bf16x2<0>(codes, s), xv.x, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<1>(codes, s), xv.y, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<2>(codes, s), xv.z, acc);
+    acc = dot2_bf16(fp4x2_to_bf16x2<3>(codes, s), xv.w, acc);
+    return acc;
+}
+
+template <>
+__device__ __forceinline__ float chunk_dot<FmtMX4>(const uint4 &w, uint32_t scale_code, const uint8_t *xp, float acc) {
+    const float s = e8m0_to_f32(scale_code);
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(xp);
+    acc = mx4_word_dot(w.x, s, x4[0], acc);
+    acc = mx4_word_dot(w.y, s, x4[1], acc);
+    acc = mx4_word_dot(w.z, s, x4[2], acc);
+    acc = mx4_word_dot(w.w, s, x4[3], acc);
+    return acc;
+}
+
+}  // namespace moe

@@ -1,0 +1,70 @@
+// moe_internal.h -- host-side plumbing shared by the library's translation
+// units: workspace layout and the kernel launchers each .hip file exports.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_router.h"
+
+namespace moe {
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
+
+// Byte offsets of the regions of one workspace.  Region 0 holds the control
+// words: [0] the sticky device error word, the rest zero between calls.
+struct WsLayout {
+    size_t ctrl, logits, ids, wts, offsets, sorted, slot_pos, active, h, o, total;
+};
+
+inline WsLayout ws_layout(const moe_shape &s) {
+    const size_t T = (size_t)s.num_tokens, E = (size_t)s.num_experts, K = (size_t)s.top_k;
+    const size_t H = (size_t)s.hidden, I = (size_t)s.intermediate, P = T * K;
+    WsLayout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        size_t at = off;
+        off = align_up(off + bytes, 256);
+        return at;
+    };
+    L.ctrl = take(256);
+    L.logits = take(T * E * 4);
+    L.ids = take(P * 4);
+    L.wts = take(P * 4);
+    L.offsets = take((E + 1) * 4);
+    L.sorted = take(P * 4);
+    L.slot_pos = take(P * 4);
+    L.active = take((E + 1) * 4);
+    L.h = take(P * I * act_bytes(s.act_dtype));
+    L.o = take(P * H * 4);
+    L.total = off;
+    return L;
+}
+
+// ---- launchers (each returns the launch's hipError_t) ----------------------------
+
+// s[t,e] = bias[e] + x[t,:].w_router[e,:]  -> logits [T][E] fp32
+hipError_t launch_router_logits(const moe_shape &s, const void *x, const void *wr, const float *bias,
+                                float *logits, hipStream_t st);
+// top-k + softmax (+ renorm) over logits rows -> ids [T][k] ascending, w [T][k]
+hipError_t launch_topk(const moe_shape &s, const float *logits, int32_t *ids, float *w, hipStream_t st);
+// stable grouping; active = [count, expert ids with a nonempty group ascending]
+hipError_t launch_group(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted,
+                        int32_t *slot_pos, int32_t *active, int32_t *err, hipStream_t st);
+// active = [count, nonempty experts ascending] from existing offsets
+hipError_t launch_active(const moe_shape &s, const int32_t *offsets, int32_t *active, hipStream_t st);
+// h[p][i] = (wts ? wts[slot] : 1) * silu(Wg[e,i].x_t) * (Wu[e,i].x_t), act dtype, sorted order
+hipError_t launch_decode_gateup(const moe_shape &s, const void *x, const moe_expert_weights &w,
+                                const int32_t *offsets, const int32_t *sorted, const int32_t *active,
+                                const float *wts, void *h, hipStream_t st);
+// o[p][n] = Wd[e,n,:].h[p,:]  fp32, sorted order
+hipError_t launch_decode_down(const moe_shape &s, const moe_expert_weights &w, const int32_t *offsets,
+                              const int32_t *active, const void *h, float *o, hipStream_t st);
+// y[t][n] = sum_j w[t,j] o[slot_pos[t*k+j]][n]
+hipError_t launch_combine(const moe_shape &s, const float *o, const float *w, const int32_t *slot_pos,
+                          void *y, hipStream_t st);
+
+}  // namespace moe

@@ -96,17 +96,17 @@ _E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float64)
 
 
 def _e2m1_code_rne(m: np.ndarray) -> np.ndarray:
-    """Magnitude (already divided by the block scale, >= 0) -> nearest E2M1 code, ties to the
-    even code, saturating at 6 (code 7)."""
-    m = np.minimum(m, 6.0)
-    # midpoints between consecutive grid values; at a midpoint choose the even code
-    lo = np.searchsorted(_E2M1_GRID, m, side="right") - 1          # grid[lo] <= m
-    lo = np.clip(lo, 0, 7)
-    hi = np.minimum(lo + 1, 7)
-    d_lo = m - _E2M1_GRID[lo]
-    d_hi = _E2M1_GRID[hi] - m
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0) & (hi != lo))
-    return np.where(pick_hi, hi, lo).astype(np.uint8)
+    """Magnitude (already divided by the power-of-two block scale, so exact, >= 0) ->
+    nearest E2M1 code with ties to the even code, saturating at 6 (code 7).
+
+    The grid has step 0.5 on [0, 2), 1 on [2, 4) and 2 on [4, 6]; on each piece the
+    code index is an affine function of m whose parity is the code's, so numpy's
+    round-half-even (rint) gives ties-to-even codes."""
+    m = np.minimum(m, np.float32(6.0))
+    c_lo = np.rint(m * np.float32(2.0))
+    c_mid = np.float32(4.0) + np.rint(m - np.float32(2.0))
+    c_hi = np.float32(6.0) + np.rint((m - np.float32(4.0)) * np.float32(0.5))
+    return np.where(m < 2, c_lo, np.where(m < 4, c_mid, c_hi)).astype(np.uint8)
 
 
 def mxfp4_quantize(w: np.ndarray):
@@ -119,20 +119,16 @@ def mxfp4_quantize(w: np.ndarray):
     w = np.ascontiguousarray(w, dtype=np.float32)
     R, C = w.shape
     assert C % 32 == 0
-    blk = w.reshape(R, C // 32, 32).astype(np.float64)
+    blk = w.reshape(R, C // 32, 32)
     amax = np.abs(blk).max(axis=2)
-    safe = np.where(amax > 0, amax, 1.0)
-    e = np.floor(np.log2(safe)).astype(np.int64) - 2
-    # guard floor(log2) against rounding at exact powers of two
-    e = np.where(np.ldexp(1.0, e + 2) > safe, e - 1, e)
-    e = np.where(np.ldexp(1.0, e + 3) <= safe, e + 1, e)
-    scale_code = np.where(amax > 0, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
-    X = np.ldexp(1.0, scale_code.astype(np.int64) - 127)[..., None]
-    mag = np.abs(blk) / X
-    code = _e2m1_code_rne(mag)
-    code = code | np.where(blk < 0, 8, 0).astype(np.uint8)
-    code = np.where(amax[..., None] > 0, code, 0).astype(np.uint8)
-    code = code.reshape(R, C)
+    _, ex = np.frexp(amax)                   # amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = ex.astype(np.int64) - 1 - 2
+    nz = amax > 0
+    scale_code = np.where(nz, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
+    X = np.ldexp(np.float32(1.0), scale_code.astype(np.int32) - 127).astype(np.float32)[..., None]
+    mag = np.abs(blk) / X                    # exact: X is a power of two
+    code = _e2m1_code_rne(mag) | np.where(blk < 0, np.uint8(8), np.uint8(0))
+    code = np.where(nz[..., None], code, np.uint8(0)).reshape(R, C)
     packed = (code[:, 0::2] & 15) | ((code[:, 1::2] & 15) << 4)
     return packed.astype(np.uint8), scale_code
 

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, sizes workspaces, and rejects bad arguments on the host
+before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import prefill_moe_router_amd as pm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pm.LIB_PATH), reason="libmoe_router.so not built")
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails first
+
+
+def _declared_functions():
+    names = []
+    for f in os.listdir(os.path.join(ROOT, "include")):
+        if f.endswith(".h"):
+            src = open(os.path.join(ROOT, "include", f)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names += re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_functions_exported():
+    names = _declared_functions()
+    assert set(names) == set(pm.EXPORTS), names
+    L = pm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _shape(**kw):
+    base = dict(num_tokens=4, hidden=2048, num_experts=128, top_k=8, intermediate=768)
+    base.update(kw)
+    return pm.LayerShape(**base)
+
+
+def test_workspace_size_grows_with_tokens():
+    a = pm.workspace_size(_shape(num_tokens=1))
+    b = pm.workspace_size(_shape(num_tokens=8192))
+    assert 0 < a < b
+    assert a % 256 == 0 and b % 256 == 0
+
+
+@pytest.mark.parametrize("kw", [dict(top_k=0), dict(top_k=129), dict(num_tokens=-1), dict(hidden=100),
+                                dict(intermediate=12), dict(act_dtype=7), dict(weight_dtype=5),
+                                dict(weight_dtype=pm.MXFP4, hidden=2048 + 16), dict(path=9)])
+def test_bad_shapes_get_zero_workspace(kw):
+    assert pm.workspace_size(_shape(**kw)) == 0
+
+
+@pytest.mark.parametrize("kw", [dict(num_experts=2048, top_k=8), dict(top_k=64, num_experts=128),
+                                dict(act_dtype=pm.F32, weight_dtype=pm.BF16)])
+def test_unsupported_combinations(kw):
+    s = _shape(**kw).c()
+    st = pm.lib().moe_router_topk(ctypes.byref(s), FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == pm.ERR_UNSUPPORTED
+
+
+def _router(shape, x=FAKE, wr=FAKE, bias=None, ids=FAKE, w=FAKE, ws=FAKE, nbytes=None):
+    s = shape.c()
+    if nbytes is None:
+        nbytes = pm.workspace_size(shape)
+    return pm.lib().moe_router_topk(ctypes.byref(s), x, wr, bias, ids, w, ws, nbytes, None)
+
+
+def test_router_validation():
+    sh = _shape()
+    assert _router(sh, x=None) == pm.ERR_INVALID_ARG
+    assert _router(sh, x=FAKE + 4) == pm.ERR_INVALID_ARG          # misaligned
+    assert _router(sh, bias=FAKE + 2) == pm.ERR_INVALID_ARG
+    assert _router(sh, ws=None) == pm.ERR_INVALID_ARG
+    assert _router(sh, nbytes=pm.workspace_size(sh) - 1) == pm.ERR_WORKSPACE
+    # T == 0 is a no-op that launches nothing
+    assert _router(_shape(num_tokens=0)) == pm.OK
+
+
+def test_forward_validation():
+    sh = _shape()
+    s = sh.c()
+    w = pm.ExpertWeights(FAKE, FAKE, FAKE, None, None, None)
+    n = pm.workspace_size(sh)
+    L = pm.lib()
+    assert L.moe_forward(ctypes.byref(s), FAKE, FAKE, None, None, FAKE, None, None, FAKE, n, None) == pm.ERR_INVALID_ARG
+    wbad = pm.ExpertWeights(FAKE, None, FAKE, None, None, None)
+    assert L.moe_forward(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(wbad), FAKE, None, None, FAKE, n,
+                         None) == pm.ERR_INVALID_ARG
+    # MXFP4 needs its scale arrays
+    smx = _shape(weight_dtype=pm.MXFP4).c()
+    nmx = pm.workspace_size(_shape(weight_dtype=pm.MXFP4))
+    assert L.moe_forward(ctypes.byref(smx), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE, nmx,
+                         None) == pm.ERR_INVALID_ARG
+    s0 = _shape(num_tokens=0).c()
+    assert L.moe_forward(ctypes.byref(s0), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE,
+                         pm.workspace_size(_shape(num_tokens=0)), None) == pm.OK
+
+
+def test_status_strings():
+    for st in (pm.OK, pm.ERR_INVALID_ARG, pm.ERR_UNSUPPORTED, pm.ERR_WORKSPACE, pm.ERR_HIP, pm.ERR_DEVICE):
+        assert pm.status_string(st) and pm.status_string(st) != "unknown status"
+    assert pm.status_string(12345) == "unknown status"

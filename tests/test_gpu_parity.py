@@ -1,0 +1,285 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle on the same
+seeded inputs.  Needs an MI355X; run with -m gpu."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import prefill_moe_router_amd as pm
+import synth
+from tests.gpu_common import (DevLayer, canary_ok, compare_forward, guarded, layer, layer_of, lshape, note,
+                              run_forward, tdev, to_f64)
+from tests.helpers import grouping_violations, max_abs, oracle_layer, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
+    pm.lib()  # loud failure when the library is missing
+
+
+def _sample(T, n=48):
+    """Token sample spanning the chunk: first, last, and evenly spread in between."""
+    if T <= n:
+        return np.arange(T)
+    return np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, n - 2).astype(int)]))
+
+
+# ---- router ------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c0_tiny_f32", "c1_decode1_bf16", "c2_decode8_bf16", "c3_prefill8192_bf16",
+                                  "c4_mxfp4_decode8"])
+def test_router_topk_parity(name):
+    note(f"router parity {name}")
+    li = layer(name)
+    dl = DevLayer(li)
+    sh = lshape(li)
+    T, K = li.shape.T, li.shape.K
+    ws = pm.alloc_workspace(sh)
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    pm.router_topk(sh, dl.x, dl.wr, dl.bias, ids, w, ws)
+    torch.cuda.synchronize()
+    ref = oracle.router(oracle_layer(li))
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    mism = (gids != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
+    ok = ~mism
+    assert max_abs(gw[ok], ref["w"][ok]) <= 1e-6
+    assert np.all(np.diff(gids, axis=1) > 0)          # ascending ids
+    note(f"  near-ties {int(ref['near'].sum())}, id mismatches {int(mism.sum())}")
+
+
+def test_router_exact_ties_pick_lower_id():
+    """Identical router rows give bit-identical logits; the lower id must win."""
+    sh_ = synth.Shape(16, 256, 12, 3, 64, "bf16", "bf16")
+    li = layer_of(sh_)
+    popular = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(li.wr[2]) * 4)   # make 2/5/9 win often
+    for e in (2, 5, 9):
+        li.wr[e] = popular
+    dl = DevLayer(li)
+    sh = lshape(li)
+    ws = pm.alloc_workspace(sh)
+    ids = torch.empty(16, 3, dtype=torch.int32, device="cuda")
+    w = torch.empty(16, 3, dtype=torch.float32, device="cuda")
+    pm.router_topk(sh, dl.x, dl.wr, None, ids, w, ws)
+    ref = oracle.router(oracle_layer(li))
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
+
+
+# ---- grouping ----------------------------------------------------------------------------
+
+def _group_gpu(ids_np, E, T, K):
+    sh = pm.LayerShape(T, 256, E, K, 64)
+    ws = pm.alloc_workspace(sh)
+    P = T * K
+    ids = tdev(ids_np.astype(np.int32))
+    obuf, off = guarded(E + 1, torch.int32)
+    sbuf, srt = guarded(P, torch.int32)
+    pbuf, pos = guarded(P, torch.int32)
+    pm.group_tokens(sh, ids, off, srt, pos, ws)
+    torch.cuda.synchronize()
+    for b, n in ((obuf, E + 1), (sbuf, P), (pbuf, P)):
+        assert canary_ok(b, n, torch.int32)
+    return off.cpu().numpy(), srt.cpu().numpy(), pos.cpu().numpy(), ws
+
+
+@pytest.mark.parametrize("T,E,K,kind", [(1, 128, 8, "uniform"), (8, 128, 8, "uniform"), (5, 8, 8, "uniform"),
+                                        (8192, 128, 8, "zipf"), (8192, 128, 8, "one_hot"),
+                                        (2048, 1024, 32, "uniform"), (4096, 256, 8, "uniform"),
+                                        (333, 64, 3, "zipf"), (0, 16, 2, "uniform")])
+def test_group_parity(T, E, K, kind):
+    note(f"group parity T={T} E={E} K={K} {kind}")
+    rng = np.random.default_rng(T * 7 + E + K)
+    if kind == "uniform":
+        ids = np.stack([np.sort(rng.choice(E, K, replace=False)) for _ in range(T)]) if T else np.zeros((0, K))
+    elif kind == "zipf":
+        p = 1.0 / np.arange(1, E + 1)
+        p /= p.sum()
+        ids = np.stack([np.sort(rng.choice(E, K, replace=False, p=p)) for _ in range(T)])
+    else:  # every token routes to experts 0..K-1: one group per expert of size T, the rest empty
+        ids = np.tile(np.arange(K), (T, 1))
+    ids = ids.astype(np.int32).reshape(T, K)
+    off, srt, pos, _ = _group_gpu(ids, E, T, K)
+    roff, rsrt, rpos = oracle.group(ids, E)
+    np.testing.assert_array_equal(off, roff)
+    np.testing.assert_array_equal(srt, rsrt)
+    np.testing.assert_array_equal(pos, rpos)
+    assert grouping_violations(ids, E, off, srt, pos) == []
+
+
+def test_group_rejects_out_of_range_ids_without_oob_writes():
+    T, E, K = 64, 16, 2
+    rng = np.random.default_rng(3)
+    ids = np.stack([np.sort(rng.choice(E, K, replace=False)) for _ in range(T)]).astype(np.int32)
+    ids[5, 1] = E + 3
+    ids[9, 0] = -4
+    off, srt, pos, ws = _group_gpu(ids, E, T, K)
+    assert pm.check_device_error(ws) & pm.DEVERR_BAD_EXPERT_ID
+    assert pm.check_device_error(ws) == 0                       # read-and-clear
+    assert off[-1] == T * K - 2 and pos[5 * K + 1] == -1 and pos[9 * K] == -1
+    good = ids.copy()
+    # the grouped part equals the oracle's grouping of the valid slots
+    valid = (good >= 0) & (good < E)
+    for e in range(E):
+        seg = srt[off[e]:off[e + 1]]
+        assert np.all(good.reshape(-1)[seg] == e)
+        assert np.all(np.diff(seg) > 0)
+    assert np.sum(np.diff(off)) == valid.sum()
+
+
+# ---- staged expert FFN and combine ----------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c0_tiny_f32", "c1_decode1_bf16", "c2_decode8_bf16"])
+def test_staged_pipeline_parity(name):
+    """router_topk -> group_tokens -> expert_ffn -> combine, each checked."""
+    note(f"staged pipeline {name}")
+    li = layer(name)
+    dl = DevLayer(li)
+    sh = lshape(li)
+    T, K, E, H = li.shape.T, li.shape.K, li.shape.E, li.shape.H
+    P = T * K
+    ws = pm.alloc_workspace(sh)
+    ids = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    srt = torch.empty(P, dtype=torch.int32, device="cuda")
+    pos = torch.empty(P, dtype=torch.int32, device="cuda")
+    obuf, o = guarded(P * H, torch.float32)
+    o = o.view(P, H)
+    pm.router_topk(sh, dl.x, dl.wr, dl.bias, ids, w, ws)
+    pm.group_tokens(sh, ids, off, srt, pos, ws)
+    pm.expert_ffn(sh, dl.x, dl.weights, off, srt, o, ws)
+    y = torch.empty(T, H, dtype=dl.act_torch(), device="cuda")
+    pm.combine(sh, o, w, pos, y)
+    torch.cuda.synchronize()
+    assert canary_ok(obuf, P * H, torch.float32)
+    gids = ids.cpu().numpy()
+    L = oracle_layer(li)
+    roff, rsrt, rpos = oracle.group(gids, E)
+    np.testing.assert_array_equal(off.cpu().numpy(), roff)
+    np.testing.assert_array_equal(srt.cpu().numpy(), rsrt)
+    # expert outputs in sorted order against the oracle's pairs
+    toks = rsrt // K
+    exps = gids.reshape(-1)[rsrt]
+    oref = oracle.expert_pairs(L, toks, exps)
+    og = o.cpu().numpy().astype(np.float64)
+    tol = 1e-5 if li.shape.act == "f32" else 1e-2
+    assert rel_l2(og, oref) <= tol, rel_l2(og, oref)
+    # combine of the GPU's own expert outputs: fp32 sums of k terms, one final rounding
+    yref = np.zeros((T, H))
+    gw = w.cpu().numpy().astype(np.float64)
+    for t in range(T):
+        for j in range(K):
+            yref[t] += gw[t, j] * og[rpos[t * K + j]]
+    yg = to_f64(y, li.shape.act)
+    if li.shape.act == "f32":
+        assert max_abs(yg, yref) <= 1e-5 * max(1.0, np.abs(yref).max())
+    else:
+        # one bf16 rounding of the fp32 sum: within 2^-8 relative of each element
+        assert np.all(np.abs(yg - yref) <= np.abs(yref) * 2.0 ** -8 + 1e-6)
+    compare_forward(li, dict(y=y, ids=gids, w=w.cpu().numpy()), label=f"staged {name}")
+
+
+def test_combine_parity_random():
+    T, H, K = 37, 512, 5
+    rng = np.random.default_rng(11)
+    o = rng.standard_normal((T * K, H)).astype(np.float32)
+    w = rng.random((T, K)).astype(np.float32)
+    perm = rng.permutation(T * K).astype(np.int32)
+    sh = pm.LayerShape(T, H, 16, K, 64, act_dtype=pm.BF16, weight_dtype=pm.BF16)
+    y = torch.empty(T, H, dtype=torch.int16, device="cuda")
+    pm.combine(sh, tdev(o), tdev(w), tdev(perm), y)
+    ref = np.zeros((T, H))
+    for t in range(T):
+        for j in range(K):
+            ref[t] += np.float64(w[t, j]) * o[perm[t * K + j]]
+    yg = to_f64(y, "bf16")
+    assert np.all(np.abs(yg - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
+
+
+# ---- whole layer ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", ["c0_tiny_f32", "c1_decode1_bf16", "c2_decode8_bf16"])
+def test_forward_parity_decode_configs(name):
+    note(f"forward parity {name}")
+    li = layer(name)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=name)
+
+
+def test_forward_parity_prefill_chunk_sampled():
+    """8192-token Zipf-skewed chunk: all ids and the grouping checked everywhere, y on a
+    token sample spanning the chunk."""
+    name = "c3_prefill8192_bf16"
+    note(f"forward parity {name} (sampled)")
+    li = layer(name)
+    got = run_forward(DevLayer(li))
+    ref = oracle.router(oracle_layer(li))
+    mism = (got["ids"] != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any()
+    compare_forward(li, got, tokens=_sample(li.shape.T, 40), label=name)
+
+
+@pytest.mark.parametrize("name", ["c4_mxfp4_decode1", "c4_mxfp4_decode8"])
+def test_forward_parity_mxfp4_decode(name):
+    note(f"forward parity {name}")
+    li = layer(name)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=name)
+
+
+def test_forward_parity_mxfp4_small_ragged():
+    li = layer_of(synth.Shape(13, 256, 16, 4, 128, "bf16", "mxfp4"))
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label="mxfp4 small")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13])
+def test_forward_token_sweep(T):
+    note(f"token sweep T={T}")
+    li = layer_of(synth.Shape(T, 2048, 128, 8, 768, "bf16", "bf16", bias="normal"), batch=T)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=f"sweep T={T}")
+
+
+@pytest.mark.parametrize("K,renorm,E", [(1, True, 8), (8, True, 8), (3, False, 16), (32, True, 64)])
+def test_forward_k_and_renorm_edges(K, renorm, E):
+    li = layer_of(synth.Shape(6, 256, E, K, 64, "bf16", "bf16", bias="normal", renorm=renorm))
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=f"K={K} renorm={renorm} E={E}")
+
+
+def test_forward_zero_tokens_is_noop():
+    li = layer("c0_tiny_f32")
+    dl = DevLayer(li)
+    sh = lshape(li, T=0)
+    ws = pm.alloc_workspace(sh)
+    y = torch.full((4,), 3.0, device="cuda")
+    pm.forward(sh, dl.x, dl.wr, None, dl.weights, y, ws)
+    torch.cuda.synchronize()
+    assert torch.all(y == 3.0)
+
+
+def test_forward_deterministic():
+    li = layer("c2_decode8_bf16")
+    dl = DevLayer(li)
+    a = run_forward(dl)
+    b = run_forward(dl)
+    assert torch.equal(a["y"], b["y"])
+    np.testing.assert_array_equal(a["ids"], b["ids"])
+
+
+def test_forward_identical_experts_closed_form():
+    """All experts equal (renorm on): y = FFN(x) whatever the routing."""
+    li = layer_of(synth.Shape(7, 256, 8, 3, 64, "bf16", "bf16", bias="normal"))
+    for n in ("wg", "wu", "wd"):
+        a = getattr(li, n)
+        setattr(li, n, np.ascontiguousarray(np.broadcast_to(a[:1], a.shape)))
+    got = run_forward(DevLayer(li))
+    L1 = oracle.Layer(x=li.x, wr=li.wr[:1].copy(), wg=li.wg[:1].copy(), wu=li.wu[:1].copy(), wd=li.wd[:1].copy(),
+                      top_k=1)
+    ffn = oracle.forward(L1)["y"]
+    assert rel_l2(to_f64(got["y"], "bf16"), ffn) <= 1e-2
