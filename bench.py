@@ -1,0 +1,300 @@
+"""Benchmark of the MI355X MoE layer (router top-k softmax, token->expert
+grouping, SwiGLU experts, weighted combine) through the C ABI.
+
+One step = one moe_forward over one batch of synthetic, seeded inputs that
+are already resident in HBM.  Default workload: decode, 1 token, bf16,
+H=2048, E=128, top-8, I=768.  Other workloads (--config) serve for
+measurement of the other shapes; the default is the headline line.
+
+Decode steps rotate over `--copies` copies of the layer's weights (each at its
+own addresses, 16 x 1.2 GB by default) so the 256 MB Infinity Cache cannot
+serve repeats: every step streams its experts from HBM.  The steps are
+captured once into a HIP graph (through torch.cuda.CUDAGraph) and replayed,
+so host launch cost does not hide µs-scale GPU work; replays are checked
+against eager results before timing.
+
+Prints ONE JSON line.  The roofline object reports the dominant kernel (the
+fused decode launch, or the expert gate/up + SwiGLU launch of the staged
+path): algorithmic bytes (decode) or flops (prefill) per launch over its
+average duration.  The durations are HIP events that moe_forward_timed ties
+to that launch's start and end (hipExtLaunchKernelGGL), over a second timed
+pass of the same steps on torch's current stream.  The cpu_baseline object times the fp64 CPU oracle
+on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
+
+METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % peak"
+
+WORKLOADS = {
+    "decode1": ("c1_decode1_bf16", "decode, 1 token, bf16: H=2048, E=128, top-8 renorm, I=768, SwiGLU"),
+    "decode8": ("c2_decode8_bf16", "decode, 8 tokens, bf16, router bias N(0,0.5): H=2048, E=128, top-8, I=768"),
+    "prefill8192": ("c3_prefill8192_bf16",
+                    "prefill chunk, 8192 tokens, bf16, Zipf(1) router bias: H=2048, E=128, top-8, I=768"),
+    "mxfp4_decode1": ("c4_mxfp4_decode1", "decode, 1 token, MXFP4 experts, bf16 acts: H=4096, E=256, top-8, I=1024"),
+    "mxfp4_decode8": ("c4_mxfp4_decode8", "decode, 8 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
+    "mxfp4_prefill4096": ("c4_mxfp4_prefill4096",
+                          "prefill chunk, 4096 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
+    "tiny": ("c0_tiny_f32", "tiny fp32: 4 tokens, H=256, E=8, top-2, I=128"),
+}
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_elem(w: str) -> float:
+    return {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0}[w]
+
+
+def act_bytes(a: str) -> int:
+    return 4 if a == "f32" else 2
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="decode1", choices=sorted(WORKLOADS))
+    ap.add_argument("--copies", type=int, default=None, help="weight copies rotated over (defeats the MALL)")
+    ap.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--events-replays", type=int, default=10)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is measured on one MI355X", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import prefill_moe_router_amd as pm
+    import synth
+
+    name, desc = WORKLOADS[args.config]
+    sh = synth.CONFIGS[name]
+    decode = sh.T <= 8
+    copies = args.copies or (16 if decode else 2)
+    steps = args.steps or (1600 if decode else 20)
+    warmup = args.warmup if args.warmup is not None else (160 if decode else 4)
+    path = {"auto": pm.PATH_AUTO, "decode": pm.PATH_DECODE, "grouped": pm.PATH_GROUPED}[args.path]
+
+    torch.cuda.set_device(0)
+    t0 = time.time()
+    li = synth.make_layer(name)
+    log(f"generated {args.config} inputs in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        if a is None:
+            return None
+        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
+
+    w0 = dict(wg=dev(li.wg), wu=dev(li.wu), wd=dev(li.wd), sg=dev(li.sg), su=dev(li.su), sd=dev(li.sd))
+    wcopies = [w0] + [{k: (v.clone() if v is not None else None) for k, v in w0.items()} for _ in range(copies - 1)]
+    wr, bias = dev(li.wr), dev(li.bias)
+    xs = [dev(synth.make_x(sh, seed=0, batch=b)) for b in range(copies)]
+    shape = pm.LayerShape(sh.T, sh.H, sh.E, sh.K, sh.I, sh.renorm,
+                          pm.F32 if sh.act == "f32" else pm.BF16,
+                          {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4}[sh.w], path)
+    ws = pm.alloc_workspace(shape)
+    ydt = torch.float32 if sh.act == "f32" else torch.int16
+    ys = [torch.empty(sh.T, sh.H, dtype=ydt, device="cuda") for _ in range(copies)]
+    ids = [torch.empty(sh.T, sh.K, dtype=torch.int32, device="cuda") for _ in range(copies)]
+    wts = [torch.empty(sh.T, sh.K, dtype=torch.float32, device="cuda") for _ in range(copies)]
+    torch.cuda.synchronize()
+    log(f"resident: {copies} weight copies, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    def step(b, stream=None):
+        pm.forward(shape, xs[b], wr, bias, wcopies[b], ys[b], ws, ids[b], wts[b], stream=stream)
+
+    # eager reference results
+    for b in range(copies):
+        step(b)
+    torch.cuda.synchronize()
+    assert pm.check_device_error(ws) == 0
+    y_eager = [y.clone() for y in ys]
+    ids_eager = [i.clone() for i in ids]
+
+    # graph of one sweep over the copies
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step(0, stream=s)          # a warm call on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for b in range(copies):
+            step(b)
+    rem = steps % copies
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem):
+            for b in range(rem):
+                step(b)
+    for r in range(3):
+        for y in ys:
+            y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        for b in range(copies):
+            assert torch.equal(ys[b], y_eager[b]), f"graph replay {r} differs from eager (copy {b})"
+            assert torch.equal(ids[b], ids_eager[b])
+    log("graph replays match eager results")
+
+    n_full, n_w = steps // copies, max(1, math.ceil(warmup / copies))
+    for _ in range(n_w):
+        g.replay()
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` forward calls ----
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ev0.record()
+    for _ in range(n_full):
+        g.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall * 1e3 / steps
+    tokens_per_s = sh.T * steps / wall
+    log(f"timed {steps} steps: {wall * 1e3:.2f} ms wall ({gpu_ms:.2f} ms GPU events), {ms_per_step * 1e3:.2f} us/step")
+
+    # ---- algorithmic work per step --------------------------------------------------
+    bw = weight_bytes_per_elem(sh.w)
+    ba = act_bytes(sh.act)
+    U = [len(np.unique(i.cpu().numpy())) for i in ids_eager]
+    layer_bytes = [u * 3 * sh.H * sh.I * bw + sh.E * sh.H * ba + 2 * sh.T * sh.H * ba
+                   + (4 * sh.E if li.bias is not None else 0) for u in U]
+    gateup_bytes = [u * 2 * sh.H * sh.I * bw + sh.T * sh.H * ba for u in U]
+    layer_flops = 2 * sh.T * sh.K * 3 * sh.H * sh.I + 2 * sh.T * sh.H * sh.E
+    gateup_flops = 2 * sh.T * sh.K * 2 * sh.H * sh.I
+
+    # ---- dominant-kernel duration: start/stop events of that launch, every step ---------
+    stages = pm.forward_stages(shape)
+    dom_name = "decode_fused" if "decode_fused" in stages else "gate_up"
+    dom = stages.index(dom_name)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b_ in pairs:          # torch creates the underlying hipEvent_t at the first record
+        a.record()
+        b_.record()
+    torch.cuda.synchronize()
+    for k in range(steps):
+        b = k % copies
+        marks = [None] * (2 * len(stages))
+        marks[2 * dom], marks[2 * dom + 1] = pairs[k][0].cuda_event, pairs[k][1].cuda_event
+        pm.forward_timed(shape, xs[b], wr, bias, wcopies[b], ys[b], ws, marks, ids[b], wts[b])
+    torch.cuda.synchronize()
+    for b in range(copies):
+        assert torch.equal(ys[b], y_eager[b]), "timed pass changed results"
+    durs = [a.elapsed_time(b_) * 1e-3 for a, b_ in pairs]     # seconds
+    kern_s = float(np.mean(durs))
+    fused = dom_name == "decode_fused"
+    if decode:
+        kb = layer_bytes if fused else gateup_bytes
+        achieved = float(np.mean(kb)) / kern_s / 1e9
+        roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        kernel=("decode_fused (whole layer in one launch)" if fused
+                                else "gate_up (expert gate/up GEMV + SwiGLU)"),
+                        kernel_us=round(kern_s * 1e6, 3), kernel_us_median=round(float(np.median(durs)) * 1e6, 3),
+                        algorithmic_bytes=round(float(np.mean(kb))))
+    else:
+        achieved = gateup_flops / kern_s / 1e12
+        roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                        kernel="gate_up (grouped expert gate/up + SwiGLU)", kernel_us=round(kern_s * 1e6, 3),
+                        kernel_us_median=round(float(np.median(durs)) * 1e6, 3), algorithmic_flops=gateup_flops)
+    log(f"dominant kernel {dom_name}: {kern_s * 1e6:.2f} us avg over {len(durs)} launches")
+
+    layer_s = wall / steps
+    extra = dict(layer_us=round(layer_s * 1e6, 3), unique_experts_mean=float(np.mean(U)),
+                 stages=stages)
+    if decode:
+        gbs = float(np.mean(layer_bytes)) / layer_s / 1e9
+        extra.update(layer_bytes=round(float(np.mean(layer_bytes))), layer_gbs=round(gbs, 1),
+                     layer_hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        tf = layer_flops / layer_s / 1e12
+        extra.update(layer_flops=layer_flops, layer_tflops=round(tf, 2),
+                     layer_mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4))
+
+    out = {
+        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": n_w * copies, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": sh.w if sh.w != "f32" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,sd) random-init weights)",
+        "config": {"workload": desc, "tokens_per_step": sh.T, "hidden": sh.H, "experts": sh.E, "top_k": sh.K,
+                   "intermediate": sh.I, "weight_copies": copies, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "layer": extra,
+    }
+
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(li, sh, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(li, sh, target_s: float) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
+    import oracle
+    import synth
+
+    def layer_for(x):
+        return oracle.Layer(x=x, wr=li.wr, wg=li.wg, wu=li.wu, wd=li.wd, top_k=sh.K, renorm=sh.renorm,
+                            bias=li.bias, sg=li.sg, su=li.su, sd=li.sd)
+
+    threads = oracle.num_threads()
+    if sh.T <= 8:
+        # independent decode steps: batches of the same shape stacked into one oracle call
+        def run(nsteps):
+            x = np.concatenate([synth.make_x(sh, seed=0, batch=100 + b) for b in range(nsteps)])
+            t = time.perf_counter()
+            oracle.forward(layer_for(x))
+            return time.perf_counter() - t, nsteps * sh.T
+        dt, n = run(max(1, threads // sh.T))
+        nsteps = max(1, int(max(1, threads // sh.T) * target_s / max(dt, 1e-3)))
+        dt, n = run(nsteps)
+        sample = f"{nsteps} independent {sh.T}-token decode steps ({n} token rows) in one oracle call"
+    else:
+        x = li.x
+
+        def run(ntok):
+            toks = np.linspace(0, sh.T - 1, ntok).astype(np.int32)
+            t = time.perf_counter()
+            oracle.forward(layer_for(x), tokens=toks)
+            return time.perf_counter() - t, ntok
+        dt, n = run(threads)
+        ntok = max(1, int(threads * target_s / max(dt, 1e-3)))
+        dt, n = run(ntok)
+        sample = f"{ntok} tokens spread over the {sh.T}-token chunk (whole layer per token)"
+    log(f"cpu baseline: {n} tokens in {dt:.1f}s on {min(threads, n)} threads")
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(min(threads, n)), kind="oracle",
+                sample=sample, seconds=round(dt, 2))
+
+
+if __name__ == "__main__":
+    main()

@@ -147,6 +147,27 @@ moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_rout
                        void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * moe_forward with stage timing, for the per-stage profile the fused MoE
+ * profiling plan asks for (topk / expert kernel / activation / sum times,
+ * "Decode 吞吐专项实验分析报告", subsection "下一步 profiling 方向").
+ * stage_events holds n_stage_events hipEvent_t handles created by the caller
+ * (NULL entries are skipped): stage_events[2i] and stage_events[2i+1] bracket
+ * the i-th kernel launch of the call, as named by moe_forward_stages.  For the
+ * fused decode launch they are the kernel's own start and end timestamps
+ * (hipExtLaunchKernelGGL); for the staged launches they are recorded on
+ * `stream` right before and after the launch.  Results are identical to
+ * moe_forward.
+ */
+moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *w_router,
+                             const float *bias, const moe_expert_weights *w, void *y,
+                             int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
+                             void *stream, void *const *stage_events, int32_t n_stage_events);
+
+/* Comma-separated names of the kernel launches moe_forward makes for `shape`,
+ * in order (static string; "" for an invalid shape). */
+const char *moe_forward_stages(const moe_shape *shape);
+
+/*
  * Synchronises `stream`, reads the workspace's device error word into
  * *err_bits (host pointer, MOE_DEVERR_* bits), clears it, and returns
  * MOE_ERR_DEVICE when it was nonzero.

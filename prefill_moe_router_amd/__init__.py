@@ -31,7 +31,8 @@ PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 DEVERR_BAD_EXPERT_ID, DEVERR_TIMEOUT = 1, 2
 
 EXPORTS = ["moe_workspace_size", "moe_router_topk", "moe_group_tokens", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_check_device_error", "moe_status_string"]
+           "moe_forward", "moe_forward_timed", "moe_forward_stages", "moe_check_device_error",
+           "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -75,6 +76,10 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.argtypes = [PS, vp, vp, vp, vp, vp]
         L.moe_forward.restype = i32
         L.moe_forward.argtypes = [PS, vp, vp, vp, PW, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_timed.restype = i32
+        L.moe_forward_timed.argtypes = [PS, vp, vp, vp, PW, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp), i32]
+        L.moe_forward_stages.restype = ctypes.c_char_p
+        L.moe_forward_stages.argtypes = [PS]
         L.moe_check_device_error.restype = i32
         L.moe_check_device_error.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -172,6 +177,23 @@ def forward(shape: LayerShape, x, w_router, bias, weights: dict, y, ws, topk_ids
     w = _weights(**weights)
     _check(lib().moe_forward(ctypes.byref(s), _p(x), _p(w_router), _p(bias), ctypes.byref(w), _p(y),
                              _p(topk_ids), _p(topk_w), _p(ws), ws.numel(), _stream(stream)), "moe_forward")
+
+
+def forward_timed(shape: LayerShape, x, w_router, bias, weights: dict, y, ws, stage_events, topk_ids=None,
+                  topk_w=None, stream=None):
+    """moe_forward recording stage_events[i] (hipEvent_t handles or None) before launch i and
+    after the last launch."""
+    s = shape.c()
+    w = _weights(**weights)
+    arr = (ctypes.c_void_p * max(1, len(stage_events)))(*[e for e in stage_events])
+    _check(lib().moe_forward_timed(ctypes.byref(s), _p(x), _p(w_router), _p(bias), ctypes.byref(w), _p(y),
+                                   _p(topk_ids), _p(topk_w), _p(ws), ws.numel(), _stream(stream), arr,
+                                   len(stage_events)), "moe_forward_timed")
+
+
+def forward_stages(shape: LayerShape) -> list:
+    s = shape.c()
+    return lib().moe_forward_stages(ctypes.byref(s)).decode().split(",")
 
 
 def check_device_error(ws, stream=None) -> int:

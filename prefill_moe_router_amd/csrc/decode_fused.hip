@@ -1,0 +1,593 @@
+// decode_fused.hip -- the whole MoE layer for a decode batch (T <= 8 tokens)
+// in ONE persistent launch: router gate, top-k softmax, grouping, expert
+// gate/up + SwiGLU, down projection and weighted combine.
+//
+// The decode step of the serving report is starved by small kernels and the
+// bubbles between them ("Decode 吞吐专项实验分析报告", 一、结论摘要 and
+// 四、瓶颈判断: low GPU utilisation with many small kernels and syncs); one
+// launch pays the fixed launch/drain cost once.  The routing never leaves the
+// device ("第 9 章 prefill：最大的瓶颈" §9.9) and every token-expert pair is
+// computed whatever the batch (no 8-entry group limit, §9.5).
+//
+// One work-group per CU, all co-resident; phases are separated by a grid
+// barrier: a 64-bit arrival counter in the workspace that only grows (a
+// barrier completes when it reaches the next multiple of the grid size), with
+// relaxed atomics only.  Data that crosses work-groups (logits, h') is written
+// with write-through agent-scope stores and read with agent-scope loads, so
+// no cache writeback or invalidation is needed at the barrier.  Every wait is
+// bounded and sets MOE_DEVERR_TIMEOUT instead of hanging.
+//   0. router: expert rows spread one per wave over the grid; logits to the
+//      workspace (write-through stores).                          -- barrier
+//   1. every work-group redundantly takes the top-k of all T tokens and
+//      groups the T*k slots by expert in LDS (tiny: T*k <= 256).
+//   2. gate/up: one wave per (active expert, row i); the two 16-byte-chunked
+//      rows are dotted with the tokens of that expert (x staged in LDS);
+//      h'[slot][i] = w_slot * silu(g) * u goes to the workspace.   -- barrier
+//      (each wave issues its first down-projection loads before waiting)
+//   3. down + combine: one wave (or wave slice) per output row n streams
+//      Wd[e][n][:] of every active expert and accumulates
+//      y[t][n] = sum over t's slots of Wd[e][n].h'[slot] -- the weighted sum
+//      over the token's experts needs no second pass.
+#include <hip/hip_ext.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int FWPB = 8;                 // waves per work-group
+constexpr int FTHREADS = FWPB * WAVE;
+constexpr int FMAX_T = 8;
+constexpr int FMAX_P = 256;             // T * k
+constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
+constexpr int FDB = 8;                  // experts per down-projection load batch
+constexpr size_t FLDS_MAX = 144 * 1024; // staged x / h' bytes per work-group
+constexpr uint64_t SPIN_TICKS = 20000000ull;  // 0.2 s of the 100 MHz real-time clock
+
+struct FusedParams {
+    const uint8_t *x, *wr;
+    const float *bias;
+    const uint8_t *wg, *wu, *wd, *sg, *su, *sd;
+    uint8_t *y;
+    int32_t *ids_out;
+    float *w_out;
+    float *logits;    // workspace [T][E]
+    uint8_t *hbuf;    // workspace [P][I] (activation dtype)
+    uint64_t *bar;    // workspace control word: grid-barrier arrivals (only grows)
+    int32_t *err;
+    int T, H, E, K, I, renorm, nblocks;
+};
+
+// ---- grid barrier --------------------------------------------------------------------
+
+// The counter only grows and is a multiple of the grid size between calls.
+// Read at kernel start it lies in [base, base + G) -- no work-group can pass
+// the first barrier before every work-group has read it -- so rounding down
+// gives the call's base; barrier i completes at base + i*G.
+__device__ __forceinline__ uint64_t bar_base(uint64_t *bar, int nblocks) {
+    const uint64_t c = __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return c - c % (uint64_t)nblocks;
+}
+
+// Arrival: every wave's cross-group stores are acknowledged first, then one
+// relaxed increment per work-group whose result is not waited for.
+__device__ __forceinline__ void bar_arrive(uint64_t *bar) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(bar, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ACQ: end with an agent-scope acquire (invalidates this CU's stale cache lines) so that
+// plain loads may read what other work-groups wrote before the barrier.
+template <bool ACQ = false>
+__device__ __forceinline__ void bar_wait(uint64_t *bar, uint64_t target, int32_t *err) {
+    if (threadIdx.x == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            __builtin_amdgcn_s_sleep(1);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+                atomicOr(err, MOE_DEVERR_TIMEOUT);
+                break;
+            }
+        }
+        if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+}
+
+// ---- small helpers -------------------------------------------------------------------
+
+// C chunks of 16 bytes per lane: chunk lane0 + stride*c of the row (c < C), zero past nch
+template <class F, int C>
+__device__ __forceinline__ void load_chunks(const uint8_t *row, const uint8_t *srow, int nch, int lane0, int stride,
+                                            uint4 (&q)[C], uint32_t (&s)[C]) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int ch = lane0 + stride * c;
+        const bool ok = ch < nch;
+        q[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+        s[c] = (F::SCALED && ok) ? (uint32_t)srow[ch] : 0u;
+    }
+}
+
+template <class F, int C>
+__device__ __forceinline__ float row_dot(const uint4 (&q)[C], const uint32_t (&s)[C], const uint8_t *act, int nch,
+                                         int lane0, int stride) {
+    float acc = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int ch = lane0 + stride * c;
+        if (ch < nch) acc = chunk_dot<F>(q[c], s[c], act + (size_t)ch * F::XB, acc);
+    }
+    return acc;
+}
+
+// total of each group of `lpr` (16, 32 or 64) lanes, in the group's last lane
+__device__ __forceinline__ float group_sum_last(float v, int lpr) {
+    v = dpp_sum16(v);
+    if (lpr >= 32) v += dpp_f<0x142, 0xa>(v, 0.f);
+    if (lpr == 64) v += dpp_f<0x143, 0xc>(v, 0.f);
+    return v;
+}
+
+__device__ __forceinline__ void store_act_sc1(uint8_t *base, size_t idx, float v, bool f32) {
+    if (f32)
+        __hip_atomic_store(reinterpret_cast<float *>(base) + idx, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        __hip_atomic_store(reinterpret_cast<uint16_t *>(base) + idx, (uint16_t)f32_to_bf16_rne(v), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = threadIdx.x & 63;
+    return l ? (~0ull >> (64 - l)) : 0ull;
+}
+
+// Top-k of one token's E (<= 1024) logits in one wave, by radix selection on
+// order-preserving keys: the k-th largest key is found bit by bit from the
+// top with ballot counts, keys above it are kept, and keys equal to it are
+// kept in ascending expert id until k are kept (ties go to the lower id).
+// Writes ids (ascending) and weights (softmax over all E at the kept ids,
+// renormalised over the kept set when renorm) to ids[0..k) / w[0..k).
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float *logits, int E, int K, int renorm, int *ids, float *w,
+                                          int32_t *ids_g, float *w_g) {
+    const int lane = threadIdx.x & 63;
+    constexpr int nj = NJ;
+    float v[NJ];
+    uint32_t key[NJ];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        const bool ok = e < E;
+        v[j] = ok ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
+        key[j] = ok ? f32_order_key(v[j]) : 0u;
+        m = fmaxf(m, v[j]);
+    }
+    m = wave_max_u(m);
+    uint32_t prefix = 0;
+    int need = K;
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        const uint32_t hi = cand >> b;
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] != 0u && (key[j] >> b) == hi));
+        if (cnt >= need)
+            prefix = cand;
+        else
+            need -= cnt;
+    }
+    // kept: key > prefix, or key == prefix among the first `need` such in id order
+    const uint64_t lt = lanemask_lt();
+    int eq_before = 0, sel_before = 0;
+    float z = 0.f;
+    float pe[NJ];
+    bool sel[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bool valid = key[j] != 0u;
+        const bool eq = valid && key[j] == prefix;
+        const uint64_t eqm = __ballot(eq);
+        const int eq_rank = eq_before + __popcll(eqm & lt);
+        eq_before += __popcll(eqm);
+        sel[j] = valid && (key[j] > prefix || (eq && eq_rank < need));
+        pe[j] = valid ? __expf(v[j] - m) : 0.f;
+        if (!renorm || sel[j]) z += pe[j];
+    }
+    const float denom = wave_sum_u(z);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const uint64_t sm = __ballot(sel[j]);
+        const int pos = sel_before + __popcll(sm & lt);
+        sel_before += __popcll(sm);
+        if (sel[j]) {
+            const int e = lane + 64 * j;
+            ids[pos] = e;
+            w[pos] = pe[j] / denom;
+            if (ids_g) ids_g[pos] = e;
+            if (w_g) w_g[pos] = pe[j] / denom;
+        }
+    }
+}
+
+// ---- the kernel ------------------------------------------------------------------------
+
+// F: expert weight format; A: activation / router format (FmtF32 or FmtBF16);
+// CG / CR / CD: 16-byte chunks per lane of a gate-up row, a router row and a
+// down row (slice).
+template <class F, class A, int CG, int CR, int CD>
+__global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // staged x, later staged h'
+    __shared__ __attribute__((aligned(16))) int s_ids[FMAX_P + 4];
+    __shared__ float s_w[FMAX_P];
+    __shared__ int s_sorted[FMAX_P];
+    __shared__ __attribute__((aligned(16))) int s_first[FMAX_P + 4];
+    __shared__ int s_act_e[FMAX_P], s_act_start[FMAX_P], s_act_cnt[FMAX_P];
+    __shared__ int s_nact;
+    __shared__ uint64_t s_base;
+
+    const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, P = T * K;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int G = p.nblocks;
+    const int NW = G * FWPB;
+    const int gw = blockIdx.x + G * wave;        // consecutive work items land on different CUs
+    const bool f32 = A::EPC == 4;
+    const int ab = f32 ? 4 : 2;
+
+    if (tid == 0) s_base = bar_base(p.bar, G);
+
+    // ---- phase 0: router logits (row loads first, then x staged into LDS) ----------------
+    {
+        const int nch = H / A::EPC;
+        const size_t xrow = (size_t)H * ab;
+        const int e = blockIdx.x + G * wave;
+        uint4 q[CR];
+        uint32_t sc[CR];
+        if (e < E) load_chunks<A, CR>(p.wr + (size_t)e * nch * 16, nullptr, nch, lane, WAVE, q, sc);
+        const int n16 = T * H * ab / 16;
+        const uint4 *src = reinterpret_cast<const uint4 *>(p.x);
+        uint4 *dst = reinterpret_cast<uint4 *>(smem);
+        for (int i = tid; i < n16; i += FTHREADS) dst[i] = src[i];
+        __syncthreads();
+        for (int ee = e; ee < E; ee += NW) {
+            if (ee != e) load_chunks<A, CR>(p.wr + (size_t)ee * nch * 16, nullptr, nch, lane, WAVE, q, sc);
+            const float b = p.bias ? p.bias[ee] : 0.f;
+#pragma unroll
+            for (int t = 0; t < FMAX_T; ++t) {
+                if (t < T) {
+                    const float v = dpp_sum64(row_dot<A, CR>(q, sc, smem + t * xrow, nch, lane, WAVE));
+                    if (lane == 63)
+                        __hip_atomic_store(p.logits + (size_t)t * E + ee, v + b, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
+    bar_arrive(p.bar);
+    bar_wait(p.bar, s_base + (uint64_t)G, p.err);
+
+    // ---- phase 1: top-k + softmax per token (wave t), then grouping ----------------------
+    if (wave < T) {
+        const bool out = blockIdx.x == 0;
+        const float *lg = p.logits + (size_t)wave * E;
+        int *ii = s_ids + wave * K;
+        float *ww = s_w + wave * K;
+        int32_t *ig = out && p.ids_out ? p.ids_out + wave * K : nullptr;
+        float *wg = out && p.w_out ? p.w_out + wave * K : nullptr;
+        if (E <= 64) wave_topk<1>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 128) wave_topk<2>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 256) wave_topk<4>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 512) wave_topk<8>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else wave_topk<16>(lg, E, K, p.renorm, ii, ww, ig, wg);
+    }
+    __syncthreads();
+    // pad the id table to a multiple of 4 with a sentinel no id equals or exceeds
+    if (tid < 4) s_ids[P + tid] = 0x7fffffff;
+    __syncthreads();
+    const int P4 = (P + 3) >> 2;
+    int my_e = 0, my_less = 0, my_cnt = 0;
+    if (tid < P) {
+        my_e = s_ids[tid];
+        int before = 0;
+        const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
+#pragma unroll 4
+        for (int q4 = 0; q4 < P4; ++q4) {
+            const int4 v = ids4[q4];
+            const int q = q4 * 4;
+            my_less += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
+            my_cnt += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
+            before += (v.x == my_e && q < tid) + (v.y == my_e && q + 1 < tid) + (v.z == my_e && q + 2 < tid) +
+                      (v.w == my_e && q + 3 < tid);
+        }
+        s_sorted[my_less + before] = tid;
+        s_first[tid] = before == 0 ? my_e : 0x7fffffff;   // first slot of its expert carries the id
+    }
+    if (tid < 4) s_first[P + tid] = 0x7fffffff;
+    __syncthreads();
+    if (tid < P && s_first[tid] == my_e) {
+        int dl = 0;
+        const int4 *f4 = reinterpret_cast<const int4 *>(s_first);
+#pragma unroll 4
+        for (int q4 = 0; q4 < P4; ++q4) {
+            const int4 v = f4[q4];
+            dl += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
+        }
+        s_act_e[dl] = my_e;
+        s_act_start[dl] = my_less;
+        s_act_cnt[dl] = my_cnt;
+    }
+    if (tid == 0) {
+        int n = 0;
+        for (int q = 0; q < P; ++q) n += s_first[q] != 0x7fffffff;
+        s_nact = n;
+    }
+    __syncthreads();
+    const int U = s_nact;
+
+    // ---- phase 2: gate/up + SwiGLU -> h' (next item's rows in flight while computing) -----
+    {
+        const int nch = H / F::EPC;
+        const size_t xrow = (size_t)H * ab;
+        const long nitems = (long)U * I;
+        uint4 gq[CG], uq[CG], gq2[CG], uq2[CG];
+        uint32_t gs[CG], us[CG], gs2[CG], us2[CG];
+        auto fetch = [&](long q, uint4 (&g)[CG], uint32_t (&gsc)[CG], uint4 (&u)[CG], uint32_t (&usc)[CG]) {
+            const int uu = (int)(q / I), i = (int)(q - (long)uu * I);
+            const size_t rsel = (size_t)s_act_e[uu] * I + i;
+            load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * nch : nullptr, nch, lane, WAVE, g, gsc);
+            load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * nch : nullptr, nch, lane, WAVE, u, usc);
+        };
+        auto consume = [&](long q, const uint4 (&g)[CG], const uint32_t (&gsc)[CG], const uint4 (&u)[CG],
+                           const uint32_t (&usc)[CG]) {
+            const int uu = (int)(q / I), i = (int)(q - (long)uu * I);
+            const int start = s_act_start[uu], cnt = s_act_cnt[uu];
+#pragma unroll
+            for (int c = 0; c < FMAX_T; ++c) {
+                if (c < cnt) {
+                    const int slot = s_sorted[start + c];
+                    const uint8_t *xa = smem + (size_t)(slot / K) * xrow;
+                    const float gv = dpp_sum64(row_dot<F, CG>(g, gsc, xa, nch, lane, WAVE));
+                    const float uv = dpp_sum64(row_dot<F, CG>(u, usc, xa, nch, lane, WAVE));
+                    if (lane == 63) store_act_sc1(p.hbuf, (size_t)(start + c) * I + i, s_w[slot] * swiglu(gv, uv), f32);
+                }
+            }
+        };
+        long q = gw;
+        if (q < nitems) fetch(q, gq, gs, uq, us);
+        while (q < nitems) {
+            const long q2 = q + NW;
+            if (q2 < nitems) fetch(q2, gq2, gs2, uq2, us2);
+            consume(q, gq, gs, uq, us);
+            if (q2 >= nitems) break;
+            const long q3 = q2 + NW;
+            if (q3 < nitems) fetch(q3, gq, gs, uq, us);
+            consume(q2, gq2, gs2, uq2, us2);
+            q = q3;
+        }
+    }
+
+    // ---- barrier, with the first down-projection loads issued before the wait -------------
+    // The wave's work is the sequence (row item, batch of DB active experts); two
+    // batches are in flight, the first one issued before the barrier wait.
+    constexpr int DB = CD >= 4 ? 2 : (CD == 2 ? 4 : 8);
+    const int nchd = I / F::EPC;
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);   // lanes per output row
+    const int rpw = WAVE / lpr;                                       // rows per wave
+    const int lg = lane / lpr, li = lane % lpr;
+    const int nrow_items = (H + rpw - 1) / rpw;
+    const int nbat = (U + DB - 1) / DB;
+    const int nrw = gw < nrow_items ? (nrow_items - 1 - gw) / NW + 1 : 0;
+    const int total = nrw * nbat;
+    uint4 dqa[DB][CD], dqb[DB][CD];
+    uint32_t dsa[DB][CD], dsb[DB][CD];
+    auto load_seq = [&](int sq, uint4 (&dq)[DB][CD], uint32_t (&ds)[DB][CD]) {
+        const int n = (gw + NW * (sq / nbat)) * rpw + lg;
+        const int u0 = (sq % nbat) * DB;
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+            const int u = u0 + b;
+            const bool okb = u < U && n < H;
+            const size_t rsel = (size_t)(okb ? s_act_e[u] : 0) * H + (okb ? n : 0);
+            const uint8_t *row = p.wd + rsel * nchd * 16;
+#pragma unroll
+            for (int c = 0; c < CD; ++c) {
+                const int ch = li + lpr * c;
+                const bool ok = okb && ch < nchd;
+                dq[b][c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+                ds[b][c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
+            }
+        }
+    };
+    bar_arrive(p.bar);
+    if (total > 0) load_seq(0, dqa, dsa);
+    bar_wait(p.bar, s_base + 2 * (uint64_t)G, p.err);
+
+    // stage h' (all P slots, sorted order) into LDS with agent-scope loads
+    {
+        const int n8 = P * I * ab / 8;
+        const uint64_t *src = reinterpret_cast<const uint64_t *>(p.hbuf);
+        uint64_t *dst = reinterpret_cast<uint64_t *>(smem);
+        for (int i = tid; i < n8; i += FTHREADS)
+            dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+
+    // ---- phase 3: down projection + weighted combine, by output row ------------------------
+    {
+        const size_t hrow = (size_t)I * ab;
+        float acc[FMAX_T];
+#pragma unroll
+        for (int t = 0; t < FMAX_T; ++t) acc[t] = 0.f;
+        auto consume = [&](int sq, const uint4 (&dq)[DB][CD], const uint32_t (&ds)[DB][CD]) {
+            const int n = (gw + NW * (sq / nbat)) * rpw + lg;
+            const int u0 = (sq % nbat) * DB;
+#pragma unroll
+            for (int b = 0; b < DB; ++b) {
+                const int u = u0 + b;
+                if (u < U) {
+                    const int start = s_act_start[u], cnt = s_act_cnt[u];
+                    for (int c = 0; c < cnt; ++c) {
+                        const int slot = s_sorted[start + c];
+                        const int t = slot / K;
+                        const uint8_t *ha = smem + (size_t)(start + c) * hrow;
+                        float d = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < CD; ++cc) {
+                            const int ch = li + lpr * cc;
+                            if (ch < nchd) d = chunk_dot<F>(dq[b][cc], ds[b][cc], ha + (size_t)ch * F::XB, d);
+                        }
+#pragma unroll
+                        for (int tt = 0; tt < FMAX_T; ++tt) acc[tt] += (t == tt) ? d : 0.f;
+                    }
+                }
+            }
+            if (sq % nbat == nbat - 1) {   // last batch of this row: reduce and store
+#pragma unroll
+                for (int t = 0; t < FMAX_T; ++t) {
+                    if (t < T) {
+                        const float v = group_sum_last(acc[t], lpr);
+                        if (li == lpr - 1 && n < H) {
+                            if (f32)
+                                reinterpret_cast<float *>(p.y)[(size_t)t * H + n] = v;
+                            else
+                                reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
+                        }
+                    }
+                    acc[t] = 0.f;
+                }
+            }
+        };
+        for (int sq = 0; sq < total; sq += 2) {
+            if (sq + 1 < total) load_seq(sq + 1, dqb, dsb);
+            consume(sq, dqa, dsa);
+            if (sq + 1 >= total) break;
+            if (sq + 2 < total) load_seq(sq + 2, dqa, dsa);
+            consume(sq + 1, dqb, dsb);
+        }
+    }
+}
+
+// true when the fused kernel covers this shape (otherwise the staged kernels run)
+static bool fused_bucket_built(int cg, int cr, int cd);
+static int bucket(int chunks_per_lane);
+
+bool decode_fused_supported(const moe_shape &s) {
+    const size_t ab = act_bytes(s.act_dtype);
+    const size_t P = (size_t)s.num_tokens * s.top_k;
+    if (s.num_tokens < 1 || s.num_tokens > FMAX_T || P > FMAX_P) return false;
+    const int epc = s.weight_dtype == MOE_F32 ? 4 : s.weight_dtype == MOE_BF16 ? 8 : 32;
+    const int aepc = s.act_dtype == MOE_F32 ? 4 : 8;
+    if ((s.hidden / epc + WAVE - 1) / WAVE > FMAX_C) return false;          // gate/up rows
+    if ((s.hidden / aepc + WAVE - 1) / WAVE > FMAX_C) return false;         // router rows
+    const int nchd = s.intermediate / epc;
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
+    if (nchd < 16 || (nchd + lpr - 1) / lpr > FMAX_C / 2) return false;    // down rows
+    if ((size_t)s.num_tokens * s.hidden * ab > FLDS_MAX || P * s.intermediate * ab > FLDS_MAX) return false;
+    if (s.num_experts > 1024) return false;
+    return fused_bucket_built(bucket((s.hidden / epc + WAVE - 1) / WAVE), bucket((s.hidden / aepc + WAVE - 1) / WAVE),
+                              bucket((nchd + lpr - 1) / lpr));
+}
+
+template <class F, class A, int CG, int CR, int CD>
+static hipError_t fused_launch(const FusedParams &prm, size_t lds, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    auto kern = decode_fused_kernel<F, A, CG, CR, CD>;
+    static bool attr_done = false;  // raising the dynamic-LDS cap is idempotent
+    if (!attr_done) {
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)FLDS_MAX);
+        if (r != hipSuccess) return r;
+        attr_done = true;
+    }
+    if (ev0 || ev1) {
+        hipExtLaunchKernelGGL(kern, dim3(prm.nblocks), dim3(FTHREADS), lds, st, ev0, ev1, 0, prm);
+    } else {
+        hipLaunchKernelGGL(kern, dim3(prm.nblocks), dim3(FTHREADS), lds, st, prm);
+    }
+    return hipGetLastError();
+}
+
+static int bucket(int chunks_per_lane) { return chunks_per_lane <= 1 ? 1 : chunks_per_lane <= 2 ? 2 : chunks_per_lane <= 4 ? 4 : 8; }
+
+template <class F, class A>
+static hipError_t fused_dispatch(const moe_shape &s, const FusedParams &prm, size_t lds, hipStream_t st,
+                                 hipEvent_t ev0, hipEvent_t ev1) {
+    const int cg = bucket((s.hidden / F::EPC + WAVE - 1) / WAVE);
+    const int cr = bucket((s.hidden / A::EPC + WAVE - 1) / WAVE);
+    const int nchd = s.intermediate / F::EPC;
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
+    const int cd = bucket((nchd + lpr - 1) / lpr);
+#define MOE_FL(CG, CR, CD) \
+    if (cg == CG && cr == CR && cd == CD) return fused_launch<F, A, CG, CR, CD>(prm, lds, st, ev0, ev1)
+    // (gate/up, router, down) chunk buckets of the supported shapes
+    MOE_FL(4, 4, 2);   // H 2048 bf16, I 768..1024 bf16
+    MOE_FL(4, 4, 1);
+    MOE_FL(4, 4, 4);
+    MOE_FL(2, 8, 1);   // H 4096 MXFP4 (router bf16), I 1024
+    MOE_FL(2, 8, 2);
+    MOE_FL(1, 4, 1);   // H 2048 MXFP4
+    MOE_FL(1, 1, 1);   // H 256 fp32 / H 512 bf16, small I
+    MOE_FL(1, 1, 2);
+    MOE_FL(2, 2, 1);   // H 1024 bf16
+    MOE_FL(2, 2, 2);
+    MOE_FL(8, 8, 2);   // H 4096 bf16
+    MOE_FL(8, 8, 4);
+#undef MOE_FL
+    return hipErrorInvalidConfiguration;
+}
+
+// (gate/up, router, down) chunk buckets the fused kernel is built for
+static bool fused_bucket_built(int cg, int cr, int cd) {
+    static const int combos[][3] = {{4, 4, 2}, {4, 4, 1}, {4, 4, 4}, {2, 8, 1}, {2, 8, 2}, {1, 4, 1},
+                                    {1, 1, 1}, {1, 1, 2}, {2, 2, 1}, {2, 2, 2}, {8, 8, 2}, {8, 8, 4}};
+    for (const auto &c : combos)
+        if (c[0] == cg && c[1] == cr && c[2] == cd) return true;
+    return false;
+}
+
+hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr, const float *bias,
+                               const moe_expert_weights &w, void *y, int32_t *ids_out, float *w_out, void *ws,
+                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    const WsLayout L = ws_layout(s);
+    int dev = 0, cus = 0;
+    hipError_t r = hipGetDevice(&dev);
+    if (r != hipSuccess) return r;
+    r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (r != hipSuccess) return r;
+    FusedParams prm{};
+    prm.x = static_cast<const uint8_t *>(x);
+    prm.wr = static_cast<const uint8_t *>(wr);
+    prm.bias = bias;
+    prm.wg = static_cast<const uint8_t *>(w.w_gate);
+    prm.wu = static_cast<const uint8_t *>(w.w_up);
+    prm.wd = static_cast<const uint8_t *>(w.w_down);
+    prm.sg = w.s_gate;
+    prm.su = w.s_up;
+    prm.sd = w.s_down;
+    prm.y = static_cast<uint8_t *>(y);
+    prm.ids_out = ids_out;
+    prm.w_out = w_out;
+    uint8_t *wsb = static_cast<uint8_t *>(ws);
+    prm.logits = reinterpret_cast<float *>(wsb + L.logits);
+    prm.hbuf = wsb + L.h;
+    prm.bar = reinterpret_cast<uint64_t *>(wsb + L.ctrl + 8);
+    prm.err = reinterpret_cast<int32_t *>(wsb + L.ctrl);
+    prm.T = s.num_tokens;
+    prm.H = s.hidden;
+    prm.E = s.num_experts;
+    prm.K = s.top_k;
+    prm.I = s.intermediate;
+    prm.renorm = s.renormalize ? 1 : 0;
+    prm.nblocks = cus;
+    const size_t ab = act_bytes(s.act_dtype);
+    const size_t lds = std::max((size_t)s.num_tokens * s.hidden * ab,
+                                (size_t)s.num_tokens * s.top_k * s.intermediate * ab);
+    switch (s.weight_dtype) {
+        case MOE_F32: return fused_dispatch<FmtF32, FmtF32>(s, prm, lds, st, ev0, ev1);
+        case MOE_BF16: return fused_dispatch<FmtBF16, FmtBF16>(s, prm, lds, st, ev0, ev1);
+        default: return fused_dispatch<FmtMX4, FmtBF16>(s, prm, lds, st, ev0, ev1);
+    }
+}
+
+}  // namespace moe

@@ -148,9 +148,38 @@ moe_status moe_combine(const moe_shape *shape, const float *expert_out, const fl
     return MOE_OK;
 }
 
-moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
-                       const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
-                       size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+const char *const kStagesStaged = "router_logits,topk,group,gate_up,down,combine";
+const char *const kStagesFused = "decode_fused";
+
+bool use_fused(const moe_shape &s) {
+    return s.path != MOE_PATH_GROUPED && s.num_tokens <= 8 && decode_fused_supported(s);
+}
+
+// Event pair (start, stop) of launch i, taken from ev[2i], ev[2i+1] when present.
+struct StageEvents {
+    hipEvent_t *ev;
+    int n;
+    hipEvent_t start(int i) const { return (ev && 2 * i < n) ? ev[2 * i] : nullptr; }
+    hipEvent_t stop(int i) const { return (ev && 2 * i + 1 < n) ? ev[2 * i + 1] : nullptr; }
+};
+
+// Records the pair around a launch made by the staged launchers.
+template <class Fn>
+hipError_t around(const StageEvents &se, int i, hipStream_t st, Fn &&fn) {
+    hipError_t r;
+    if (se.start(i) && (r = hipEventRecord(se.start(i), st)) != hipSuccess) return r;
+    if ((r = fn()) != hipSuccess) return r;
+    if (se.stop(i) && (r = hipEventRecord(se.stop(i), st)) != hipSuccess) return r;
+    return hipSuccess;
+}
+
+moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                        const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, hipStream_t st, hipEvent_t *events, int n_events) {
     MOE_CHECK(check_shape(shape));
     MOE_CHECK(check_path(shape));
     if (shape->num_tokens == 0) return MOE_OK;
@@ -161,19 +190,55 @@ moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_rout
         return MOE_ERR_INVALID_ARG;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return MOE_ERR_INVALID_ARG;
     MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const StageEvents se{events, n_events};
+    if (use_fused(*shape)) {
+        MOE_TRY(launch_decode_fused(*shape, x, w_router, bias, *w, y, topk_ids_out, topk_w_out, ws, st, se.start(0),
+                                    se.stop(0)));
+        return MOE_OK;
+    }
     const WsLayout L = ws_layout(*shape);
-    hipStream_t st = static_cast<hipStream_t>(stream);
     int32_t *ids = topk_ids_out ? topk_ids_out : at<int32_t>(ws, L.ids);
     float *wts = topk_w_out ? topk_w_out : at<float>(ws, L.wts);
     int32_t *offsets = at<int32_t>(ws, L.offsets), *sorted = at<int32_t>(ws, L.sorted);
     int32_t *slot_pos = at<int32_t>(ws, L.slot_pos), *active = at<int32_t>(ws, L.active);
-    MOE_TRY(launch_router_logits(*shape, x, w_router, bias, at<float>(ws, L.logits), st));
-    MOE_TRY(launch_topk(*shape, at<float>(ws, L.logits), ids, wts, st));
-    MOE_TRY(launch_group(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.ctrl), st));
-    MOE_TRY(launch_decode_gateup(*shape, x, *w, offsets, sorted, active, nullptr, at<void>(ws, L.h), st));
-    MOE_TRY(launch_decode_down(*shape, *w, offsets, active, at<void>(ws, L.h), at<float>(ws, L.o), st));
-    MOE_TRY(launch_combine(*shape, at<float>(ws, L.o), wts, slot_pos, y, st));
+    float *logits = at<float>(ws, L.logits), *o = at<float>(ws, L.o);
+    void *h = at<void>(ws, L.h);
+    int32_t *err = at<int32_t>(ws, L.ctrl);
+    MOE_TRY(around(se, 0, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
+    MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
+    MOE_TRY(around(se, 2, st, [&] { return launch_group(*shape, ids, offsets, sorted, slot_pos, active, err, st); }));
+    MOE_TRY(around(se, 3, st, [&] {
+        return launch_decode_gateup(*shape, x, *w, offsets, sorted, active, nullptr, h, st);
+    }));
+    MOE_TRY(around(se, 4, st, [&] { return launch_decode_down(*shape, *w, offsets, active, h, o, st); }));
+    MOE_TRY(around(se, 5, st, [&] { return launch_combine(*shape, o, wts, slot_pos, y, st); }));
     return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                       const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                       size_t ws_bytes, void *stream) {
+    return forward_impl(shape, x, w_router, bias, w, y, topk_ids_out, topk_w_out, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                             const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out,
+                             void *ws, size_t ws_bytes, void *stream, void *const *stage_events,
+                             int32_t n_stage_events) {
+    if (n_stage_events < 0 || (n_stage_events > 0 && !stage_events)) return MOE_ERR_INVALID_ARG;
+    return forward_impl(shape, x, w_router, bias, w, y, topk_ids_out, topk_w_out, ws, ws_bytes,
+                        static_cast<hipStream_t>(stream),
+                        reinterpret_cast<hipEvent_t *>(const_cast<void **>(stage_events)), n_stage_events);
+}
+
+const char *moe_forward_stages(const moe_shape *shape) {
+    if (check_shape(shape) != MOE_OK) return "";
+    return use_fused(*shape) ? kStagesFused : kStagesStaged;
 }
 
 moe_status moe_check_device_error(void *ws, int32_t *err_bits, void *stream) {

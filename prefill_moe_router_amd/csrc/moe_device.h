@@ -11,6 +11,7 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
 
 constexpr int WAVE = 64;
 
@@ -50,6 +51,12 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t packed, float scale
 // silu(g) * u
 __device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// streaming (non-temporal) 16-byte load: weights are read once per call
+__device__ __forceinline__ uint4 ld_stream16(const void *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // ---- wave64 reductions -----------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -59,6 +66,53 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
+
+// DPP move of v (fp32 bits); lanes with no source read `fill`
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ float dpp_f(float v, float fill) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(fill), __float_as_int(v), CTRL, ROW_MASK, 0xf,
+                                                      false));
+}
+
+// Sums of groups of 16 / 32 / 64 consecutive lanes through DPP row shifts and
+// row broadcasts (no LDS traffic).  The group's total lands in its last lane
+// (lane 15 of each row, lanes 31 and 63, or lane 63).
+__device__ __forceinline__ float dpp_sum16(float v) {
+    v += dpp_f<0x111>(v, 0.f);  // row_shr:1
+    v += dpp_f<0x112>(v, 0.f);  // row_shr:2
+    v += dpp_f<0x114>(v, 0.f);  // row_shr:4
+    v += dpp_f<0x118>(v, 0.f);  // row_shr:8
+    return v;
+}
+__device__ __forceinline__ float dpp_sum32(float v) {
+    v = dpp_sum16(v);
+    return v + dpp_f<0x142, 0xa>(v, 0.f);  // row_bcast:15 into rows 1 and 3
+}
+__device__ __forceinline__ float dpp_sum64(float v) {
+    v = dpp_sum32(v);
+    return v + dpp_f<0x143, 0xc>(v, 0.f);  // row_bcast:31 into rows 2 and 3
+}
+// wave-uniform total of v over the 64 lanes
+__device__ __forceinline__ float wave_sum_u(float v) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(dpp_sum64(v)), 63));
+}
+__device__ __forceinline__ float wave_max_u(float v) {
+    const float ninf = -__builtin_inff();
+    v = fmaxf(v, dpp_f<0x111>(v, ninf));
+    v = fmaxf(v, dpp_f<0x112>(v, ninf));
+    v = fmaxf(v, dpp_f<0x114>(v, ninf));
+    v = fmaxf(v, dpp_f<0x118>(v, ninf));
+    v = fmaxf(v, dpp_f<0x142, 0xa>(v, ninf));
+    v = fmaxf(v, dpp_f<0x143, 0xc>(v, ninf));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// order-preserving map of fp32 to uint32 (-0 and +0 map to the same key)
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 
 // ---- element formats -------------------------------------------------------------
 // A "chunk" is 16 bytes of a weight row: 4 fp32, 8 bf16 or 32 MXFP4 codes (one

@@ -67,4 +67,10 @@ hipError_t launch_decode_down(const moe_shape &s, const moe_expert_weights &w, c
 hipError_t launch_combine(const moe_shape &s, const float *o, const float *w, const int32_t *slot_pos,
                           void *y, hipStream_t st);
 
+// whole layer for T <= 8 in one persistent launch (see decode_fused.hip)
+bool decode_fused_supported(const moe_shape &s);
+hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr, const float *bias,
+                               const moe_expert_weights &w, void *y, int32_t *ids_out, float *w_out, void *ws,
+                               hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+
 }  // namespace moe

@@ -283,3 +283,32 @@ def test_forward_identical_experts_closed_form():
                       top_k=1)
     ffn = oracle.forward(L1)["y"]
     assert rel_l2(to_f64(got["y"], "bf16"), ffn) <= 1e-2
+
+
+def test_forward_graph_capture_replays_match_eager():
+    """moe_forward makes no host synchronisation or device read: it can be captured in a
+    HIP graph; every replay (with eager work and syncs between them) equals the eager run."""
+    li = layer("c2_decode8_bf16")
+    dl = DevLayer(li)
+    sh = lshape(li)
+    ws = pm.alloc_workspace(sh)
+    xs = [dl.x, tdev(synth.make_x(li.shape, batch=1)), tdev(synth.make_x(li.shape, batch=2))]
+    ys = [torch.empty(li.shape.T, li.shape.H, dtype=torch.int16, device="cuda") for _ in xs]
+    for x, y in zip(xs, ys):
+        pm.forward(sh, x, dl.wr, dl.bias, dl.weights, y, ws)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, y in zip(xs, ys):
+            pm.forward(sh, x, dl.wr, dl.bias, dl.weights, y, ws)
+    for r in range(4):
+        for y in ys:
+            y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y, e), f"replay {r}"
+        pm.forward(sh, xs[0], dl.wr, dl.bias, dl.weights, ys[0], ws)   # eager work between replays
+        torch.cuda.synchronize()
