@@ -40,6 +40,28 @@ BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA, TFLOP/s
 
 METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % peak"
 
+# HBM traffic of the dominant kernel from rocprofv3 counter passes (FETCH_SIZE, then
+# WRITE_SIZE, KiB per dispatch), scaled by what the same counters read for a device copy
+# of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
+# the counters were taken on (sha1 of the listed files); otherwise traffic is null.
+COUNTED_TRAFFIC = {
+    "decode1": dict(kernel="decode_fused", fetch_kib=37561.3125, write_kib=244.0625, fetch_scale=2.0,
+                    write_scale=1.0, sources={"prefill_moe_router_amd/csrc/decode_fused.hip":
+                                              "6ea87f5014871c9feb7527477f0384caf9b044da"}),
+}
+
+
+def counted_traffic(config: str, kernel: str):
+    import hashlib
+    rec = COUNTED_TRAFFIC.get(config)
+    if not rec or rec["kernel"] != kernel:
+        return None
+    for path, sha in rec["sources"].items():
+        with open(os.path.join(ROOT, path), "rb") as f:
+            if hashlib.sha1(f.read()).hexdigest() != sha:
+                return None
+    return round(rec["fetch_kib"] * 1024 * rec["fetch_scale"] + rec["write_kib"] * 1024 * rec["write_scale"])
+
 WORKLOADS = {
     "decode1": ("c1_decode1_bf16", "decode, 1 token, bf16: H=2048, E=128, top-8 renorm, I=768, SwiGLU"),
     "decode8": ("c2_decode8_bf16", "decode, 8 tokens, bf16, router bias N(0,0.5): H=2048, E=128, top-8, I=768"),
@@ -217,7 +239,7 @@ def main():
         kb = layer_bytes if fused else gateup_bytes
         achieved = float(np.mean(kb)) / kern_s / 1e9
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None,
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=counted_traffic(args.config, dom_name),
                         kernel=("decode_fused (whole layer in one launch)" if fused
                                 else "gate_up (expert gate/up GEMV + SwiGLU)"),
                         kernel_us=round(kern_s * 1e6, 3), kernel_us_median=round(float(np.median(durs)) * 1e6, 3),

@@ -40,85 +40,6 @@ __device__ int block_exclusive_scan(int *data, int n, int *tmp) {
     return total;
 }
 
-// Single work-group grouping.  LDS: cnt[E] running counts, wcnt[nw][E]
-// per-wave counts of the current round, flags[E], tmp[blockDim].
-__global__ __launch_bounds__(1024) void group_kernel(const int32_t *__restrict__ ids, int P, int E,
-                                                     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted,
-                                                     int32_t *__restrict__ slot_pos, int32_t *__restrict__ active,
-                                                     int32_t *__restrict__ err) {
-    extern __shared__ int smem[];
-    const int nth = blockDim.x, nw = nth / WAVE;
-    int *cnt = smem;
-    int *wcnt = cnt + E;
-    int *flags = wcnt + nw * E;
-    int *tmp = flags + E;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    int nbits = 0;
-    while ((1 << nbits) < E) ++nbits;
-    for (int e = tid; e < E; e += nth) cnt[e] = 0;
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int rounds = (P + nth - 1) / nth;
-    for (int r = 0; r < rounds; ++r) {
-        for (int i = tid; i < nw * E; i += nth) wcnt[i] = 0;
-        __syncthreads();
-        const int p = r * nth + tid;
-        int id = p < P ? ids[p] : -1;
-        const bool valid = p < P;
-        const bool ok = valid && id >= 0 && id < E;
-        if (valid && !ok) atomicOr(err, MOE_DEVERR_BAD_EXPERT_ID);
-        if (!ok) id = 0;
-        uint64_t match = __ballot(ok);
-        for (int b = 0; b < nbits; ++b) {
-            const uint64_t bb = __ballot(ok && ((id >> b) & 1));
-            match &= ((id >> b) & 1) ? bb : ~bb;
-        }
-        const int rank_w = __popcll(match & lt_mask);
-        if (ok && rank_w == 0) wcnt[wave * E + id] = __popcll(match);
-        __syncthreads();
-        if (ok) {
-            int pre = cnt[id];
-            for (int w2 = 0; w2 < wave; ++w2) pre += wcnt[w2 * E + id];
-            slot_pos[p] = pre + rank_w;  // rank inside the expert; made absolute below
-        } else if (valid) {
-            slot_pos[p] = -1;
-        }
-        __syncthreads();
-        for (int e = tid; e < E; e += nth) {
-            int s = 0;
-            for (int w2 = 0; w2 < nw; ++w2) s += wcnt[w2 * E + e];
-            cnt[e] += s;
-        }
-        __syncthreads();
-    }
-    // flags of nonempty experts, then both scans
-    for (int e = tid; e < E; e += nth) flags[e] = cnt[e] > 0 ? 1 : 0;
-    __syncthreads();
-    const int total = block_exclusive_scan(cnt, E, tmp);
-    const int nact = block_exclusive_scan(flags, E, tmp);
-    for (int e = tid; e < E; e += nth) {
-        offsets[e] = cnt[e];
-        const int next = (e + 1 < E) ? cnt[e + 1] : total;
-        if (next > cnt[e]) active[1 + flags[e]] = e;
-    }
-    if (tid == 0) {
-        offsets[E] = total;
-        active[0] = nact;
-    }
-    for (int r = 0; r < rounds; ++r) {
-        const int p = r * nth + tid;
-        if (p < P) {
-            const int id = ids[p];
-            if (id >= 0 && id < E) {
-                const int pos = cnt[id] + slot_pos[p];
-                sorted[pos] = p;
-                slot_pos[p] = pos;
-            }
-        }
-    }
-    // positions past the grouped slots (only when ids were rejected)
-    for (int q = total + tid; q < P; q += nth) sorted[q] = -1;
-}
-
 // active list from existing offsets: [count, nonempty experts ascending]
 __global__ __launch_bounds__(1024) void active_kernel(const int32_t *__restrict__ offsets, int E,
                                                       int32_t *__restrict__ active) {
@@ -134,17 +55,145 @@ __global__ __launch_bounds__(1024) void active_kernel(const int32_t *__restrict_
     if (tid == 0) active[0] = nact;
 }
 
-hipError_t launch_group(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted,
-                        int32_t *slot_pos, int32_t *active, int32_t *err, hipStream_t st) {
+// ---- multi-block grouping: per-chunk stable ranks, then a scan and a scatter ---------------
+
+// Block b takes slots [b*chunk, (b+1)*chunk): ballot-matched stable ranks inside the
+// chunk (written to slot_pos, made absolute by the scatter) and per-expert counts of
+// the chunk (counts[b][E]).
+__global__ __launch_bounds__(1024) void group_count_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
+                                                           int32_t *__restrict__ counts,
+                                                           int32_t *__restrict__ slot_pos, int32_t *__restrict__ err) {
+    extern __shared__ int smem[];
+    const int nth = blockDim.x, nw = nth / WAVE;
+    int *cnt = smem;
+    int *wcnt = cnt + E;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    for (int e = tid; e < E; e += nth) cnt[e] = 0;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
+    const int rounds = (c1 - c0 + nth - 1) / nth;
+    for (int r = 0; r < rounds; ++r) {
+        for (int i = tid; i < nw * E; i += nth) wcnt[i] = 0;
+        __syncthreads();
+        const int p = c0 + r * nth + tid;
+        int id = p < c1 ? ids[p] : -1;
+        const bool valid = p < c1;
+        const bool ok = valid && id >= 0 && id < E;
+        if (valid && !ok) atomicOr(err, MOE_DEVERR_BAD_EXPERT_ID);
+        if (!ok) id = 0;
+        uint64_t match = __ballot(ok);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t bb = __ballot(ok && ((id >> b) & 1));
+            match &= ((id >> b) & 1) ? bb : ~bb;
+        }
+        const int rank_w = __popcll(match & lt_mask);
+        if (ok && rank_w == 0) wcnt[wave * E + id] = __popcll(match);
+        __syncthreads();
+        if (ok) {
+            int pre = cnt[id];
+            for (int w2 = 0; w2 < wave; ++w2) pre += wcnt[w2 * E + id];
+            slot_pos[p] = pre + rank_w;
+        } else if (valid) {
+            slot_pos[p] = -1;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += nth) {
+            int sum = 0;
+            for (int w2 = 0; w2 < nw; ++w2) sum += wcnt[w2 * E + e];
+            cnt[e] += sum;
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < E; e += nth) counts[(size_t)blockIdx.x * E + e] = cnt[e];
+}
+
+// Every block rebuilds the expert offsets from the chunk counts (exclusive scan of the
+// totals) and its own base per expert (offset + counts of the earlier chunks), then
+// places its chunk's slots.  Block 0 also writes the offsets, the list of nonempty
+// experts and, when asked, the m-tile offsets of the grouped GEMM (tiles of mtile_rows).
+__global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
+                                                             int nb, const int32_t *__restrict__ counts,
+                                                             int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ sorted,
+                                                             int32_t *__restrict__ slot_pos,
+                                                             int32_t *__restrict__ active,
+                                                             int32_t *__restrict__ mtile_off, int mtile_rows) {
+    extern __shared__ int smem[];
+    const int nth = blockDim.x;
+    int *tot = smem;            // [E] totals, then exclusive offsets
+    int *base = tot + E;        // [E] this block's base
+    int *flags = base + E;      // [E]
+    int *tmp = flags + E;       // [nth]
+    const int tid = threadIdx.x, b = blockIdx.x;
+    for (int e = tid; e < E; e += nth) {
+        int t = 0, pre = 0;
+        for (int b2 = 0; b2 < nb; ++b2) {
+            const int c = counts[(size_t)b2 * E + e];
+            t += c;
+            pre += b2 < b ? c : 0;
+        }
+        tot[e] = t;
+        base[e] = pre;
+        flags[e] = t > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan(tot, E, tmp);
+    for (int e = tid; e < E; e += nth) base[e] += tot[e];
+    __syncthreads();
+    const int c0 = b * chunk, c1 = min(P, c0 + chunk);
+    for (int p = c0 + tid; p < c1; p += nth) {
+        const int id = ids[p];
+        if (id >= 0 && id < E) {
+            const int pos = base[id] + slot_pos[p];
+            sorted[pos] = p;
+            slot_pos[p] = pos;
+        }
+    }
+    if (b != 0) return;
+    for (int e = tid; e < E; e += nth) offsets[e] = tot[e];
+    if (tid == 0) offsets[E] = total;
+    for (int q = total + tid; q < P; q += nth) sorted[q] = -1;
+    // nonempty experts, ascending
+    const int nact = block_exclusive_scan(flags, E, tmp);
+    for (int e = tid; e < E; e += nth) {
+        const int next = (e + 1 < E) ? tot[e + 1] : total;
+        if (next > tot[e]) active[1 + flags[e]] = e;
+    }
+    if (tid == 0) active[0] = nact;
+    if (mtile_off) {
+        __syncthreads();
+        for (int e = tid; e < E; e += nth) {
+            const int next = (e + 1 < E) ? tot[e + 1] : total;
+            flags[e] = (next - tot[e] + mtile_rows - 1) / mtile_rows;
+        }
+        __syncthreads();
+        const int nt = block_exclusive_scan(flags, E, tmp);
+        for (int e = tid; e < E; e += nth) mtile_off[e] = flags[e];
+        if (tid == 0) mtile_off[E] = nt;
+    }
+}
+
+constexpr int GROUP_CHUNK = 4096;
+
+int group_chunks(int P) { return P > 0 ? (P + GROUP_CHUNK - 1) / GROUP_CHUNK : 1; }
+
+hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted, int32_t *slot_pos,
+                         int32_t *active, int32_t *counts, int32_t *mtile_off, int mtile_rows, int32_t *err,
+                         hipStream_t st) {
     const int E = s.num_experts;
     const int P = s.num_tokens * s.top_k;
-    // LDS budget 64 KB: (2 + nw) * E ints + nth ints
+    const int nb = group_chunks(P);
     int nw = 16;
-    while (nw > 1 && ((size_t)(2 + nw) * E + nw * WAVE) * 4 > 65536) nw >>= 1;
-    const int nth = nw * WAVE;
-    const size_t lds = ((size_t)(2 + nw) * E + nth) * 4;
-    hipLaunchKernelGGL(group_kernel, dim3(1), dim3(nth), lds, st, ids, P, E, offsets, sorted, slot_pos, active,
-                       err);
+    while (nw > 1 && ((size_t)(1 + nw) * E) * 4 > 65536) nw >>= 1;
+    hipLaunchKernelGGL(group_count_kernel, dim3(nb), dim3(nw * WAVE), (size_t)(1 + nw) * E * 4, st, ids, P, E,
+                       GROUP_CHUNK, counts, slot_pos, err);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+    const int nth = 1024;
+    hipLaunchKernelGGL(group_scatter_kernel, dim3(nb), dim3(nth), (size_t)(3 * E + nth) * 4, st, ids, P, E, GROUP_CHUNK,
+                       nb, counts, offsets, sorted, slot_pos, active, mtile_off, mtile_rows);
     return hipGetLastError();
 }
 

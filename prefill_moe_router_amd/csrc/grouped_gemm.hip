@@ -1,0 +1,442 @@
+// grouped_gemm.hip -- MFMA (bf16, fp32 accumulate) grouped GEMM for prefill
+// chunks: the dense contractions of the layer when each expert sees many
+// tokens (the 8192-token chunks of "第 9 章 prefill：最大的瓶颈" §9.8, whose
+// fused path groups tokens by expert on the device, §9.9).
+//
+// One kernel template, three uses:
+//   ROUTER : logits[t][e] = x[t] . Wr[e] + bias[e]                  (fp32 out)
+//   GATEUP : h'[p][i] = w_slot * silu(x_t . Wg[e][i]) * (x_t . Wu[e][i])
+//            for sorted position p of expert e, token t = slot / k     (bf16 out)
+//   DOWN   : o'[slot][n] = h'[p] . Wd[e][n]                          (bf16 out,
+//            rows scattered to token-major slot order for the combine)
+//   DOWN_F32: o[p][n] = h[p] . Wd[e][n] in sorted order, fp32 (the staged call)
+//
+// Tiling: a work-group computes a BM x BN output tile (two of them, gate and
+// up, for GATEUP) with K steps of BK, from double-buffered LDS staged through
+// registers; LDS rows padded by 16 bytes so the 16-byte MFMA operand reads of
+// 16 consecutive rows hit 64 distinct banks.  Tiles are ordered m-tile major
+// (the n-tiles of one m-tile share the gathered A rows) and the block id is
+// remapped so each XCD works on a contiguous range of that order.
+#include <hip/hip_ext.h>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int NXCD = 8;
+
+enum { GM_ROUTER = 0, GM_GATEUP = 1, GM_DOWN = 2, GM_DOWN_F32 = 3 };
+
+#ifndef MOE_GEMM_GM
+#define MOE_GEMM_GM 8   // m-tiles per ordering group of the tile order
+#endif
+
+struct GemmParams {
+    const uint8_t *a;          // x [T][K] (ROUTER, GATEUP) or h' [P][K] (DOWN), bf16
+    const int32_t *sorted;     // sorted slots [P]
+    const int32_t *offsets;    // expert offsets [E+1]
+    const int32_t *mtile_off;  // m-tile offsets [E+1] (tiles of BM rows per expert)
+    const uint8_t *b0, *b1;    // weights [E][N][K] bf16 (b1: up, GATEUP only)
+    const float *wts;          // gate weight per slot (GATEUP)
+    const float *bias;         // router bias [N] or null
+    uint8_t *out;
+    int M, N, K, topk, E;
+    int mt_max, nt;            // logical grid: nt n-tiles x mt_max m-tiles
+};
+
+__device__ __forceinline__ int find_expert(const int32_t *mtile_off, int E, int mt) {
+    int lo = 0, hi = E;  // mtile_off[lo] <= mt < mtile_off[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (mtile_off[mid] <= mt) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// BM x BN output tile per matrix (NB = 2 matrices, gate and up, for GATEUP), K steps
+// of BK, WM x WN waves, each wave MI x NJ blocks of 32x32 per matrix.  LDS rows are
+// padded by 16 bytes so 16 consecutive rows read at one k offset hit distinct banks.
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p) {
+    constexpr int NTH = WM * WN * 64;
+    constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
+    constexpr int MI = BM / WM / 32, NJ = BN / WN / 32;
+    constexpr int CPR = BK / 8;                       // 16-byte chunks per row
+    constexpr int RPP = NTH / CPR;                    // rows staged per pass of all threads
+    constexpr int AR = BM / RPP, BR = BN / RPP;       // staged rows per thread (A, each B)
+    constexpr int GROW = BK * 2 + 16;                 // padded LDS row bytes
+    constexpr int STAGE = (BM + NB * BN) * GROW;
+    static_assert(AR * RPP == BM && BR * RPP == BN, "staging must tile the block");
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ int s_slot[BM];
+    __shared__ float s_scale[BM];
+
+    // ---- which tile ----------------------------------------------------------------------
+    // Logical order: groups of MOE_GEMM_GM consecutive m-tiles, each group swept n-tile by
+    // n-tile, so the tiles running together on one XCD share A rows and weight slices
+    // in its L2; each XCD takes a contiguous range of that order.
+    const int nblk = gridDim.x;
+    const int per_xcd = nblk / NXCD;                 // grid is a multiple of NXCD
+    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+    constexpr int GM = MOE_GEMM_GM;
+    const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
+    const int n_tile = in_grp / GM, mt = grp * GM + in_grp % GM;
+    if (mt >= p.mt_max) return;
+    int e = 0, m0, m_end;
+    if (MODE == GM_ROUTER) {
+        m0 = mt * BM;
+        m_end = p.M;
+        if (m0 >= m_end) return;
+    } else {
+        if (mt >= p.mtile_off[p.E]) return;
+        e = find_expert(p.mtile_off, p.E, mt);
+        m0 = p.offsets[e] + (mt - p.mtile_off[e]) * BM;
+        m_end = p.offsets[e + 1];
+    }
+    const int n0 = n_tile * BN;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t krow = (size_t)p.K * 2;   // bytes per A / B row
+
+    if (MODE != GM_ROUTER) {
+        for (int m = tid; m < BM; m += NTH) {
+            const int pos = min(m0 + m, m_end - 1);
+            const int slot = p.sorted[pos];
+            s_slot[m] = slot;
+            s_scale[m] = (MODE == GM_GATEUP && m0 + m < m_end) ? (p.wts ? p.wts[slot] : 1.f) : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- global sources of the rows this thread stages (CPR chunks of 16 B per row) ------
+    const int sr = tid / CPR, sc = tid % CPR;
+    const uint8_t *arow[AR];
+#pragma unroll
+    for (int i = 0; i < AR; ++i) {
+        const int m = sr + RPP * i;
+        const int pos = min(m0 + m, m_end - 1);
+        const size_t row = MODE == GM_GATEUP ? (size_t)(s_slot[m] / p.topk) : (size_t)pos;
+        arow[i] = p.a + row * krow + sc * 16;
+    }
+    const uint8_t *brow[NB][BR];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+        const uint8_t *base = (b == 0 ? p.b0 : p.b1) + ((size_t)e * p.N + n0) * krow;
+#pragma unroll
+        for (int i = 0; i < BR; ++i) brow[b][i] = base + (size_t)(sr + RPP * i) * krow + sc * 16;
+    }
+
+    // two register sets: a K slice is loaded one whole step before it is written to LDS
+    u32x4_t ra0[AR], rb0[NB][BR], ra1[AR], rb1[NB][BR];
+#define GG_GLOAD(RA, RB, kt)                                                                              \
+    do {                                                                                                  \
+        const size_t ko_ = (size_t)(kt) * BK * 2;                                                         \
+        _Pragma("unroll") for (int i = 0; i < AR; ++i) RA[i] = *reinterpret_cast<const u32x4_t *>(arow[i] + ko_); \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
+            _Pragma("unroll") for (int i = 0; i < BR; ++i) RB[b][i] =                                     \
+                *reinterpret_cast<const u32x4_t *>(brow[b][i] + ko_);                                      \
+    } while (0)
+#define GG_LSTORE(RA, RB, stage)                                                                          \
+    do {                                                                                                  \
+        uint8_t *base_ = lds + (stage) * STAGE;                                                           \
+        _Pragma("unroll") for (int i = 0; i < AR; ++i)                                                    \
+            *reinterpret_cast<u32x4_t *>(base_ + (sr + RPP * i) * GROW + sc * 16) = RA[i];                \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
+            _Pragma("unroll") for (int i = 0; i < BR; ++i)                                                \
+                *reinterpret_cast<u32x4_t *>(base_ + (BM + b * BN + sr + RPP * i) * GROW + sc * 16) = RB[b][i]; \
+    } while (0)
+
+    // ---- MFMA main loop ----------------------------------------------------------------------
+    const int wm = (wave / WN) * (BM / WM), wn = (wave % WN) * (BN / WN);
+    const int lr = lane & 31, lk = (lane >> 5) * 16;          // operand row, k byte offset
+    f32x16_t acc[NB][MI][NJ];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[b][i][j][r] = 0.f;
+
+    // Double-buffered LDS, two register sets.  Step kt computes from LDS stage kt&1
+    // while the global loads of slice kt+2 fill one register set and slice kt+1 (loaded
+    // a step earlier) goes from the other set into stage (kt+1)&1.  Inside a step the
+    // operands of k-slice ks+1 are read from LDS while the MFMAs of slice ks run; the
+    // scheduling hints interleave MFMA, DS-read and VMEM issue.
+    static_assert(NS == 2, "two LDS stages");
+    constexpr int KS = BK / 16;
+    constexpr int NMF = NB * MI * NJ, NDS = MI + NB * NJ;
+    const int KT = p.K / BK;
+    bf16x8_t av[2][MI], bv[2][NB][NJ];
+#define GG_OPLOAD(buf, base_, ks_)                                                                        \
+    do {                                                                                                  \
+        const int ko_ = (ks_) * 32 + lk;                                                                  \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) av[buf][i] =                                       \
+            *reinterpret_cast<const bf16x8_t *>((base_) + (wm + 32 * i + lr) * GROW + ko_);               \
+        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
+            _Pragma("unroll") for (int j = 0; j < NJ; ++j) bv[buf][b][j] =                                \
+                *reinterpret_cast<const bf16x8_t *>((base_) + (BM + b * BN + wn + 32 * j + lr) * GROW + ko_); \
+    } while (0)
+#define GG_STEP(kt_, RA_LOAD, RB_LOAD, RA_STORE, RB_STORE)                                                 \
+    do {                                                                                                  \
+        GG_GLOAD(RA_LOAD, RB_LOAD, min((kt_) + 2, KT - 1));                                               \
+        const uint8_t *base = lds + ((kt_) & 1) * STAGE;                                                  \
+        _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                               \
+            const int cur = ks & 1;                                                                       \
+            if (ks + 1 < KS) GG_OPLOAD(cur ^ 1, base, ks + 1);                                            \
+            _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+                _Pragma("unroll") for (int i = 0; i < MI; ++i)                                            \
+                    _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[b][i][j] =                         \
+                        __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[cur][i], bv[cur][b][j], acc[b][i][j], 0, 0, 0); \
+        }                                                                                                 \
+        _Pragma("unroll") for (int q = 0; q < KS * NMF; ++q) {                                            \
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
+            if (q < (KS - 1) * NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    \
+            if (q < AR + NB * BR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
+        }                                                                                                 \
+        GG_LSTORE(RA_STORE, RB_STORE, ((kt_) + 1) & 1);                                                   \
+        __syncthreads();                                                                                  \
+        GG_OPLOAD(0, lds + (((kt_) + 1) & 1) * STAGE, 0);                                                 \
+    } while (0)
+    GG_GLOAD(ra0, rb0, 0);
+    GG_GLOAD(ra1, rb1, min(1, KT - 1));
+    GG_LSTORE(ra0, rb0, 0);
+    __syncthreads();
+    GG_OPLOAD(0, lds, 0);
+    for (int kt = 0; kt < KT; kt += 2) {
+        GG_STEP(kt, ra0, rb0, ra1, rb1);
+        if (kt + 1 < KT) GG_STEP(kt + 1, ra1, rb1, ra0, rb0);
+    }
+#undef GG_STEP
+#undef GG_GLOAD
+#undef GG_LSTORE
+#undef GG_OPLOAD
+
+    // ---- epilogue ------------------------------------------------------------------------------
+    // acc[.][i][j][r] holds C[row][col] with row = wm + 32i + 8(r/4) + 4(lane/32) + r%4,
+    // col = wn + 32j + lane%32.
+    if (MODE == GM_GATEUP || MODE == GM_DOWN) {
+        // bf16 outputs: each wave transposes its tile through LDS and stores whole
+        // 16-byte row pieces (the main loop is done with LDS after the last barrier)
+        constexpr int TR = MI * 32, TC = NJ * 32, PITCH = TC + 8;
+        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * TR * PITCH;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ml = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    float v;
+                    if (MODE == GM_GATEUP) v = s_scale[wm + ml] * swiglu(acc[0][i][j][r], acc[NB - 1][i][j][r]);
+                    else v = acc[0][i][j][r];
+                    ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(v);
+                }
+            }
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        constexpr int CPRow = TC / 8;   // 16-byte pieces per tile row
+        for (int q = lane; q < TR * CPRow; q += 64) {
+            const int ml = q / CPRow, ch = q % CPRow;
+            const int m = wm + ml;
+            if (m0 + m >= m_end) continue;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
+            const size_t row = MODE == GM_GATEUP ? (size_t)(m0 + m) : (size_t)s_slot[m];
+            *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + row * p.N + n0 + wn + ch * 8) = v;
+        }
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int m = wm + 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            if (m0 + m >= m_end) continue;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int n = n0 + wn + 32 * j + lr;
+                if (MODE == GM_ROUTER) {
+                    const float b = p.bias ? p.bias[n] : 0.f;
+                    reinterpret_cast<float *>(p.out)[(size_t)(m0 + m) * p.N + n] = acc[0][i][j][r] + b;
+                } else {
+                    reinterpret_cast<float *>(p.out)[(size_t)(m0 + m) * p.N + n] = acc[0][i][j][r];
+                }
+            }
+        }
+    }
+}
+
+// Tile shapes (rows per m-tile = the grouping's kGroupedTileM for the expert GEMMs,
+// columns per n-tile and matrix, wave grid, K step).
+#ifndef MOE_GU_CFG
+#define MOE_GU_CFG 128, 128, 2, 4, 64   // gate/up: 128 x (128 + 128), 8 waves
+#endif
+#ifndef MOE_DN_CFG
+#define MOE_DN_CFG 128, 256, 2, 4, 64   // down: 128 x 256, 8 waves
+#endif
+#define MOE_R_CFG 128, 128, 2, 2, 64    // router: x . Wr
+template <int BM_, int BN_, int WM_, int WN_, int BK_, int NS_ = 2>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
+};
+using CfgGU = TileCfg<MOE_GU_CFG>;
+using CfgDN = TileCfg<MOE_DN_CFG>;
+using CfgR = TileCfg<MOE_R_CFG>;
+static_assert(CfgGU::BM == kGroupedTileM && CfgDN::BM == kGroupedTileM, "m-tiles follow the grouping");
+
+// m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / kGroupedTileM)
+__global__ __launch_bounds__(1024) void mtile_offsets_kernel(const int32_t *__restrict__ offsets, int E,
+                                                             int32_t *__restrict__ mtile_off) {
+    __shared__ int s[1025];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += blockDim.x) s[e] = (offsets[e + 1] - offsets[e] + kGroupedTileM - 1) / kGroupedTileM;
+    __syncthreads();
+    if (tid == 0) {
+        int run = 0;
+        for (int e = 0; e < E; ++e) {
+            const int c = s[e];
+            s[e] = run;
+            run += c;
+        }
+        s[E] = run;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += blockDim.x) mtile_off[e] = s[e];
+}
+
+// y[t][n] = sum_j o'[t*k + j][n]  (bf16 rows of one token, fp32 sum, one rounding)
+__global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__restrict__ o, uint16_t *__restrict__ y,
+                                                           int T, int H, int k) {
+    const int t = blockIdx.x;
+    const int n8 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
+    if (t >= T || n8 >= H) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(o + ((size_t)t * k + j) * H + n8);
+        acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
+        acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
+        acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
+        acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+    }
+    uint4 r;
+    r.x = pack_bf16x2(acc[0], acc[1]);
+    r.y = pack_bf16x2(acc[2], acc[3]);
+    r.z = pack_bf16x2(acc[4], acc[5]);
+    r.w = pack_bf16x2(acc[6], acc[7]);
+    *reinterpret_cast<uint4 *>(y + (size_t)t * H + n8) = r;
+}
+
+bool grouped_supported(const moe_shape &s) {
+    return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.hidden % CfgDN::BN == 0 &&
+           s.hidden % CfgGU::BK == 0 && s.intermediate % CfgGU::BN == 0 && s.intermediate % CfgDN::BK == 0;
+}
+
+bool router_mfma_supported(const moe_shape &s) {
+    return s.act_dtype == MOE_BF16 && s.num_experts % CfgR::BN == 0 && s.hidden % CfgR::BK == 0;
+}
+
+template <int MODE, class C>
+static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
+    constexpr size_t stage_bytes = C::NS * (size_t)(C::BM + NB * C::BN) * (C::BK * 2 + 16);
+    constexpr size_t epi_bytes = (size_t)C::WM * C::WN * (C::BM / C::WM) * (C::BN / C::WN + 8) * 2;
+    constexpr size_t lds = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
+    static_assert(lds <= 158 * 1024, "LDS budget");
+    static bool attr_done = false;
+    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS>;
+    if (!attr_done) {
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (r != hipSuccess) return r;
+        attr_done = true;
+    }
+    int nblk = (prm.mt_max + MOE_GEMM_GM - 1) / MOE_GEMM_GM * MOE_GEMM_GM * prm.nt;
+    nblk = (nblk + NXCD - 1) / NXCD * NXCD;
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(C::WM * C::WN * 64), lds, st, ev0, ev1, 0, prm);
+    else
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(C::WM * C::WN * 64), lds, st, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    GemmParams prm{};
+    prm.a = static_cast<const uint8_t *>(x);
+    prm.b0 = static_cast<const uint8_t *>(wr);
+    prm.bias = bias;
+    prm.out = reinterpret_cast<uint8_t *>(logits);
+    prm.M = s.num_tokens;
+    prm.N = s.num_experts;
+    prm.K = s.hidden;
+    prm.topk = s.top_k;
+    prm.E = 1;
+    prm.mt_max = (s.num_tokens + CfgR::BM - 1) / CfgR::BM;
+    prm.nt = s.num_experts / CfgR::BN;
+    return gemm_launch<GM_ROUTER, CfgR>(prm, st, ev0, ev1);
+}
+
+hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, hipStream_t st) {
+    hipLaunchKernelGGL(mtile_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, s.num_experts, mtile_off);
+    return hipGetLastError();
+}
+
+static int mt_max_of(const moe_shape &s) {
+    const long P = (long)s.num_tokens * s.top_k;
+    // sum over experts of ceil(cnt/BM) <= P/BM + (number of nonempty experts)
+    return (int)(P / kGroupedTileM + std::min<long>(s.num_experts, P));
+}
+
+hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
+                              const int32_t *sorted, const int32_t *mtile_off, const float *wts, void *h,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    GemmParams prm{};
+    prm.a = static_cast<const uint8_t *>(x);
+    prm.sorted = sorted;
+    prm.offsets = offsets;
+    prm.mtile_off = mtile_off;
+    prm.b0 = static_cast<const uint8_t *>(w.w_gate);
+    prm.b1 = static_cast<const uint8_t *>(w.w_up);
+    prm.wts = wts;
+    prm.out = static_cast<uint8_t *>(h);
+    prm.M = s.num_tokens * s.top_k;
+    prm.N = s.intermediate;
+    prm.K = s.hidden;
+    prm.topk = s.top_k;
+    prm.E = s.num_experts;
+    prm.mt_max = mt_max_of(s);
+    prm.nt = s.intermediate / CfgGU::BN;
+    return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
+}
+
+hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, const int32_t *offsets,
+                            const int32_t *sorted, const int32_t *mtile_off, const void *h, void *o, bool f32_sorted,
+                            hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    GemmParams prm{};
+    prm.a = static_cast<const uint8_t *>(h);
+    prm.sorted = sorted;
+    prm.offsets = offsets;
+    prm.mtile_off = mtile_off;
+    prm.b0 = static_cast<const uint8_t *>(w.w_down);
+    prm.out = static_cast<uint8_t *>(o);
+    prm.M = s.num_tokens * s.top_k;
+    prm.N = s.hidden;
+    prm.K = s.intermediate;
+    prm.topk = s.top_k;
+    prm.E = s.num_experts;
+    prm.mt_max = mt_max_of(s);
+    prm.nt = s.hidden / CfgDN::BN;
+    if (f32_sorted) return gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
+    return gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
+}
+
+hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st) {
+    dim3 grid(s.num_tokens, (s.hidden / 8 + 255) / 256);
+    hipLaunchKernelGGL(combine_rows_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t *>(o),
+                       static_cast<uint16_t *>(y), s.num_tokens, s.hidden, s.top_k);
+    return hipGetLastError();
+}
+
+}  // namespace moe

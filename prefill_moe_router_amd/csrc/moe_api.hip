@@ -56,9 +56,15 @@ moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
 }
 
 moe_status check_path(const moe_shape *s) {
-    // the grouped MFMA family covers bf16 / MXFP4 weights; fp32 runs on the decode family
-    if (s->path == MOE_PATH_GROUPED) return MOE_ERR_UNSUPPORTED;
+    // the grouped MFMA family covers bf16 experts; fp32 runs on the decode family
+    if (s->path == MOE_PATH_GROUPED && !grouped_supported(*s)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
+}
+
+// kernel family for the expert FFN: AUTO takes the grouped MFMA GEMMs above 8 tokens
+bool use_grouped(const moe_shape &s) {
+    if (s.path == MOE_PATH_GROUPED) return true;
+    return s.path == MOE_PATH_AUTO && s.num_tokens > 8 && grouped_supported(s);
 }
 
 template <class T>
@@ -112,8 +118,8 @@ moe_status moe_group_tokens(const moe_shape *shape, const int32_t *topk_ids, int
     const WsLayout L = ws_layout(*shape);
     hipStream_t st = static_cast<hipStream_t>(stream);
     // T == 0 still defines the offsets (all zero)
-    MOE_TRY(launch_group(*shape, topk_ids, expert_offsets, sorted_slots, slot_pos, at<int32_t>(ws, L.active),
-                         at<int32_t>(ws, L.ctrl), st));
+    MOE_TRY(launch_group2(*shape, topk_ids, expert_offsets, sorted_slots, slot_pos, at<int32_t>(ws, L.active),
+                          at<int32_t>(ws, L.gcounts), nullptr, kGroupedTileM, at<int32_t>(ws, L.ctrl), st));
     return MOE_OK;
 }
 
@@ -130,6 +136,15 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *x, const moe_exper
     MOE_CHECK(check_ws(shape, ws, ws_bytes));
     const WsLayout L = ws_layout(*shape);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (use_grouped(*shape)) {
+        int32_t *mtile = at<int32_t>(ws, L.mtile);
+        MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, st));
+        MOE_TRY(launch_gateup_mfma(*shape, x, *w, expert_offsets, sorted_slots, mtile, nullptr, at<void>(ws, L.h), st,
+                                   nullptr, nullptr));
+        MOE_TRY(launch_down_mfma(*shape, *w, expert_offsets, sorted_slots, mtile, at<void>(ws, L.h), expert_out, true,
+                                 st, nullptr, nullptr));
+        return MOE_OK;
+    }
     int32_t *active = at<int32_t>(ws, L.active);
     MOE_TRY(launch_active(*shape, expert_offsets, active, st));
     MOE_TRY(launch_decode_gateup(*shape, x, *w, expert_offsets, sorted_slots, active, nullptr, at<void>(ws, L.h), st));
@@ -154,9 +169,10 @@ namespace {
 
 const char *const kStagesStaged = "router_logits,topk,group,gate_up,down,combine";
 const char *const kStagesFused = "decode_fused";
+const char *const kStagesGrouped = "router_logits,topk,group,gate_up,down,combine";
 
 bool use_fused(const moe_shape &s) {
-    return s.path != MOE_PATH_GROUPED && s.num_tokens <= 8 && decode_fused_supported(s);
+    return !use_grouped(s) && s.num_tokens <= 8 && decode_fused_supported(s);
 }
 
 // Event pair (start, stop) of launch i, taken from ev[2i], ev[2i+1] when present.
@@ -204,9 +220,29 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     float *logits = at<float>(ws, L.logits), *o = at<float>(ws, L.o);
     void *h = at<void>(ws, L.h);
     int32_t *err = at<int32_t>(ws, L.ctrl);
+    if (use_grouped(*shape)) {
+        int32_t *mtile = at<int32_t>(ws, L.mtile);
+        if (router_mfma_supported(*shape)) {
+            MOE_TRY(launch_router_mfma(*shape, x, w_router, bias, logits, st, se.start(0), se.stop(0)));
+        } else {
+            MOE_TRY(around(se, 0, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
+        }
+        MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
+        MOE_TRY(around(se, 2, st, [&] {
+            return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), mtile,
+                                 kGroupedTileM, err, st);
+        }));
+        MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, wts, h, st, se.start(3), se.stop(3)));
+        MOE_TRY(launch_down_mfma(*shape, *w, offsets, sorted, mtile, h, o, false, st, se.start(4), se.stop(4)));
+        MOE_TRY(around(se, 5, st, [&] { return launch_combine_rows(*shape, o, y, st); }));
+        return MOE_OK;
+    }
     MOE_TRY(around(se, 0, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
     MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
-    MOE_TRY(around(se, 2, st, [&] { return launch_group(*shape, ids, offsets, sorted, slot_pos, active, err, st); }));
+    MOE_TRY(around(se, 2, st, [&] {
+        return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), nullptr,
+                             kGroupedTileM, err, st);
+    }));
     MOE_TRY(around(se, 3, st, [&] {
         return launch_decode_gateup(*shape, x, *w, offsets, sorted, active, nullptr, h, st);
     }));
@@ -238,6 +274,7 @@ moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *
 
 const char *moe_forward_stages(const moe_shape *shape) {
     if (check_shape(shape) != MOE_OK) return "";
+    if (use_grouped(*shape)) return kStagesGrouped;
     return use_fused(*shape) ? kStagesFused : kStagesStaged;
 }
 

@@ -12,12 +12,18 @@ namespace moe {
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
+// rows of one m-tile of the grouped GEMM (the grouping emits m-tile offsets for it)
+#ifndef MOE_TILE_M
+#define MOE_TILE_M 128
+#endif
+constexpr int kGroupedTileM = MOE_TILE_M;
+
 inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word, the rest zero between calls.
 struct WsLayout {
-    size_t ctrl, logits, ids, wts, offsets, sorted, slot_pos, active, h, o, total;
+    size_t ctrl, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, gcounts, h, o, total;
 };
 
 inline WsLayout ws_layout(const moe_shape &s) {
@@ -38,6 +44,8 @@ inline WsLayout ws_layout(const moe_shape &s) {
     L.sorted = take(P * 4);
     L.slot_pos = take(P * 4);
     L.active = take((E + 1) * 4);
+    L.mtile = take((E + 1) * 4);
+    L.gcounts = take((P > 0 ? (P + 4095) / 4096 : 1) * E * 4);
     L.h = take(P * I * act_bytes(s.act_dtype));
     L.o = take(P * H * 4);
     L.total = off;
@@ -51,9 +59,12 @@ hipError_t launch_router_logits(const moe_shape &s, const void *x, const void *w
                                 float *logits, hipStream_t st);
 // top-k + softmax (+ renorm) over logits rows -> ids [T][k] ascending, w [T][k]
 hipError_t launch_topk(const moe_shape &s, const float *logits, int32_t *ids, float *w, hipStream_t st);
-// stable grouping; active = [count, expert ids with a nonempty group ascending]
-hipError_t launch_group(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted,
-                        int32_t *slot_pos, int32_t *active, int32_t *err, hipStream_t st);
+// multi-block stable grouping (chunks of 4096 slots): counts [chunks][E] scratch;
+// mtile_off (optional) receives the m-tile offsets for tiles of mtile_rows rows
+int group_chunks(int P);
+hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted, int32_t *slot_pos,
+                         int32_t *active, int32_t *counts, int32_t *mtile_off, int mtile_rows, int32_t *err,
+                         hipStream_t st);
 // active = [count, nonempty experts ascending] from existing offsets
 hipError_t launch_active(const moe_shape &s, const int32_t *offsets, int32_t *active, hipStream_t st);
 // h[p][i] = (wts ? wts[slot] : 1) * silu(Wg[e,i].x_t) * (Wu[e,i].x_t), act dtype, sorted order
@@ -72,5 +83,22 @@ bool decode_fused_supported(const moe_shape &s);
 hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr, const float *bias,
                                const moe_expert_weights &w, void *y, int32_t *ids_out, float *w_out, void *ws,
                                hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
+
+// MFMA grouped GEMM family (see grouped_gemm.hip)
+bool grouped_supported(const moe_shape &s);
+bool router_mfma_supported(const moe_shape &s);
+hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, hipStream_t st);
+// h'[p][i] = (wts ? wts[slot] : 1) * silu(g) * u, bf16, sorted order
+hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
+                              const int32_t *sorted, const int32_t *mtile_off, const float *wts, void *h,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// f32_sorted: o[p][n] fp32 in sorted order; else o'[slot][n] bf16 in slot (token-major) order
+hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, const int32_t *offsets,
+                            const int32_t *sorted, const int32_t *mtile_off, const void *h, void *o, bool f32_sorted,
+                            hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// y[t] = sum_j o'[t*k+j] (bf16 rows)
+hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st);
 
 }  // namespace moe

@@ -312,3 +312,43 @@ def test_forward_graph_capture_replays_match_eager():
             assert torch.equal(y, e), f"replay {r}"
         pm.forward(sh, xs[0], dl.wr, dl.bias, dl.weights, ys[0], ws)   # eager work between replays
         torch.cuda.synchronize()
+
+
+# ---- grouped MFMA family ----------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 8, 129])
+def test_forward_grouped_path_forced(T):
+    """The MFMA grouped family must match the oracle at any T, also decode sizes."""
+    note(f"grouped forced T={T}")
+    li = layer_of(synth.Shape(T, 2048, 128, 8, 768, "bf16", "bf16", bias="normal"), batch=50 + T)
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    compare_forward(li, got, tokens=_sample(T, 64), label=f"grouped T={T}")
+
+
+def test_forward_grouped_ragged_zipf():
+    """333 tokens with a strongly skewed router: partial m-tiles, empty experts."""
+    sh_ = synth.Shape(333, 256, 64, 6, 256, "bf16", "bf16", bias="zipf")
+    li = synth.make_layer(sh_, beta=2.0)
+    got = run_forward(DevLayer(li))
+    counts = np.bincount(got["ids"].ravel(), minlength=64)
+    note(f"  group sizes max {counts.max()} empty {(counts == 0).sum()}")
+    compare_forward(li, got, label="grouped ragged zipf")
+
+
+def test_staged_expert_ffn_grouped_path():
+    """moe_expert_ffn on the grouped family: fp32 expert outputs in sorted order."""
+    li = layer_of(synth.Shape(77, 256, 16, 4, 128, "bf16", "bf16", bias="normal"))
+    dl = DevLayer(li)
+    T, K, E, H = li.shape.T, li.shape.K, li.shape.E, li.shape.H
+    sh = lshape(li, path=pm.PATH_GROUPED)
+    ws = pm.alloc_workspace(sh)
+    ref = oracle.router(oracle_layer(li))
+    ids_np = ref["ids"]
+    off, srt, pos = oracle.group(ids_np, E)
+    obuf, o = guarded(T * K * H, torch.float32)
+    pm.expert_ffn(sh, dl.x, dl.weights, tdev(off), tdev(srt), o.view(T * K, H), ws)
+    torch.cuda.synchronize()
+    assert canary_ok(obuf, T * K * H, torch.float32)
+    oref = oracle.expert_pairs(oracle_layer(li), srt // K, ids_np.reshape(-1)[srt])
+    r = rel_l2(o.view(T * K, H).cpu().numpy(), oref)
+    assert r <= 1e-2, r
