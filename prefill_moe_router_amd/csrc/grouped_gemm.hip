@@ -37,7 +37,8 @@ struct GemmParams {
     const int32_t *sorted;     // sorted slots [P]
     const int32_t *offsets;    // expert offsets [E+1]
     const int32_t *mtile_off;  // m-tile offsets [E+1] (tiles of BM rows per expert)
-    const uint8_t *b0, *b1;    // weights [E][N][K] bf16 (b1: up, GATEUP only)
+    const uint8_t *b0, *b1;    // weights [E][N][K] bf16, or MXFP4 codes [E][N][K/2] (b1: up, GATEUP only)
+    const uint8_t *s0, *s1;    // MXFP4 E8M0 scales [E][N][K/32]
     const float *wts;          // gate weight per slot (GATEUP)
     const float *bias;         // router bias [N] or null
     uint8_t *out;
@@ -58,7 +59,7 @@ __device__ __forceinline__ int find_expert(const int32_t *mtile_off, int E, int 
 // BM x BN output tile per matrix (NB = 2 matrices, gate and up, for GATEUP), K steps
 // of BK, WM x WN waves, each wave MI x NJ blocks of 32x32 per matrix.  LDS rows are
 // padded by 16 bytes so 16 consecutive rows read at one k offset hit distinct banks.
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p) {
     constexpr int NTH = WM * WN * 64;
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
@@ -124,27 +125,68 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
     for (int b = 0; b < NB; ++b) {
         const uint8_t *base = (b == 0 ? p.b0 : p.b1) + ((size_t)e * p.N + n0) * krow;
 #pragma unroll
-        for (int i = 0; i < BR; ++i) brow[b][i] = base + (size_t)(sr + RPP * i) * krow + sc * 16;
+        for (int i = 0; i < BR; ++i) brow[b][i] = MX ? nullptr : base + (size_t)(sr + RPP * i) * krow + sc * 16;
+    }
+    // MXFP4 weights: a 16-byte chunk of E2M1 codes (32 K elements, one scale block) per
+    // (weight row, chunk); dequantised to bf16 while it is written to LDS
+    constexpr int CQ = BK / 32;                                   // code chunks per row and K step
+    constexpr int BQ = MX ? NB * BN * CQ / NTH : 1;               // code chunks staged per thread
+    static_assert(!MX || BQ * NTH == NB * BN * CQ, "MXFP4 staging must tile the block");
+    const uint8_t *bqrow[BQ], *bqsc[BQ];
+    int bqlds[BQ];
+#pragma unroll
+    for (int i = 0; i < BQ; ++i) {
+        const int idx = tid + NTH * i, r = idx / CQ, c = idx % CQ;   // r: row over both matrices
+        const int b = r / BN, rr = r % BN;
+        const size_t grow = (size_t)e * p.N + n0 + rr;
+        bqrow[i] = MX ? (b == 0 ? p.b0 : p.b1) + grow * (size_t)(p.K / 2) + c * 16 : nullptr;
+        bqsc[i] = MX ? (b == 0 ? p.s0 : p.s1) + grow * (size_t)(p.K / 32) + c : nullptr;
+        bqlds[i] = (BM + r) * GROW + c * 64;
     }
 
     // two register sets: a K slice is loaded one whole step before it is written to LDS
-    u32x4_t ra0[AR], rb0[NB][BR], ra1[AR], rb1[NB][BR];
-#define GG_GLOAD(RA, RB, kt)                                                                              \
+    constexpr int BRX = MX ? 1 : BR;
+    u32x4_t ra0[AR], rb0[NB][BRX], ra1[AR], rb1[NB][BRX];
+    u32x4_t rq0[BQ], rq1[BQ];
+    uint32_t rs0[BQ], rs1[BQ];
+#define GG_GLOAD(RA, RB, RQ, RS, kt)                                                                      \
     do {                                                                                                  \
         const size_t ko_ = (size_t)(kt) * BK * 2;                                                         \
         _Pragma("unroll") for (int i = 0; i < AR; ++i) RA[i] = *reinterpret_cast<const u32x4_t *>(arow[i] + ko_); \
-        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
-            _Pragma("unroll") for (int i = 0; i < BR; ++i) RB[b][i] =                                     \
-                *reinterpret_cast<const u32x4_t *>(brow[b][i] + ko_);                                      \
+        if constexpr (MX) {                                                                               \
+            _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
+                RQ[i] = *reinterpret_cast<const u32x4_t *>(bqrow[i] + (size_t)(kt) * (BK / 2));           \
+                RS[i] = bqsc[i][(kt) * CQ];                                                               \
+            }                                                                                             \
+        } else {                                                                                          \
+            _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+                _Pragma("unroll") for (int i = 0; i < BR; ++i) RB[b][i] =                                 \
+                    *reinterpret_cast<const u32x4_t *>(brow[b][i] + ko_);                                  \
+        }                                                                                                 \
     } while (0)
-#define GG_LSTORE(RA, RB, stage)                                                                          \
+#define GG_LSTORE(RA, RB, RQ, RS, stage)                                                                  \
     do {                                                                                                  \
         uint8_t *base_ = lds + (stage) * STAGE;                                                           \
         _Pragma("unroll") for (int i = 0; i < AR; ++i)                                                    \
             *reinterpret_cast<u32x4_t *>(base_ + (sr + RPP * i) * GROW + sc * 16) = RA[i];                \
-        _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                    \
-            _Pragma("unroll") for (int i = 0; i < BR; ++i)                                                \
-                *reinterpret_cast<u32x4_t *>(base_ + (BM + b * BN + sr + RPP * i) * GROW + sc * 16) = RB[b][i]; \
+        if constexpr (MX) {                                                                               \
+            _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
+                const float s_ = e8m0_to_f32(RS[i]);                                                      \
+                _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                           \
+                    const uint32_t cw = RQ[i][w];                                                         \
+                    u32x4_t o_;                                                                           \
+                    o_[0] = fp4x2_to_bf16x2<0>(cw, s_);                                                   \
+                    o_[1] = fp4x2_to_bf16x2<1>(cw, s_);                                                   \
+                    o_[2] = fp4x2_to_bf16x2<2>(cw, s_);                                                   \
+                    o_[3] = fp4x2_to_bf16x2<3>(cw, s_);                                                   \
+                    *reinterpret_cast<u32x4_t *>(base_ + bqlds[i] + w * 16) = o_;                         \
+                }                                                                                         \
+            }                                                                                             \
+        } else {                                                                                          \
+            _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
+                _Pragma("unroll") for (int i = 0; i < BR; ++i)                                            \
+                    *reinterpret_cast<u32x4_t *>(base_ + (BM + b * BN + sr + RPP * i) * GROW + sc * 16) = RB[b][i]; \
+        }                                                                                                 \
     } while (0)
 
     // ---- MFMA main loop ----------------------------------------------------------------------
@@ -179,9 +221,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
             _Pragma("unroll") for (int j = 0; j < NJ; ++j) bv[buf][b][j] =                                \
                 *reinterpret_cast<const bf16x8_t *>((base_) + (BM + b * BN + wn + 32 * j + lr) * GROW + ko_); \
     } while (0)
-#define GG_STEP(kt_, RA_LOAD, RB_LOAD, RA_STORE, RB_STORE)                                                 \
+#define GG_STEP(kt_, RA_LOAD, RB_LOAD, RQ_LOAD, RS_LOAD, RA_STORE, RB_STORE, RQ_STORE, RS_STORE)            \
     do {                                                                                                  \
-        GG_GLOAD(RA_LOAD, RB_LOAD, min((kt_) + 2, KT - 1));                                               \
+        GG_GLOAD(RA_LOAD, RB_LOAD, RQ_LOAD, RS_LOAD, min((kt_) + 2, KT - 1));                             \
         const uint8_t *base = lds + ((kt_) & 1) * STAGE;                                                  \
         _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                               \
             const int cur = ks & 1;                                                                       \
@@ -194,20 +236,20 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         _Pragma("unroll") for (int q = 0; q < KS * NMF; ++q) {                                            \
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                            \
             if (q < (KS - 1) * NDS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                    \
-            if (q < AR + NB * BR) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                      \
+            if (q < AR + (MX ? 2 * BQ : NB * BR)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      \
         }                                                                                                 \
-        GG_LSTORE(RA_STORE, RB_STORE, ((kt_) + 1) & 1);                                                   \
+        GG_LSTORE(RA_STORE, RB_STORE, RQ_STORE, RS_STORE, ((kt_) + 1) & 1);                               \
         __syncthreads();                                                                                  \
         GG_OPLOAD(0, lds + (((kt_) + 1) & 1) * STAGE, 0);                                                 \
     } while (0)
-    GG_GLOAD(ra0, rb0, 0);
-    GG_GLOAD(ra1, rb1, min(1, KT - 1));
-    GG_LSTORE(ra0, rb0, 0);
+    GG_GLOAD(ra0, rb0, rq0, rs0, 0);
+    GG_GLOAD(ra1, rb1, rq1, rs1, min(1, KT - 1));
+    GG_LSTORE(ra0, rb0, rq0, rs0, 0);
     __syncthreads();
     GG_OPLOAD(0, lds, 0);
     for (int kt = 0; kt < KT; kt += 2) {
-        GG_STEP(kt, ra0, rb0, ra1, rb1);
-        if (kt + 1 < KT) GG_STEP(kt + 1, ra1, rb1, ra0, rb0);
+        GG_STEP(kt, ra0, rb0, rq0, rs0, ra1, rb1, rq1, rs1);
+        if (kt + 1 < KT) GG_STEP(kt + 1, ra1, rb1, rq1, rs1, ra0, rb0, rq0, rs0);
     }
 #undef GG_STEP
 #undef GG_GLOAD
@@ -329,15 +371,16 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
 }
 
 bool grouped_supported(const moe_shape &s) {
-    return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.hidden % CfgDN::BN == 0 &&
-           s.hidden % CfgGU::BK == 0 && s.intermediate % CfgGU::BN == 0 && s.intermediate % CfgDN::BK == 0;
+    return s.act_dtype == MOE_BF16 && (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4) &&
+           s.hidden % CfgDN::BN == 0 && s.hidden % CfgGU::BK == 0 && s.intermediate % CfgGU::BN == 0 &&
+           s.intermediate % CfgDN::BK == 0;
 }
 
 bool router_mfma_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 && s.num_experts % CfgR::BN == 0 && s.hidden % CfgR::BK == 0;
 }
 
-template <int MODE, class C>
+template <int MODE, class C, bool MX = false>
 static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
     constexpr size_t stage_bytes = C::NS * (size_t)(C::BM + NB * C::BN) * (C::BK * 2 + 16);
@@ -345,7 +388,7 @@ static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
     static_assert(lds <= 158 * 1024, "LDS budget");
     static bool attr_done = false;
-    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS>;
+    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -399,6 +442,8 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.mtile_off = mtile_off;
     prm.b0 = static_cast<const uint8_t *>(w.w_gate);
     prm.b1 = static_cast<const uint8_t *>(w.w_up);
+    prm.s0 = w.s_gate;
+    prm.s1 = w.s_up;
     prm.wts = wts;
     prm.out = static_cast<uint8_t *>(h);
     prm.M = s.num_tokens * s.top_k;
@@ -408,6 +453,7 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.E = s.num_experts;
     prm.mt_max = mt_max_of(s);
     prm.nt = s.intermediate / CfgGU::BN;
+    if (s.weight_dtype == MOE_MXFP4) return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
     return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
 }
 
@@ -420,6 +466,7 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
     prm.offsets = offsets;
     prm.mtile_off = mtile_off;
     prm.b0 = static_cast<const uint8_t *>(w.w_down);
+    prm.s0 = w.s_down;
     prm.out = static_cast<uint8_t *>(o);
     prm.M = s.num_tokens * s.top_k;
     prm.N = s.hidden;
@@ -428,8 +475,10 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
     prm.E = s.num_experts;
     prm.mt_max = mt_max_of(s);
     prm.nt = s.hidden / CfgDN::BN;
-    if (f32_sorted) return gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
-    return gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
+    const bool mx = s.weight_dtype == MOE_MXFP4;
+    if (f32_sorted) return mx ? gemm_launch<GM_DOWN_F32, CfgDN, true>(prm, st, ev0, ev1)
+                              : gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
+    return mx ? gemm_launch<GM_DOWN, CfgDN, true>(prm, st, ev0, ev1) : gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
 }
 
 hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st) {

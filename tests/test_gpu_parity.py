@@ -352,3 +352,22 @@ def test_staged_expert_ffn_grouped_path():
     oref = oracle.expert_pairs(oracle_layer(li), srt // K, ids_np.reshape(-1)[srt])
     r = rel_l2(o.view(T * K, H).cpu().numpy(), oref)
     assert r <= 1e-2, r
+
+
+def test_forward_grouped_mxfp4_small():
+    """MXFP4 experts on the grouped MFMA family (codes dequantised to bf16 in LDS)."""
+    li = layer_of(synth.Shape(77, 256, 16, 4, 128, "bf16", "mxfp4", bias="normal"))
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    compare_forward(li, got, label="grouped mxfp4 small")
+
+
+def test_forward_parity_mxfp4_prefill_sampled():
+    """4096-token MXFP4 chunk (H=4096, E=256, top-8, I=1024): all ids checked, y sampled."""
+    name = "c4_mxfp4_prefill4096"
+    note(f"forward parity {name} (sampled)")
+    li = layer(name)
+    got = run_forward(DevLayer(li))
+    ref = oracle.router(oracle_layer(li))
+    mism = (got["ids"] != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any()
+    compare_forward(li, got, tokens=_sample(li.shape.T, 24), label=name)
