@@ -9,25 +9,29 @@
 // device ("第 9 章 prefill：最大的瓶颈" §9.9) and every token-expert pair is
 // computed whatever the batch (no 8-entry group limit, §9.5).
 //
-// One work-group per CU, all co-resident; phases are separated by a grid
-// barrier: a 64-bit arrival counter in the workspace that only grows (a
+// One work-group per CU, all co-resident; gate/up and down are separated by a
+// grid barrier: a 64-bit arrival counter in the workspace that only grows (the
 // barrier completes when it reaches the next multiple of the grid size), with
 // relaxed atomics only.  Data that crosses work-groups (logits, h') is written
 // with write-through agent-scope stores and read with agent-scope loads, so
 // no cache writeback or invalidation is needed at the barrier.  Every wait is
 // bounded and sets MOE_DEVERR_TIMEOUT instead of hanging.
-//   0. router: expert rows spread one per wave over the grid; logits to the
-//      workspace (write-through stores).                          -- barrier
-//   1. every work-group redundantly takes the top-k of all T tokens and
-//      groups the T*k slots by expert in LDS (tiny: T*k <= 256).
+//   0. router: expert rows spread one per wave over the grid; each logit goes
+//      to the workspace as one self-validating 64-bit word (value | call tag),
+//      so no barrier is needed before it is read.
+//   1. every work-group redundantly takes the top-k of all T tokens (polling
+//      until all words carry this call's tag) and groups the T*k slots by
+//      expert in LDS (tiny: T*k <= 256).
 //   2. gate/up: one wave per (active expert, row i); the two 16-byte-chunked
 //      rows are dotted with the tokens of that expert (x staged in LDS);
 //      h'[slot][i] = w_slot * silu(g) * u goes to the workspace.   -- barrier
 //      (each wave issues its first down-projection loads before waiting)
-//   3. down + combine: one wave (or wave slice) per output row n streams
-//      Wd[e][n][:] of every active expert and accumulates
-//      y[t][n] = sum over t's slots of Wd[e][n].h'[slot] -- the weighted sum
-//      over the token's experts needs no second pass.
+//   3. down + combine: a work-group owns a tile of output rows, its waves
+//      split the active experts; each wave streams the tile's rows of Wd[e]
+//      once and dots them with e's h' rows (staged in LDS), and the tile's
+//      y[t][n] = sum over t's slots of Wd[e][n].h'[slot] is summed over the
+//      waves in LDS -- the weighted sum over the token's experts needs no
+//      second pass.
 #include <hip/hip_ext.h>
 
 #include "moe_device.h"
@@ -37,11 +41,11 @@ namespace moe {
 
 constexpr int FWPB = 8;                 // waves per work-group
 constexpr int FTHREADS = FWPB * WAVE;
-constexpr int FMAX_T = 8;
+constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
-constexpr int FDB = 8;                  // experts per down-projection load batch
-constexpr size_t FLDS_MAX = 144 * 1024; // staged x / h' bytes per work-group
+constexpr int FMAX_RT = 32;             // rows of a down-projection tile (8 rows x 4 lane groups)
+constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
 constexpr uint64_t SPIN_TICKS = 20000000ull;  // 0.2 s of the 100 MHz real-time clock
 
 struct FusedParams {
@@ -51,7 +55,7 @@ struct FusedParams {
     uint8_t *y;
     int32_t *ids_out;
     float *w_out;
-    float *logits;    // workspace [T][E]
+    uint64_t *logits; // workspace [FMAX_T][E] words: logit bits | (call tag << 32)
     uint8_t *hbuf;    // workspace [P][I] (activation dtype)
     uint64_t *bar;    // workspace control word: grid-barrier arrivals (only grows)
     int32_t *err;
@@ -149,37 +153,70 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // kept in ascending expert id until k are kept (ties go to the lower id).
 // Writes ids (ascending) and weights (softmax over all E at the kept ids,
 // renormalised over the kept set when renorm) to ids[0..k) / w[0..k).
+// The logits arrive as self-validating words (value | call tag << 32), written by the
+// waves that own the router rows; the wave re-reads until every word carries this
+// call's tag (bounded wait, MOE_DEVERR_TIMEOUT on expiry).
 template <int NJ>
-__device__ __forceinline__ void wave_topk(const float *logits, int E, int K, int renorm, int *ids, float *w,
-                                          int32_t *ids_g, float *w_g) {
+__device__ __forceinline__ void wave_topk(const uint64_t *logits, uint32_t tag, int E, int K, int renorm, int *ids,
+                                          float *w, int32_t *ids_g, float *w_g, int32_t *err) {
     const int lane = threadIdx.x & 63;
     constexpr int nj = NJ;
     float v[NJ];
     uint32_t key[NJ];
     float m = -__builtin_inff();
+    uint64_t word[NJ];
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        bool ready = true;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int e = lane + 64 * j;
+            word[j] = e < E ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : ((uint64_t)tag << 32);
+            ready = ready && (uint32_t)(word[j] >> 32) == tag;
+        }
+        if (__ballot(!ready) == 0ull) break;
+        if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+            if (lane == 0) atomicOr(err, MOE_DEVERR_TIMEOUT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int e = lane + 64 * j;
         const bool ok = e < E;
-        v[j] = ok ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : -__builtin_inff();
+        v[j] = ok ? __uint_as_float((uint32_t)word[j]) : -__builtin_inff();
         key[j] = ok ? f32_order_key(v[j]) : 0u;
         m = fmaxf(m, v[j]);
     }
     m = wave_max_u(m);
+    // Bit by bit from the top: `avail` keys share the prefix chosen so far, `need` of
+    // them are still to be kept.  Once they are equal, every key sharing the prefix is
+    // kept and the remaining bits need not be looked at (the common case after a dozen
+    // bits); otherwise the walk ends at bit 0 with the threshold key itself.
     uint32_t prefix = 0;
-    int need = K;
-    for (int b = 31; b >= 0; --b) {
+    int need = K, avail = E;
+    int b = 31;
+    for (; b >= 0; --b) {
         const uint32_t cand = prefix | (1u << b);
-        const uint32_t hi = cand >> b;
+        const uint32_t hi = cand >> b;   // odd, so the key 0 of a padding lane never matches
         int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[j] != 0u && (key[j] >> b) == hi));
-        if (cnt >= need)
+        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot((key[j] >> b) == hi));
+        if (cnt >= need) {
             prefix = cand;
-        else
+            avail = cnt;
+        } else {
             need -= cnt;
+            avail -= cnt;
+        }
+        if (avail == need) break;
     }
-    // kept: key > prefix, or key == prefix among the first `need` such in id order
+    const int sh = b < 0 ? 0 : b;        // keys are compared on bits [sh, 32)
+    const uint32_t pfx = prefix >> sh;
+    // kept: top bits above the prefix, or equal to it among the first `need` such in id
+    // order (all of them when the walk stopped early)
     const uint64_t lt = lanemask_lt();
     int eq_before = 0, sel_before = 0;
     float z = 0.f;
@@ -188,11 +225,12 @@ __device__ __forceinline__ void wave_topk(const float *logits, int E, int K, int
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const bool valid = key[j] != 0u;
-        const bool eq = valid && key[j] == prefix;
+        const uint32_t top = key[j] >> sh;
+        const bool eq = valid && top == pfx;
         const uint64_t eqm = __ballot(eq);
         const int eq_rank = eq_before + __popcll(eqm & lt);
         eq_before += __popcll(eqm);
-        sel[j] = valid && (key[j] > prefix || (eq && eq_rank < need));
+        sel[j] = valid && (top > pfx || (eq && eq_rank < need));
         pe[j] = valid ? __expf(v[j] - m) : 0.f;
         if (!renorm || sel[j]) z += pe[j];
     }
@@ -222,11 +260,14 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // staged x, later staged h'
     __shared__ __attribute__((aligned(16))) int s_ids[FMAX_P + 4];
     __shared__ float s_w[FMAX_P];
-    __shared__ int s_sorted[FMAX_P];
+    __shared__ int s_tok[FMAX_P];     // token of each slot, in expert-sorted order
+    __shared__ float s_wq[FMAX_P];    // routing weight of each slot, in expert-sorted order
     __shared__ __attribute__((aligned(16))) int s_first[FMAX_P + 4];
     __shared__ int s_act_e[FMAX_P], s_act_start[FMAX_P], s_act_cnt[FMAX_P];
     __shared__ int s_nact;
+    __shared__ float s_part[FWPB * FMAX_T * FMAX_RT];   // down partials [wave][token][tile row]
     __shared__ uint64_t s_base;
+    __shared__ uint32_t s_tag;
 
     const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, P = T * K;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -236,7 +277,18 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const bool f32 = A::EPC == 4;
     const int ab = f32 ? 4 : 2;
 
-    if (tid == 0) s_base = bar_base(p.bar, G);
+    if (tid == 0) {
+        s_base = bar_base(p.bar, G);
+        // one grid barrier per call, so base/G counts the completed calls on this workspace
+        s_tag = (uint32_t)(s_base / (uint64_t)G) + 1u;
+        s_nact = 0;
+    }
+    for (int i = tid; i < FWPB * FMAX_T * FMAX_RT; i += FTHREADS) s_part[i] = 0.f;
+    // pad the id tables to a multiple of 4 with a sentinel no id equals or exceeds
+    if (tid < 4) {
+        s_ids[P + tid] = 0x7fffffff;
+        s_first[P + tid] = 0x7fffffff;
+    }
 
     // ---- phase 0: router logits (row loads first, then x staged into LDS) ----------------
     {
@@ -254,37 +306,33 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         for (int ee = e; ee < E; ee += NW) {
             if (ee != e) load_chunks<A, CR>(p.wr + (size_t)ee * nch * 16, nullptr, nch, lane, WAVE, q, sc);
             const float b = p.bias ? p.bias[ee] : 0.f;
+            // every row t < FMAX_T is rewritten each call (rows past T with the tag only), so
+            // a word this call reads was last written by this call or by the one before it
 #pragma unroll
             for (int t = 0; t < FMAX_T; ++t) {
-                if (t < T) {
-                    const float v = dpp_sum64(row_dot<A, CR>(q, sc, smem + t * xrow, nch, lane, WAVE));
-                    if (lane == 63)
-                        __hip_atomic_store(p.logits + (size_t)t * E + ee, v + b, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
+                const float v = t < T ? dpp_sum64(row_dot<A, CR>(q, sc, smem + t * xrow, nch, lane, WAVE)) + b
+                                      : 0.f;
+                if (lane == 63)
+                    __hip_atomic_store(p.logits + (size_t)t * E + ee,
+                                       (uint64_t)__float_as_uint(v) | ((uint64_t)s_tag << 32), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
             }
         }
     }
-    bar_arrive(p.bar);
-    bar_wait(p.bar, s_base + (uint64_t)G, p.err);
-
     // ---- phase 1: top-k + softmax per token (wave t), then grouping ----------------------
     if (wave < T) {
         const bool out = blockIdx.x == 0;
-        const float *lg = p.logits + (size_t)wave * E;
+        const uint64_t *lg = p.logits + (size_t)wave * E;
         int *ii = s_ids + wave * K;
         float *ww = s_w + wave * K;
         int32_t *ig = out && p.ids_out ? p.ids_out + wave * K : nullptr;
         float *wg = out && p.w_out ? p.w_out + wave * K : nullptr;
-        if (E <= 64) wave_topk<1>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 128) wave_topk<2>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 256) wave_topk<4>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 512) wave_topk<8>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else wave_topk<16>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        if (E <= 64) wave_topk<1>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
+        else if (E <= 128) wave_topk<2>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
+        else if (E <= 256) wave_topk<4>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
+        else if (E <= 512) wave_topk<8>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
+        else wave_topk<16>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
     }
-    __syncthreads();
-    // pad the id table to a multiple of 4 with a sentinel no id equals or exceeds
-    if (tid < 4) s_ids[P + tid] = 0x7fffffff;
     __syncthreads();
     const int P4 = (P + 3) >> 2;
     int my_e = 0, my_less = 0, my_cnt = 0;
@@ -301,10 +349,12 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             before += (v.x == my_e && q < tid) + (v.y == my_e && q + 1 < tid) + (v.z == my_e && q + 2 < tid) +
                       (v.w == my_e && q + 3 < tid);
         }
-        s_sorted[my_less + before] = tid;
+        s_tok[my_less + before] = tid / K;
+        s_wq[my_less + before] = s_w[tid];
         s_first[tid] = before == 0 ? my_e : 0x7fffffff;   // first slot of its expert carries the id
+        const uint64_t firsts = __ballot(before == 0);      // distinct experts: one first slot each
+        if (lane == 0) atomicAdd(&s_nact, (int)__popcll(firsts));
     }
-    if (tid < 4) s_first[P + tid] = 0x7fffffff;
     __syncthreads();
     if (tid < P && s_first[tid] == my_e) {
         int dl = 0;
@@ -318,11 +368,6 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         s_act_start[dl] = my_less;
         s_act_cnt[dl] = my_cnt;
     }
-    if (tid == 0) {
-        int n = 0;
-        for (int q = 0; q < P; ++q) n += s_first[q] != 0x7fffffff;
-        s_nact = n;
-    }
     __syncthreads();
     const int U = s_nact;
 
@@ -330,79 +375,87 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     {
         const int nch = H / F::EPC;
         const size_t xrow = (size_t)H * ab;
-        const long nitems = (long)U * I;
+        const int nitems = U * I;
         uint4 gq[CG], uq[CG], gq2[CG], uq2[CG];
         uint32_t gs[CG], us[CG], gs2[CG], us2[CG];
-        auto fetch = [&](long q, uint4 (&g)[CG], uint32_t (&gsc)[CG], uint4 (&u)[CG], uint32_t (&usc)[CG]) {
-            const int uu = (int)(q / I), i = (int)(q - (long)uu * I);
+        auto fetch = [&](int q, uint4 (&g)[CG], uint32_t (&gsc)[CG], uint4 (&u)[CG], uint32_t (&usc)[CG]) {
+            const int uu = q / I, i = q - uu * I;
             const size_t rsel = (size_t)s_act_e[uu] * I + i;
             load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * nch : nullptr, nch, lane, WAVE, g, gsc);
             load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * nch : nullptr, nch, lane, WAVE, u, usc);
         };
-        auto consume = [&](long q, const uint4 (&g)[CG], const uint32_t (&gsc)[CG], const uint4 (&u)[CG],
+        auto consume = [&](int q, const uint4 (&g)[CG], const uint32_t (&gsc)[CG], const uint4 (&u)[CG],
                            const uint32_t (&usc)[CG]) {
-            const int uu = (int)(q / I), i = (int)(q - (long)uu * I);
+            const int uu = q / I, i = q - uu * I;
             const int start = s_act_start[uu], cnt = s_act_cnt[uu];
 #pragma unroll
             for (int c = 0; c < FMAX_T; ++c) {
                 if (c < cnt) {
-                    const int slot = s_sorted[start + c];
-                    const uint8_t *xa = smem + (size_t)(slot / K) * xrow;
+                    const uint8_t *xa = smem + (size_t)s_tok[start + c] * xrow;
                     const float gv = dpp_sum64(row_dot<F, CG>(g, gsc, xa, nch, lane, WAVE));
                     const float uv = dpp_sum64(row_dot<F, CG>(u, usc, xa, nch, lane, WAVE));
-                    if (lane == 63) store_act_sc1(p.hbuf, (size_t)(start + c) * I + i, s_w[slot] * swiglu(gv, uv), f32);
+                    if (lane == 63)
+                        store_act_sc1(p.hbuf, (size_t)(start + c) * I + i, s_wq[start + c] * swiglu(gv, uv), f32);
                 }
             }
         };
-        long q = gw;
+        int q = gw;
         if (q < nitems) fetch(q, gq, gs, uq, us);
         while (q < nitems) {
-            const long q2 = q + NW;
+            const int q2 = q + NW;
             if (q2 < nitems) fetch(q2, gq2, gs2, uq2, us2);
             consume(q, gq, gs, uq, us);
             if (q2 >= nitems) break;
-            const long q3 = q2 + NW;
+            const int q3 = q2 + NW;
             if (q3 < nitems) fetch(q3, gq, gs, uq, us);
             consume(q2, gq2, gs2, uq2, us2);
             q = q3;
         }
     }
 
-    // ---- barrier, with the first down-projection loads issued before the wait -------------
-    // The wave's work is the sequence (row item, batch of DB active experts); two
-    // batches are in flight, the first one issued before the barrier wait.
-    constexpr int DB = CD >= 4 ? 2 : (CD == 2 ? 4 : 8);
+    // ---- phase 3 set-up: down projection by (row tile, expert) --------------------------
+    // A work-group owns tiles of DR*rpw consecutive output rows; its wave w takes the
+    // active experts w, w+FWPB, ...  An item (tile, expert) is DR rows x I of Wd[e]
+    // (one contiguous block), held in registers; each h' row read from LDS serves all
+    // DR rows.  Per-wave partial sums go to s_part by token and row, and the work-group
+    // adds the FWPB partials in a fixed order at the end of each tile.  Two items are in
+    // flight, both issued before the barrier wait.
+    constexpr int DR_REG = (CG >= 8 ? 8 : 16) / (CD >= 4 ? 4 : CD);   // register budget
+    constexpr int DR = DR_REG > 8 ? 8 : DR_REG;
     const int nchd = I / F::EPC;
-    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);   // lanes per output row
-    const int rpw = WAVE / lpr;                                       // rows per wave
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);   // lanes per row
+    const int rpw = WAVE / lpr;                                       // lane groups per wave
     const int lg = lane / lpr, li = lane % lpr;
-    const int nrow_items = (H + rpw - 1) / rpw;
-    const int nbat = (U + DB - 1) / DB;
-    const int nrw = gw < nrow_items ? (nrow_items - 1 - gw) / NW + 1 : 0;
-    const int total = nrw * nbat;
-    uint4 dqa[DB][CD], dqb[DB][CD];
-    uint32_t dsa[DB][CD], dsb[DB][CD];
-    auto load_seq = [&](int sq, uint4 (&dq)[DB][CD], uint32_t (&ds)[DB][CD]) {
-        const int n = (gw + NW * (sq / nbat)) * rpw + lg;
-        const int u0 = (sq % nbat) * DB;
+    const int RT = DR * rpw;                                          // rows per tile
+    const int ntile = (H + RT - 1) / RT;
+    const int ntw = (int)blockIdx.x < ntile ? (ntile - 1 - (int)blockIdx.x) / G + 1 : 0;
+    const int nexp = wave < U ? (U - 1 - wave) / FWPB + 1 : 0;
+    const int total = ntw * nexp;
+    uint4 dqa[DR][CD], dqb[DR][CD];
+    uint32_t dsa[DR][CD], dsb[DR][CD];
+    auto load_item = [&](int sq, uint4 (&dq)[DR][CD], uint32_t (&ds)[DR][CD]) {
+        const int j = sq / nexp, k = sq - j * nexp;
+        const int n0 = ((int)blockIdx.x + G * j) * RT + lg;
+        const size_t e = (size_t)s_act_e[wave + FWPB * k];
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-            const int u = u0 + b;
-            const bool okb = u < U && n < H;
-            const size_t rsel = (size_t)(okb ? s_act_e[u] : 0) * H + (okb ? n : 0);
+        for (int r = 0; r < DR; ++r) {
+            const int n = n0 + r * rpw;
+            const bool okr = n < H;
+            const size_t rsel = e * H + (okr ? n : 0);
             const uint8_t *row = p.wd + rsel * nchd * 16;
 #pragma unroll
             for (int c = 0; c < CD; ++c) {
                 const int ch = li + lpr * c;
-                const bool ok = okb && ch < nchd;
-                dq[b][c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-                ds[b][c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
+                const bool ok = okr && ch < nchd;
+                dq[r][c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+                ds[r][c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
             }
         }
     };
     bar_arrive(p.bar);
-    if (total > 0) load_seq(0, dqa, dsa);
-    bar_wait(p.bar, s_base + 2 * (uint64_t)G, p.err);
+    if (total > 0) load_item(0, dqa, dsa);
+    if (total > 1) load_item(1, dqb, dsb);
+    bar_wait(p.bar, s_base + (uint64_t)G, p.err);
 
     // stage h' (all P slots, sorted order) into LDS with agent-scope loads
     {
@@ -414,57 +467,72 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     }
     __syncthreads();
 
-    // ---- phase 3: down projection + weighted combine, by output row ------------------------
+    // ---- phase 3: down projection + weighted combine, by output row tile -------------------
     {
         const size_t hrow = (size_t)I * ab;
-        float acc[FMAX_T];
+        float *part = s_part + (size_t)wave * FMAX_T * FMAX_RT;
+        auto consume = [&](int sq, const uint4 (&dq)[DR][CD], const uint32_t (&ds)[DR][CD]) {
+            const int k = sq % nexp;
+            const int u = wave + FWPB * k;
+            const int start = s_act_start[u], cnt = s_act_cnt[u];
+            for (int c = 0; c < cnt; ++c) {
+                const int q = start + c;
+                const int t = s_tok[q];
+                const uint8_t *ha = smem + (size_t)q * hrow;
+                float d[DR];
 #pragma unroll
-        for (int t = 0; t < FMAX_T; ++t) acc[t] = 0.f;
-        auto consume = [&](int sq, const uint4 (&dq)[DB][CD], const uint32_t (&ds)[DB][CD]) {
-            const int n = (gw + NW * (sq / nbat)) * rpw + lg;
-            const int u0 = (sq % nbat) * DB;
+                for (int r = 0; r < DR; ++r) d[r] = 0.f;
 #pragma unroll
-            for (int b = 0; b < DB; ++b) {
-                const int u = u0 + b;
-                if (u < U) {
-                    const int start = s_act_start[u], cnt = s_act_cnt[u];
-                    for (int c = 0; c < cnt; ++c) {
-                        const int slot = s_sorted[start + c];
-                        const int t = slot / K;
-                        const uint8_t *ha = smem + (size_t)(start + c) * hrow;
-                        float d = 0.f;
+                for (int cc = 0; cc < CD; ++cc) {
+                    const int ch = li + lpr * cc;
+                    if (ch < nchd) {
+                        const uint8_t *hp = ha + (size_t)ch * F::XB;
 #pragma unroll
-                        for (int cc = 0; cc < CD; ++cc) {
-                            const int ch = li + lpr * cc;
-                            if (ch < nchd) d = chunk_dot<F>(dq[b][cc], ds[b][cc], ha + (size_t)ch * F::XB, d);
-                        }
-#pragma unroll
-                        for (int tt = 0; tt < FMAX_T; ++tt) acc[tt] += (t == tt) ? d : 0.f;
+                        for (int r = 0; r < DR; ++r) d[r] = chunk_dot<F>(dq[r][cc], ds[r][cc], hp, d[r]);
                     }
                 }
-            }
-            if (sq % nbat == nbat - 1) {   // last batch of this row: reduce and store
 #pragma unroll
-                for (int t = 0; t < FMAX_T; ++t) {
-                    if (t < T) {
-                        const float v = group_sum_last(acc[t], lpr);
-                        if (li == lpr - 1 && n < H) {
-                            if (f32)
-                                reinterpret_cast<float *>(p.y)[(size_t)t * H + n] = v;
-                            else
-                                reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
-                        }
-                    }
-                    acc[t] = 0.f;
+                for (int r = 0; r < DR; ++r) {
+                    const float v = group_sum_last(d[r], lpr);
+                    if (li == lpr - 1) atomicAdd(part + t * FMAX_RT + r * rpw + lg, v);
                 }
             }
         };
-        for (int sq = 0; sq < total; sq += 2) {
-            if (sq + 1 < total) load_seq(sq + 1, dqb, dsb);
-            consume(sq, dqa, dsa);
-            if (sq + 1 >= total) break;
-            if (sq + 2 < total) load_seq(sq + 2, dqa, dsa);
-            consume(sq + 1, dqb, dsb);
+        // the tile's sum over the work-group's waves, in wave order, then cleared
+        auto finish_tile = [&](int j) {
+            __syncthreads();
+            const int n0 = ((int)blockIdx.x + G * j) * RT;
+            for (int i = tid; i < T * RT; i += FTHREADS) {
+                const int t = i / RT, r = i - t * RT;
+                float v = 0.f;
+#pragma unroll
+                for (int w = 0; w < FWPB; ++w) {
+                    float *pp = s_part + ((size_t)w * FMAX_T + t) * FMAX_RT + r;
+                    v += *pp;
+                    *pp = 0.f;
+                }
+                const int n = n0 + r;
+                if (n < H) {
+                    if (f32)
+                        reinterpret_cast<float *>(p.y)[(size_t)t * H + n] = v;
+                    else
+                        reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
+                }
+            }
+            __syncthreads();
+        };
+        int sq = 0;
+        for (int j = 0; j < ntw; ++j) {
+            for (int k = 0; k < nexp; ++k, ++sq) {
+                if (sq & 1) {
+                    consume(sq, dqb, dsb);
+                    if (sq + 2 < total) load_item(sq + 2, dqb, dsb);
+                } else {
+                    consume(sq, dqa, dsa);
+                    if (sq + 2 < total) load_item(sq + 2, dqa, dsa);
+                }
+            }
+            finish_tile(j);
         }
     }
 }
@@ -569,7 +637,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     prm.ids_out = ids_out;
     prm.w_out = w_out;
     uint8_t *wsb = static_cast<uint8_t *>(ws);
-    prm.logits = reinterpret_cast<float *>(wsb + L.logits);
+    prm.logits = reinterpret_cast<uint64_t *>(wsb + L.tagged);
     prm.hbuf = wsb + L.h;
     prm.bar = reinterpret_cast<uint64_t *>(wsb + L.ctrl + 8);
     prm.err = reinterpret_cast<int32_t *>(wsb + L.ctrl);

@@ -18,12 +18,15 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 #endif
 constexpr int kGroupedTileM = MOE_TILE_M;
 
+// largest token count the fused single-kernel decode path takes
+constexpr int kFusedMaxTokens = 8;
+
 inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word, the rest zero between calls.
 struct WsLayout {
-    size_t ctrl, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, gcounts, h, o, total;
+    size_t ctrl, tagged, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, gcounts, h, o, total;
 };
 
 inline WsLayout ws_layout(const moe_shape &s) {
@@ -37,6 +40,7 @@ inline WsLayout ws_layout(const moe_shape &s) {
         return at;
     };
     L.ctrl = take(256);
+    L.tagged = take((size_t)kFusedMaxTokens * E * 8);   // fused decode: logit | call tag words
     L.logits = take(T * E * 4);
     L.ids = take(P * 4);
     L.wts = take(P * 4);
