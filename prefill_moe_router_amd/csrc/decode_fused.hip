@@ -44,7 +44,7 @@ constexpr int FTHREADS = FWPB * WAVE;
 constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
-constexpr int FMAX_RT = 32;             // rows of a down-projection tile (8 rows x 4 lane groups)
+constexpr int FMAX_RT = 8;              // rows of a down-projection tile
 constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
 constexpr uint64_t SPIN_TICKS = 20000000ull;  // 0.2 s of the 100 MHz real-time clock
 
@@ -117,20 +117,33 @@ __device__ __forceinline__ void load_chunks(const uint8_t *row, const uint8_t *s
 template <class F, int C>
 __device__ __forceinline__ float row_dot(const uint4 (&q)[C], const uint32_t (&s)[C], const uint8_t *act, int nch,
                                          int lane0, int stride) {
+    // 16-byte activation chunks: branch-free (chunks past the row end read chunk 0 and
+    // are discarded), so that all LDS reads can be issued before the first dot product.
+    // MXFP4 chunks take 64 bytes of activations each; there the reads stay per chunk.
     float acc = 0.f;
 #pragma unroll
     for (int c = 0; c < C; ++c) {
         const int ch = lane0 + stride * c;
-        if (ch < nch) acc = chunk_dot<F>(q[c], s[c], act + (size_t)ch * F::XB, acc);
+        const bool ok = ch < nch;
+        if constexpr (F::XB == 16) {
+            const float v = chunk_dot<F>(q[c], s[c], act + (size_t)(ok ? ch : 0) * F::XB, acc);
+            acc = ok ? v : acc;
+        } else {
+            if (ok) acc = chunk_dot<F>(q[c], s[c], act + (size_t)ch * F::XB, acc);
+        }
     }
     return acc;
 }
 
-// total of each group of `lpr` (16, 32 or 64) lanes, in the group's last lane
-__device__ __forceinline__ float group_sum_last(float v, int lpr) {
-    v = dpp_sum16(v);
-    if (lpr >= 32) v += dpp_f<0x142, 0xa>(v, 0.f);
-    if (lpr == 64) v += dpp_f<0x143, 0xc>(v, 0.f);
+// total of each group of LR consecutive lanes (8, 16, 32 or 64), in the group's last lane
+template <int LR>
+__device__ __forceinline__ float lane_group_sum(float v) {
+    v += dpp_f<0x111>(v, 0.f);   // row_shr:1
+    v += dpp_f<0x112>(v, 0.f);   // row_shr:2
+    v += dpp_f<0x114>(v, 0.f);   // row_shr:4
+    if (LR >= 16) v += dpp_f<0x118>(v, 0.f);          // row_shr:8
+    if (LR >= 32) v += dpp_f<0x142, 0xa>(v, 0.f);     // row_bcast:15
+    if (LR >= 64) v += dpp_f<0x143, 0xc>(v, 0.f);     // row_bcast:31
     return v;
 }
 
@@ -414,42 +427,37 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     }
 
     // ---- phase 3 set-up: down projection by (row tile, expert) --------------------------
-    // A work-group owns tiles of DR*rpw consecutive output rows; its wave w takes the
-    // active experts w, w+FWPB, ...  An item (tile, expert) is DR rows x I of Wd[e]
-    // (one contiguous block), held in registers; each h' row read from LDS serves all
-    // DR rows.  Per-wave partial sums go to s_part by token and row, and the work-group
-    // adds the FWPB partials in a fixed order at the end of each tile.  Two items are in
-    // flight, both issued before the barrier wait.
-    constexpr int DR_REG = (CG >= 8 ? 8 : 16) / (CD >= 4 ? 4 : CD);   // register budget
-    constexpr int DR = DR_REG > 8 ? 8 : DR_REG;
+    // A work-group owns tiles of DR consecutive output rows; its wave w takes the active
+    // experts w, w+FWPB, ...  An item (tile, expert) is DR rows x I of Wd[e] (one
+    // contiguous block) held in registers: lane group r (LR lanes) takes row r, each lane
+    // NC of its 16-byte chunks, so a row's dot product is summed over LR lanes only.
+    // Per-wave partial sums go to s_part by token and row, and the work-group adds the
+    // FWPB partials in a fixed order at the end of each tile.  Two items are in flight,
+    // both issued before the barrier wait.
+    constexpr int DR_REG = ((CG >= 8 || F::SCALED) ? 8 : 16) / (CD >= 4 ? 4 : CD);   // register budget
+    constexpr int DR = DR_REG > 8 ? 8 : DR_REG;                        // rows per tile
+    constexpr int LR = WAVE / DR;                                      // lanes per row
+    constexpr int NC = DR * CD;                                        // chunks per lane
     const int nchd = I / F::EPC;
-    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);   // lanes per row
-    const int rpw = WAVE / lpr;                                       // lane groups per wave
-    const int lg = lane / lpr, li = lane % lpr;
-    const int RT = DR * rpw;                                          // rows per tile
-    const int ntile = (H + RT - 1) / RT;
+    const int rr = lane / LR, li = lane % LR;
+    const int ntile = (H + DR - 1) / DR;
     const int ntw = (int)blockIdx.x < ntile ? (ntile - 1 - (int)blockIdx.x) / G + 1 : 0;
     const int nexp = wave < U ? (U - 1 - wave) / FWPB + 1 : 0;
     const int total = ntw * nexp;
-    uint4 dqa[DR][CD], dqb[DR][CD];
-    uint32_t dsa[DR][CD], dsb[DR][CD];
-    auto load_item = [&](int sq, uint4 (&dq)[DR][CD], uint32_t (&ds)[DR][CD]) {
+    uint4 dqa[NC], dqb[NC];
+    uint32_t dsa[NC], dsb[NC];
+    auto load_item = [&](int sq, uint4 (&dq)[NC], uint32_t (&ds)[NC]) {
         const int j = sq / nexp, k = sq - j * nexp;
-        const int n0 = ((int)blockIdx.x + G * j) * RT + lg;
-        const size_t e = (size_t)s_act_e[wave + FWPB * k];
+        const int n = ((int)blockIdx.x + G * j) * DR + rr;
+        const bool okr = n < H;
+        const size_t rsel = (size_t)s_act_e[wave + FWPB * k] * H + (okr ? n : 0);
+        const uint8_t *row = p.wd + rsel * nchd * 16;
 #pragma unroll
-        for (int r = 0; r < DR; ++r) {
-            const int n = n0 + r * rpw;
-            const bool okr = n < H;
-            const size_t rsel = e * H + (okr ? n : 0);
-            const uint8_t *row = p.wd + rsel * nchd * 16;
-#pragma unroll
-            for (int c = 0; c < CD; ++c) {
-                const int ch = li + lpr * c;
-                const bool ok = okr && ch < nchd;
-                dq[r][c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-                ds[r][c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
-            }
+        for (int c = 0; c < NC; ++c) {
+            const int ch = li + LR * c;
+            const bool ok = okr && ch < nchd;
+            dq[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
+            ds[c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
         }
     };
     bar_arrive(p.bar);
@@ -457,13 +465,26 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     if (total > 1) load_item(1, dqb, dsb);
     bar_wait(p.bar, s_base + (uint64_t)G, p.err);
 
-    // stage h' (all P slots, sorted order) into LDS with agent-scope loads
+    // stage h' (all P slots, sorted order) into LDS with agent-scope loads, eight words
+    // in flight per thread
     {
         const int n8 = P * I * ab / 8;
+        const int nst = FTHREADS;
         const uint64_t *src = reinterpret_cast<const uint64_t *>(p.hbuf);
         uint64_t *dst = reinterpret_cast<uint64_t *>(smem);
-        for (int i = tid; i < n8; i += FTHREADS)
-            dst[i] = __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int i0 = tid; i0 < n8; i0 += 8 * nst) {
+            uint64_t v[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int i = i0 + b * nst;
+                v[b] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+            }
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const int i = i0 + b * nst;
+                if (i < n8) dst[i] = v[b];
+            }
+        }
     }
     __syncthreads();
 
@@ -471,7 +492,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     {
         const size_t hrow = (size_t)I * ab;
         float *part = s_part + (size_t)wave * FMAX_T * FMAX_RT;
-        auto consume = [&](int sq, const uint4 (&dq)[DR][CD], const uint32_t (&ds)[DR][CD]) {
+        auto consume = [&](int sq, const uint4 (&dq)[NC], const uint32_t (&ds)[NC]) {
             const int k = sq % nexp;
             const int u = wave + FWPB * k;
             const int start = s_act_start[u], cnt = s_act_cnt[u];
@@ -479,37 +500,23 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                 const int q = start + c;
                 const int t = s_tok[q];
                 const uint8_t *ha = smem + (size_t)q * hrow;
-                float d[DR];
-#pragma unroll
-                for (int r = 0; r < DR; ++r) d[r] = 0.f;
-#pragma unroll
-                for (int cc = 0; cc < CD; ++cc) {
-                    const int ch = li + lpr * cc;
-                    if (ch < nchd) {
-                        const uint8_t *hp = ha + (size_t)ch * F::XB;
-#pragma unroll
-                        for (int r = 0; r < DR; ++r) d[r] = chunk_dot<F>(dq[r][cc], ds[r][cc], hp, d[r]);
-                    }
-                }
-#pragma unroll
-                for (int r = 0; r < DR; ++r) {
-                    const float v = group_sum_last(d[r], lpr);
-                    if (li == lpr - 1) atomicAdd(part + t * FMAX_RT + r * rpw + lg, v);
-                }
+                float d = row_dot<F, NC>(dq, ds, ha, nchd, li, LR);
+                d = lane_group_sum<LR>(d);
+                if (li == LR - 1) atomicAdd(part + t * FMAX_RT + rr, d);
             }
         };
-        // the tile's sum over the work-group's waves, in wave order, then cleared
-        auto finish_tile = [&](int j) {
+        // the tile's sum over the work-group's waves, in wave order (cleared for a next tile)
+        auto finish_tile = [&](int j, bool more) {
             __syncthreads();
-            const int n0 = ((int)blockIdx.x + G * j) * RT;
-            for (int i = tid; i < T * RT; i += FTHREADS) {
-                const int t = i / RT, r = i - t * RT;
+            const int n0 = ((int)blockIdx.x + G * j) * DR;
+            for (int i = tid; i < T * DR; i += FTHREADS) {
+                const int t = i / DR, r = i - t * DR;
                 float v = 0.f;
 #pragma unroll
                 for (int w = 0; w < FWPB; ++w) {
                     float *pp = s_part + ((size_t)w * FMAX_T + t) * FMAX_RT + r;
                     v += *pp;
-                    *pp = 0.f;
+                    if (more) *pp = 0.f;
                 }
                 const int n = n0 + r;
                 if (n < H) {
@@ -519,7 +526,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                         reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
                 }
             }
-            __syncthreads();
+            if (more) __syncthreads();
         };
         int sq = 0;
         for (int j = 0; j < ntw; ++j) {
@@ -532,7 +539,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                     if (sq + 2 < total) load_item(sq + 2, dqa, dsa);
                 }
             }
-            finish_tile(j);
+            finish_tile(j, j + 1 < ntw);
         }
     }
 }
