@@ -16,7 +16,8 @@
 // with write-through agent-scope stores and read with agent-scope loads, so
 // no cache writeback or invalidation is needed at the barrier.  Every wait is
 // bounded and sets MOE_DEVERR_TIMEOUT instead of hanging.
-//   0. router: expert rows spread one per wave over the grid; each logit goes
+//   0. router: expert rows spread one per wave over the work-groups of the
+//      first-started XCDs; each logit goes
 //      to the workspace as one self-validating 64-bit word (value | call tag),
 //      so no barrier is needed before it is read.
 //   1. every work-group redundantly takes the top-k of all T tokens (polling
@@ -166,40 +167,58 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // kept in ascending expert id until k are kept (ties go to the lower id).
 // Writes ids (ascending) and weights (softmax over all E at the kept ids,
 // renormalised over the kept set when renorm) to ids[0..k) / w[0..k).
-// The logits arrive as self-validating words (value | call tag << 32), written by the
-// waves that own the router rows; the wave re-reads until every word carries this
-// call's tag (bounded wait, MOE_DEVERR_TIMEOUT on expiry).
-template <int NJ>
-__device__ __forceinline__ void wave_topk(const uint64_t *logits, uint32_t tag, int E, int K, int renorm, int *ids,
-                                          float *w, int32_t *ids_g, float *w_g, int32_t *err) {
+// Wait (one wave) until the n logit words [0, n) carry this call's tag, polling
+// words[first, first + n_first) alone before that, and copy the values to lg (LDS).
+// All the work-group's pollers share a few memory lines with the router's stores, so
+// the polls back off (up to ~0.4 us apart) to leave those lines to the writers.
+// Bounded: MOE_DEVERR_TIMEOUT on expiry.
+__device__ __forceinline__ bool poll_words(const uint64_t *words, int n, uint32_t tag, float *lg, uint64_t t0,
+                                           int32_t *err) {
     const int lane = threadIdx.x & 63;
-    constexpr int nj = NJ;
+    for (int base = 0; base < n; base += 4 * WAVE) {
+        uint64_t wd[4];
+        int nap = 1;
+        for (;;) {
+            bool ready = true;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + lane + WAVE * j;
+                wd[j] = i < n ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : ((uint64_t)tag << 32);
+                ready = ready && (uint32_t)(wd[j] >> 32) == tag;
+            }
+            if (__ballot(!ready) == 0ull) break;
+            if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
+                if (lane == 0) atomicOr(err, MOE_DEVERR_TIMEOUT);
+                return false;
+            }
+            for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
+            nap = nap < 8 ? nap * 2 : 8;
+        }
+        if (lg) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int i = base + lane + WAVE * j;
+                if (i < n) lg[i] = __uint_as_float((uint32_t)wd[j]);
+            }
+        }
+    }
+    return true;
+}
+
+// top-k of one token's logits lg[0, E) (LDS), one wave
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int renorm, int *ids, float *w,
+                                          int32_t *ids_g, float *w_g) {
+    const int lane = threadIdx.x & 63;
     float v[NJ];
     uint32_t key[NJ];
     float m = -__builtin_inff();
-    uint64_t word[NJ];
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-        bool ready = true;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-            const int e = lane + 64 * j;
-            word[j] = e < E ? __hip_atomic_load(logits + e, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                            : ((uint64_t)tag << 32);
-            ready = ready && (uint32_t)(word[j] >> 32) == tag;
-        }
-        if (__ballot(!ready) == 0ull) break;
-        if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
-            if (lane == 0) atomicOr(err, MOE_DEVERR_TIMEOUT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
         const int e = lane + 64 * j;
         const bool ok = e < E;
-        v[j] = ok ? __uint_as_float((uint32_t)word[j]) : -__builtin_inff();
+        v[j] = ok ? lg[e] : -__builtin_inff();
         key[j] = ok ? f32_order_key(v[j]) : 0u;
         m = fmaxf(m, v[j]);
     }
@@ -289,6 +308,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const int gw = blockIdx.x + G * wave;        // consecutive work items land on different CUs
     const bool f32 = A::EPC == 4;
     const int ab = f32 ? 4 : 2;
+    const size_t lg_off = ((size_t)T * H * ab + 15) & ~(size_t)15;   // LDS logits after the staged x
 
     if (tid == 0) {
         s_base = bar_base(p.bar, G);
@@ -307,7 +327,15 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     {
         const int nch = H / A::EPC;
         const size_t xrow = (size_t)H * ab;
-        const int e = blockIdx.x + G * wave;
+        // Router rows go to the work-groups of the first two XCDs (blocks b with b % 8 < 2
+        // under the round-robin block-to-XCD dispatch): measured, they start about 2 us
+        // before those of the other XCDs, so the logits are ready when the rest arrive.
+        const bool xcd8 = G % 8 == 0;
+        const int nrb = xcd8 ? G / 4 : G;                                  // router work-groups
+        const int rb = !xcd8 ? (int)blockIdx.x
+                             : ((blockIdx.x & 7) < 2 ? (int)(blockIdx.x >> 3) * 2 + (int)(blockIdx.x & 7) : -1);
+        const int NRW = nrb * FWPB;
+        const int e = rb >= 0 ? rb + nrb * wave : E;
         uint4 q[CR];
         uint32_t sc[CR];
         if (e < E) load_chunks<A, CR>(p.wr + (size_t)e * nch * 16, nullptr, nch, lane, WAVE, q, sc);
@@ -316,7 +344,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         uint4 *dst = reinterpret_cast<uint4 *>(smem);
         for (int i = tid; i < n16; i += FTHREADS) dst[i] = src[i];
         __syncthreads();
-        for (int ee = e; ee < E; ee += NW) {
+        for (int ee = e; ee < E; ee += NRW) {
             if (ee != e) load_chunks<A, CR>(p.wr + (size_t)ee * nch * 16, nullptr, nch, lane, WAVE, q, sc);
             const float b = p.bias ? p.bias[ee] : 0.f;
             // every row t < FMAX_T is rewritten each call (rows past T with the tag only), so
@@ -332,19 +360,28 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             }
         }
     }
-    // ---- phase 1: top-k + softmax per token (wave t), then grouping ----------------------
+    // ---- phase 1: logits to LDS (wave 0 waits for them), top-k + softmax per token (wave t),
+    // then grouping
+    float *s_lg = reinterpret_cast<float *>(smem + lg_off);   // [T][E], after the staged x
+    if (wave == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        // the router stores a row's words in token order: its last token's words first
+        bool ok = T == 1 || poll_words(p.logits + (size_t)(T - 1) * E, E, s_tag, nullptr, t0, p.err);
+        if (ok) poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
+    }
+    __syncthreads();
     if (wave < T) {
         const bool out = blockIdx.x == 0;
-        const uint64_t *lg = p.logits + (size_t)wave * E;
+        const float *lg = s_lg + (size_t)wave * E;
         int *ii = s_ids + wave * K;
         float *ww = s_w + wave * K;
         int32_t *ig = out && p.ids_out ? p.ids_out + wave * K : nullptr;
         float *wg = out && p.w_out ? p.w_out + wave * K : nullptr;
-        if (E <= 64) wave_topk<1>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
-        else if (E <= 128) wave_topk<2>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
-        else if (E <= 256) wave_topk<4>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
-        else if (E <= 512) wave_topk<8>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
-        else wave_topk<16>(lg, s_tag, E, K, p.renorm, ii, ww, ig, wg, p.err);
+        if (E <= 64) wave_topk<1>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 128) wave_topk<2>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 256) wave_topk<4>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else if (E <= 512) wave_topk<8>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        else wave_topk<16>(lg, E, K, p.renorm, ii, ww, ig, wg);
     }
     __syncthreads();
     const int P4 = (P + 3) >> 2;
@@ -544,6 +581,12 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     }
 }
 
+// LDS bytes of the staged x plus the logits that follow it
+static size_t fused_lds_front(const moe_shape &s) {
+    const size_t xb = (size_t)s.num_tokens * s.hidden * act_bytes(s.act_dtype);
+    return ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4;
+}
+
 // true when the fused kernel covers this shape (otherwise the staged kernels run)
 static bool fused_bucket_built(int cg, int cr, int cd);
 static int bucket(int chunks_per_lane);
@@ -559,7 +602,7 @@ bool decode_fused_supported(const moe_shape &s) {
     const int nchd = s.intermediate / epc;
     const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
     if (nchd < 16 || (nchd + lpr - 1) / lpr > FMAX_C / 2) return false;    // down rows
-    if ((size_t)s.num_tokens * s.hidden * ab > FLDS_MAX || P * s.intermediate * ab > FLDS_MAX) return false;
+    if (fused_lds_front(s) > FLDS_MAX || P * s.intermediate * ab > FLDS_MAX) return false;
     if (s.num_experts > 1024) return false;
     return fused_bucket_built(bucket((s.hidden / epc + WAVE - 1) / WAVE), bucket((s.hidden / aepc + WAVE - 1) / WAVE),
                               bucket((nchd + lpr - 1) / lpr));
@@ -656,8 +699,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     prm.renorm = s.renormalize ? 1 : 0;
     prm.nblocks = cus;
     const size_t ab = act_bytes(s.act_dtype);
-    const size_t lds = std::max((size_t)s.num_tokens * s.hidden * ab,
-                                (size_t)s.num_tokens * s.top_k * s.intermediate * ab);
+    const size_t lds = std::max(fused_lds_front(s), (size_t)s.num_tokens * s.top_k * s.intermediate * ab);
     switch (s.weight_dtype) {
         case MOE_F32: return fused_dispatch<FmtF32, FmtF32>(s, prm, lds, st, ev0, ev1);
         case MOE_BF16: return fused_dispatch<FmtBF16, FmtBF16>(s, prm, lds, st, ev0, ev1);
