@@ -119,7 +119,8 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
                                                              int32_t *__restrict__ sorted,
                                                              int32_t *__restrict__ slot_pos,
                                                              int32_t *__restrict__ active,
-                                                             int32_t *__restrict__ mtile_off, int mtile_rows) {
+                                                             int32_t *__restrict__ mtile_off,
+                                                             int4 *__restrict__ tiles, int mtile_rows) {
     extern __shared__ int smem[];
     const int nth = blockDim.x;
     int *tot = smem;            // [E] totals, then exclusive offsets
@@ -170,7 +171,13 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
         }
         __syncthreads();
         const int nt = block_exclusive_scan(flags, E, tmp);
-        for (int e = tid; e < E; e += nth) mtile_off[e] = flags[e];
+        for (int e = tid; e < E; e += nth) {
+            mtile_off[e] = flags[e];
+            if (!tiles) continue;
+            const int next = (e + 1 < E) ? tot[e + 1] : total;
+            const int t_end = (e + 1 < E) ? flags[e + 1] : nt;
+            for (int t = flags[e]; t < t_end; ++t) tiles[t] = make_int4(tot[e] + (t - flags[e]) * mtile_rows, next, e, 0);
+        }
         if (tid == 0) mtile_off[E] = nt;
     }
 }
@@ -180,8 +187,8 @@ constexpr int GROUP_CHUNK = 4096;
 int group_chunks(int P) { return P > 0 ? (P + GROUP_CHUNK - 1) / GROUP_CHUNK : 1; }
 
 hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted, int32_t *slot_pos,
-                         int32_t *active, int32_t *counts, int32_t *mtile_off, int mtile_rows, int32_t *err,
-                         hipStream_t st) {
+                         int32_t *active, int32_t *counts, int32_t *mtile_off, int32_t *tiles, int mtile_rows,
+                         int32_t *err, hipStream_t st) {
     const int E = s.num_experts;
     const int P = s.num_tokens * s.top_k;
     const int nb = group_chunks(P);
@@ -193,7 +200,8 @@ hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offset
     if (r != hipSuccess) return r;
     const int nth = 1024;
     hipLaunchKernelGGL(group_scatter_kernel, dim3(nb), dim3(nth), (size_t)(3 * E + nth) * 4, st, ids, P, E, GROUP_CHUNK,
-                       nb, counts, offsets, sorted, slot_pos, active, mtile_off, mtile_rows);
+                       nb, counts, offsets, sorted, slot_pos, active, mtile_off,
+                       mtile_off ? reinterpret_cast<int4 *>(tiles) : nullptr, mtile_rows);
     return hipGetLastError();
 }
 

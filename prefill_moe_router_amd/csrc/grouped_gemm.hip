@@ -328,9 +328,10 @@ using CfgDN = TileCfg<MOE_DN_CFG>;
 using CfgR = TileCfg<MOE_R_CFG>;
 static_assert(CfgGU::BM == kGroupedTileM && CfgDN::BM == kGroupedTileM, "m-tiles follow the grouping");
 
-// m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / kGroupedTileM)
+// m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / kGroupedTileM),
+// and the tile table: tiles[t] = {first row, end row of the expert, expert, 0}
 __global__ __launch_bounds__(1024) void mtile_offsets_kernel(const int32_t *__restrict__ offsets, int E,
-                                                             int32_t *__restrict__ mtile_off) {
+                                                             int32_t *__restrict__ mtile_off, int4 *__restrict__ tiles) {
     __shared__ int s[1025];
     const int tid = threadIdx.x;
     for (int e = tid; e < E; e += blockDim.x) s[e] = (offsets[e + 1] - offsets[e] + kGroupedTileM - 1) / kGroupedTileM;
@@ -346,6 +347,9 @@ __global__ __launch_bounds__(1024) void mtile_offsets_kernel(const int32_t *__re
     }
     __syncthreads();
     for (int e = tid; e <= E; e += blockDim.x) mtile_off[e] = s[e];
+    for (int e = tid; e < E; e += blockDim.x)
+        for (int t = s[e]; t < s[e + 1]; ++t)
+            tiles[t] = make_int4(offsets[e] + (t - s[e]) * kGroupedTileM, offsets[e + 1], e, 0);
 }
 
 // y[t][n] = sum_j o'[t*k + j][n]  (bf16 rows of one token, fp32 sum, one rounding)
@@ -421,8 +425,10 @@ hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr,
     return gemm_launch<GM_ROUTER, CfgR>(prm, st, ev0, ev1);
 }
 
-hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, hipStream_t st) {
-    hipLaunchKernelGGL(mtile_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, s.num_experts, mtile_off);
+hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
+                                hipStream_t st) {
+    hipLaunchKernelGGL(mtile_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, s.num_experts, mtile_off,
+                       reinterpret_cast<int4 *>(tiles));
     return hipGetLastError();
 }
 
@@ -433,8 +439,9 @@ static int mt_max_of(const moe_shape &s) {
 }
 
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
-                              const int32_t *sorted, const int32_t *mtile_off, const float *wts, void *h,
-                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                              const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const float *wts,
+                              void *h, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    if (wide_gateup_supported(s)) return launch_gateup_wide(s, x, w, sorted, mtile_off, tiles, wts, h, st, ev0, ev1);
     GemmParams prm{};
     prm.a = static_cast<const uint8_t *>(x);
     prm.sorted = sorted;
@@ -458,8 +465,9 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
 }
 
 hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, const int32_t *offsets,
-                            const int32_t *sorted, const int32_t *mtile_off, const void *h, void *o, bool f32_sorted,
-                            hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+                            const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const void *h,
+                            void *o, bool f32_sorted, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    if (!f32_sorted && wide_down_supported(s)) return launch_down_wide(s, w, sorted, mtile_off, tiles, h, o, st, ev0, ev1);
     GemmParams prm{};
     prm.a = static_cast<const uint8_t *>(h);
     prm.sorted = sorted;

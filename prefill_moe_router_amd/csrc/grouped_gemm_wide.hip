@@ -1,0 +1,428 @@
+// grouped_gemm_wide.hip -- the large-tile MFMA grouped GEMM for bf16 experts in
+// prefill chunks (the expert contractions of the 8192-token chunks in
+// "第 9 章 prefill：最大的瓶颈" §9.8, tokens grouped on the device as in §9.9).
+//
+//   GATEUP : h'[p][i] = w_slot * silu(x_t . Wg[e][i]) * (x_t . Wu[e][i])   (bf16, sorted order)
+//   DOWN   : o'[slot][n] = h'[p] . Wd[e][n]             (bf16, rows scattered to slot order)
+//
+// Design for gfx950:
+//  * A work-group of 4 waves owns a 128-row m-tile of one expert and 256 weight rows
+//    (GATEUP: 128 intermediate columns of both gate and up; DOWN: 256 output
+//    columns).  The waves form a 2 x 2 grid; each owns 64 rows x 128 weight rows,
+//    i.e. 8 independent 32x32 MFMA accumulators (128 registers), so one 16-deep K
+//    slice moves 6 KB of operands out of LDS per 8 MFMAs.  72 KB of LDS and <= 256
+//    registers per lane let two work-groups share a CU, so one group's tile start
+//    (metadata loads, pipeline fill) and epilogue hide under the other's MFMAs.
+//  * Each m-tile's rows come from a tile table the grouping writes ({first row, end
+//    row, expert} per tile): one load, no search over the m-tile offsets.
+//  * Operands go from global memory straight into LDS (global_load_lds_dwordx4: no
+//    staging registers, no VALU), 32 K elements per stage, in a ring of 3 stages, so
+//    two stages are in flight while one is consumed.
+//  * LDS rows are 64 bytes (four 16-byte chunks) with the chunk index XOR-swizzled
+//    by bits 2..3 of the row, so the 16-byte operand reads fall in distinct banks
+//    without padding (a direct LDS load writes 1 KB contiguously, which rules
+//    padding out).
+//  * Waits are explicit: vmcnt counts this wave's loads of the stages still in flight,
+//    and the work-group barrier carries no memory fence (a fence would drain the
+//    loads in flight).  The barrier of step kt lands after this step's operands are in
+//    registers, so the stage it frees is refilled three steps ahead.
+#include <hip/hip_ext.h>
+
+#include <type_traits>
+
+#include "moe_device.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int NXCD = 8;
+constexpr int BM = 128;                 // rows per m-tile (the grouping's tile)
+constexpr int WROWS = 128;              // weight rows per wave
+constexpr int BK = 32;                  // K elements per stage
+constexpr int ROWB = BK * 2;            // bytes of one staged row
+#ifndef MOE_WIDE_NSTAGE
+#define MOE_WIDE_NSTAGE 3
+#endif
+#ifndef MOE_WIDE_OCC
+#define MOE_WIDE_OCC 2
+#endif
+// LDS ring depth and work-groups per CU.  Measured on the 8192-token chunk: 3 stages
+// with two work-groups per CU beat 4-6 stages with one (607 vs 675-680 us gate/up).
+constexpr int NSTAGE = MOE_WIDE_NSTAGE;
+constexpr int NTH = 256;                // 4 waves
+constexpr int GM = 8;                   // m-tiles per group of the tile order
+
+enum { WG_GATEUP = 0, WG_DOWN = 1 };
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+struct WideParams {
+    const uint8_t *a;          // x [T][K] (GATEUP) or h' [P][K] (DOWN), bf16
+    const int32_t *sorted;     // sorted slots [P]
+    const int32_t *mtile_off;  // m-tile offsets [E+1] (only [E], the tile count, is read)
+    const int4 *tiles;         // per m-tile {first row, end row of the expert, expert, 0}
+    const uint8_t *b0, *b1;    // weights [E][N][K] bf16 (b1: up, GATEUP only)
+    const float *wts;          // gate weight per slot (GATEUP) or null
+    uint8_t *out;
+    int N, K, topk, E;         // N: weight rows per expert (GATEUP: I, DOWN: H)
+    int mt_max, nt;
+};
+
+// The 16-byte chunk kc of LDS row r sits at chunk slot kc ^ swz(r).  Measured on
+// gfx950 (SQ_LDS_BANK_CONFLICT of an isolated read loop): with 64-byte rows, the
+// 16-byte MFMA operand reads (32 rows, two chunks per row per half-wave) are
+// conflict-free with bits 2..3 of the row as the XOR key, 2-way with bits 1..2,
+// 4-way unswizzled.
+__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// one wave-wide direct load: 16 bytes per lane from g into LDS at l + 16 * lane (l
+// wave-uniform).  A plain (non-template) function keeps the builtin out of the host
+// pass's instantiation of the kernel template.
+__device__ __forceinline__ void load_lds16(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t *)l, 16, 0, 0);
+}
+
+// work-group barrier with no memory fence; "memory" keeps the compiler from moving
+// memory accesses across it (the waits before it are explicit)
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
+#define WG_INLINE __attribute__((always_inline))
+
+}  // namespace
+
+// WM x WN waves (WM * WN = 4); each wave owns BM/WM rows x 128 weight rows.
+template <int MODE, int WM, int WN>
+__global__ __launch_bounds__(NTH, (WM == 1 ? 1 : MOE_WIDE_OCC)) void grouped_gemm_wide_kernel(WideParams p) {
+    static_assert(WM * WN == 4, "four waves");
+    constexpr int BN = WN * WROWS;                   // weight rows per n-tile
+    constexpr int RW = BM / WM;                      // rows per wave
+    constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    constexpr int STAGE = A_BYTES + B_BYTES;
+    constexpr int A_LOADS = A_BYTES / 16 / NTH, B_LOADS = B_BYTES / 16 / NTH;   // per thread and stage
+    constexpr int LOADS = A_LOADS + B_LOADS;
+    constexpr int NCOL = MODE == WG_GATEUP ? BN / 2 : BN;   // output columns per n-tile
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+    __shared__ int s_slot[BM];
+    __shared__ float s_scale[BM];
+
+    // ---- which tile: groups of GM m-tiles swept n-tile by n-tile, each XCD a
+    // contiguous range of that order (blocks are dealt to XCDs round-robin)
+    const int per_xcd = gridDim.x / NXCD;
+    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
+    const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
+    const int n_tile = in_grp / GM, mt = grp * GM + in_grp % GM;
+    if (mt >= p.mt_max) return;
+    const int n_mt = p.mtile_off[p.E];
+    const int4 tinfo = p.tiles[mt];
+    if (mt >= n_mt) return;
+    const int m0 = tinfo.x, m_end = tinfo.y, e = tinfo.z;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int wm = wave / WN, wn = wave % WN;
+    const size_t krow = (size_t)p.K * 2;
+    const int KT = p.K / BK;   // stages; even and >= 4 (wide_*_supported)
+
+    for (int m = tid; m < BM; m += NTH) {
+        const int pos = min(m0 + m, m_end - 1);
+        const int slot = p.sorted[pos];
+        s_slot[m] = slot;
+        s_scale[m] = (MODE == WG_GATEUP && m0 + m < m_end) ? (p.wts ? p.wts[slot] : 1.f) : 0.f;
+    }
+    __syncthreads();
+
+    // ---- sources of this lane's direct loads.  One wave-wide load fills 1 KB of LDS,
+    // 16 rows of 4 chunks; lane l lands in row 16g + l/4 at chunk slot l%4, which holds
+    // the row's logical chunk (l%4) ^ swz(row).
+    const int lrow = lane >> 2;
+    const uint8_t *asrc[A_LOADS];
+#pragma unroll
+    for (int q = 0; q < A_LOADS; ++q) {
+        const int r = 16 * (wave * A_LOADS + q) + lrow;
+        const int kc = (lane & 3) ^ swz(r);
+        const size_t row = MODE == WG_GATEUP ? (size_t)(s_slot[r] / p.topk) : (size_t)min(m0 + r, m_end - 1);
+        asrc[q] = p.a + row * krow + kc * 16;
+    }
+    // B: LDS row q of the tile belongs to wave q / 128.  GATEUP: rows 0-63 of a wave's
+    // range are gate columns c0 + 64 * (q / 128) + (0..63), rows 64-127 the same up
+    // columns (c0 = the n-tile's first intermediate column).  DOWN: output column
+    // n0 + q.
+    const uint8_t *bsrc[B_LOADS];
+#pragma unroll
+    for (int q = 0; q < B_LOADS; ++q) {
+        const int r = 16 * (wave * B_LOADS + q) + lrow;
+        const int kc = (lane & 3) ^ swz(r);
+        size_t wrow;
+        const uint8_t *base;
+        if (MODE == WG_GATEUP) {
+            const int rl = r % WROWS;
+            base = rl < 64 ? p.b0 : p.b1;
+            wrow = (size_t)e * p.N + (size_t)n_tile * NCOL + 64 * (r / WROWS) + (rl & 63);
+        } else {
+            base = p.b0;
+            wrow = (size_t)e * p.N + (size_t)n_tile * BN + r;
+        }
+        bsrc[q] = base + wrow * krow + kc * 16;
+    }
+    auto issue = [&](int kt, int stage) WG_INLINE {
+        uint8_t *sa = lds + stage * STAGE;
+        const size_t ko = (size_t)kt * ROWB;
+#pragma unroll
+        for (int q = 0; q < A_LOADS; ++q)
+            load_lds16(asrc[q] + ko, sa + (wave * A_LOADS + q) * 1024);
+#pragma unroll
+        for (int q = 0; q < B_LOADS; ++q)
+            load_lds16(bsrc[q] + ko, sa + A_BYTES + (wave * B_LOADS + q) * 1024);
+    };
+
+    // ---- operand reads: lane reads row (32 * blk + lane % 32), logical chunk 2s + lane / 32
+    const int lr = lane & 31, hh = lane >> 5;
+    const int opoff0 = lr * ROWB + ((hh ^ swz(lr)) * 16);
+    const int opoff1 = lr * ROWB + (((2 + hh) ^ swz(lr)) * 16);
+    bf16x8_t av[2][2][MI], bv[2][2][NJ];   // [buffer][k16 sub-step][block]
+    // buf is a compile-time constant (std::integral_constant) so the operand arrays stay in registers
+    auto read_ops = [&](int stage, auto buf_c) WG_INLINE {
+        constexpr int buf = decltype(buf_c)::value;
+        const uint8_t *sa = lds + stage * STAGE + wm * RW * ROWB;
+        const uint8_t *sb = lds + stage * STAGE + A_BYTES + wn * WROWS * ROWB;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int o = s ? opoff1 : opoff0;
+#pragma unroll
+            for (int i = 0; i < MI; ++i) av[buf][s][i] = *reinterpret_cast<const bf16x8_t *>(sa + i * 32 * ROWB + o);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) bv[buf][s][j] = *reinterpret_cast<const bf16x8_t *>(sb + j * 32 * ROWB + o);
+        }
+    };
+
+    f32x16_t acc[MI][NJ];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    auto mfma_sub = [&](auto buf_c, auto s_c) WG_INLINE {
+        constexpr int buf = decltype(buf_c)::value, s = decltype(s_c)::value;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[buf][s][i], bv[buf][s][j], acc[i][j], 0, 0, 0);
+    };
+
+    using C0 = std::integral_constant<int, 0>;
+    using C1 = std::integral_constant<int, 1>;
+    // prologue: stages 0..2 in flight, stage 0 landed for every wave, its operands read
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st) issue(min(st, KT - 1), st);
+    wait_vm<(NSTAGE - 1) * LOADS>();
+    barrier_nofence();
+    read_ops(0, C0{});
+
+    // Step kt (operands of kt in register buffer kt&1, stages kt+1 .. kt+NSTAGE-1 in
+    // flight): MFMAs of the first K16 half; wait until this wave's loads of kt+1 landed
+    // and its LDS reads are done; barrier (so every wave's loads of kt+1 landed and
+    // every wave is done reading stage kt); refill stage kt with kt+NSTAGE; read the
+    // operands of kt+1; MFMAs of the second half.  In the last full step (vm 0) nothing
+    // is refilled.
+    // Scheduling: the MFMAs of the first half stay before the barrier, and the loads,
+    // LDS reads and MFMAs of the second half are interleaved after it.  The refill
+    // index is clamped: near the end it reloads the last stage into a stage nobody
+    // reads again, which keeps the step branch-free.
+    constexpr int NMF = MI * NJ, NRD = 2 * (MI + NJ);
+    auto step = [&](int kt, auto cur_c, auto vm_c) WG_INLINE {
+        using Next = std::integral_constant<int, 1 - decltype(cur_c)::value>;
+        constexpr bool refill = decltype(vm_c)::value != 0;
+        mfma_sub(cur_c, C0{});
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<decltype(vm_c)::value>();
+        wait_lgkm0();
+        barrier_nofence();
+        __builtin_amdgcn_sched_barrier(0);
+        if (refill) issue(min(kt + NSTAGE, KT - 1), kt % NSTAGE);
+        read_ops((kt + 1) % NSTAGE, Next{});
+        mfma_sub(cur_c, C1{});
+#pragma unroll
+        for (int q = 0; q < NMF; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // one MFMA
+            if (refill && q < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // one VMEM read
+            if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, NRD / NMF > 1 ? NRD / NMF : 1, 0);  // LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    using VL = std::integral_constant<int, (NSTAGE - 2) * LOADS>;
+    using V0 = std::integral_constant<int, 0>;
+    for (int kt = 0; kt < KT - 2; kt += 2) {
+        step(kt, C0{}, VL{});
+        step(kt + 1, C1{}, VL{});
+    }
+    step(KT - 2, C0{}, V0{});
+    mfma_sub(C1{}, C0{});
+    mfma_sub(C1{}, C1{});
+
+    // ---- epilogue: each wave transposes its tile through LDS (its own region) and
+    // stores whole 16-byte row pieces.  All waves are past their last LDS operand read
+    // once they pass this barrier.
+    __builtin_amdgcn_s_waitcnt(0);
+    barrier_nofence();
+    // acc[i][j][r] holds C[row][col], row = 32i + 8(r/4) + 4(lane/32) + r%4, col = 32j + lane%32
+    if (MODE == WG_GATEUP) {
+        // wave's h' tile: RW rows x 64 columns (gate blocks j = 0, 1 pair with up blocks 2, 3)
+        constexpr int PITCH = 64 + 8;   // bf16 elements per transposed row
+        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * RW * PITCH;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int ml = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float sc = s_scale[wm * RW + ml];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(sc * swiglu(acc[i][j][r], acc[i][2 + j][r]));
+            }
+        wait_lgkm0();
+        __builtin_amdgcn_wave_barrier();
+        const int col0 = n_tile * NCOL + 64 * wn;
+        for (int q = lane; q < RW * 8; q += 64) {
+            const int ml = q >> 3, ch = q & 7;
+            const int m = wm * RW + ml;
+            if (m0 + m >= m_end) continue;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
+            *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
+        }
+    } else {
+        // wave's o' tile: RW rows x 128 columns, in passes of 64 rows
+        constexpr int PITCH = 128 + 8;
+        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * 64 * PITCH;
+        const int col0 = n_tile * BN + WROWS * wn;
+#pragma unroll
+        for (int half = 0; half < RW / 64; ++half) {
+#pragma unroll
+            for (int ii = 0; ii < 2; ++ii) {
+                const int i = 2 * half + ii;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = 32 * ii + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                }
+            }
+            wait_lgkm0();
+            __builtin_amdgcn_wave_barrier();
+            for (int q = lane; q < 64 * 16; q += 64) {
+                const int ml = q >> 4, ch = q & 15;
+                const int m = wm * RW + 64 * half + ml;
+                if (m0 + m >= m_end) continue;
+                const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
+                *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[m] * p.N + col0 +
+                                             ch * 8) = v;
+            }
+            wait_lgkm0();
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+}
+
+namespace {
+
+// the configuration the launchers use: 2 x 2 waves (64 x 128 per wave, 128 x 256 per
+// work-group, 72 KB of LDS), two work-groups per CU
+#ifndef MOE_WIDE_WM
+#define MOE_WIDE_WM 2
+#endif
+constexpr int CWM = MOE_WIDE_WM, CWN = 4 / MOE_WIDE_WM;
+constexpr int CBN = CWN * WROWS;
+constexpr int RING = NSTAGE * (BM + CBN) * ROWB;
+
+template <int MODE>
+hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    static bool attr_done = false;
+    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN>;
+    if (!attr_done) {
+        hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, RING);
+        if (r != hipSuccess) return r;
+        attr_done = true;
+    }
+    int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
+    nblk = (nblk + NXCD - 1) / NXCD * NXCD;
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(NTH), RING, st, ev0, ev1, 0, prm);
+    else
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(NTH), RING, st, prm);
+    return hipGetLastError();
+}
+
+int mt_max_wide(const moe_shape &s) {
+    const long P = (long)s.num_tokens * s.top_k;
+    return (int)(P / BM + std::min<long>(s.num_experts, P));
+}
+
+}  // namespace
+
+static_assert(BM == kGroupedTileM, "m-tiles follow the grouping");
+
+// K must be a whole even number of stages, at least 4
+bool wide_gateup_supported(const moe_shape &s) {
+    return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.intermediate % (CBN / 2) == 0 &&
+           s.hidden % (2 * BK) == 0 && s.hidden >= 4 * BK;
+}
+bool wide_down_supported(const moe_shape &s) {
+    return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.hidden % CBN == 0 &&
+           s.intermediate % (2 * BK) == 0 && s.intermediate >= 4 * BK;
+}
+
+hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
+                              const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    WideParams prm{};
+    prm.a = static_cast<const uint8_t *>(x);
+    prm.sorted = sorted;
+    prm.mtile_off = mtile_off;
+    prm.tiles = reinterpret_cast<const int4 *>(tiles);
+    prm.b0 = static_cast<const uint8_t *>(w.w_gate);
+    prm.b1 = static_cast<const uint8_t *>(w.w_up);
+    prm.wts = wts;
+    prm.out = static_cast<uint8_t *>(h);
+    prm.N = s.intermediate;
+    prm.K = s.hidden;
+    prm.topk = s.top_k;
+    prm.E = s.num_experts;
+    prm.mt_max = mt_max_wide(s);
+    prm.nt = s.intermediate / (CBN / 2);
+    return wide_launch<WG_GATEUP>(prm, st, ev0, ev1);
+}
+
+hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, const int32_t *sorted,
+                            const int32_t *mtile_off, const int32_t *tiles, const void *h, void *o, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1) {
+    WideParams prm{};
+    prm.a = static_cast<const uint8_t *>(h);
+    prm.sorted = sorted;
+    prm.mtile_off = mtile_off;
+    prm.tiles = reinterpret_cast<const int4 *>(tiles);
+    prm.b0 = static_cast<const uint8_t *>(w.w_down);
+    prm.out = static_cast<uint8_t *>(o);
+    prm.N = s.hidden;
+    prm.K = s.intermediate;
+    prm.topk = s.top_k;
+    prm.E = s.num_experts;
+    prm.mt_max = mt_max_wide(s);
+    prm.nt = s.hidden / CBN;
+    return wide_launch<WG_DOWN>(prm, st, ev0, ev1);
+}
+
+}  // namespace moe

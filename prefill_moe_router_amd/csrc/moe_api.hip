@@ -119,7 +119,7 @@ moe_status moe_group_tokens(const moe_shape *shape, const int32_t *topk_ids, int
     hipStream_t st = static_cast<hipStream_t>(stream);
     // T == 0 still defines the offsets (all zero)
     MOE_TRY(launch_group2(*shape, topk_ids, expert_offsets, sorted_slots, slot_pos, at<int32_t>(ws, L.active),
-                          at<int32_t>(ws, L.gcounts), nullptr, kGroupedTileM, at<int32_t>(ws, L.ctrl), st));
+                          at<int32_t>(ws, L.gcounts), nullptr, nullptr, kGroupedTileM, at<int32_t>(ws, L.ctrl), st));
     return MOE_OK;
 }
 
@@ -138,11 +138,12 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *x, const moe_exper
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (use_grouped(*shape)) {
         int32_t *mtile = at<int32_t>(ws, L.mtile);
-        MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, st));
-        MOE_TRY(launch_gateup_mfma(*shape, x, *w, expert_offsets, sorted_slots, mtile, nullptr, at<void>(ws, L.h), st,
-                                   nullptr, nullptr));
-        MOE_TRY(launch_down_mfma(*shape, *w, expert_offsets, sorted_slots, mtile, at<void>(ws, L.h), expert_out, true,
-                                 st, nullptr, nullptr));
+        int32_t *tiles = at<int32_t>(ws, L.tiles);
+        MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, tiles, st));
+        MOE_TRY(launch_gateup_mfma(*shape, x, *w, expert_offsets, sorted_slots, mtile, tiles, nullptr,
+                                   at<void>(ws, L.h), st, nullptr, nullptr));
+        MOE_TRY(launch_down_mfma(*shape, *w, expert_offsets, sorted_slots, mtile, tiles, at<void>(ws, L.h),
+                                 expert_out, true, st, nullptr, nullptr));
         return MOE_OK;
     }
     int32_t *active = at<int32_t>(ws, L.active);
@@ -221,7 +222,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     void *h = at<void>(ws, L.h);
     int32_t *err = at<int32_t>(ws, L.ctrl);
     if (use_grouped(*shape)) {
-        int32_t *mtile = at<int32_t>(ws, L.mtile);
+        int32_t *mtile = at<int32_t>(ws, L.mtile), *tiles = at<int32_t>(ws, L.tiles);
         if (router_mfma_supported(*shape)) {
             MOE_TRY(launch_router_mfma(*shape, x, w_router, bias, logits, st, se.start(0), se.stop(0)));
         } else {
@@ -230,10 +231,10 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
         MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
         MOE_TRY(around(se, 2, st, [&] {
             return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), mtile,
-                                 kGroupedTileM, err, st);
+                                 tiles, kGroupedTileM, err, st);
         }));
-        MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, wts, h, st, se.start(3), se.stop(3)));
-        MOE_TRY(launch_down_mfma(*shape, *w, offsets, sorted, mtile, h, o, false, st, se.start(4), se.stop(4)));
+        MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, tiles, wts, h, st, se.start(3), se.stop(3)));
+        MOE_TRY(launch_down_mfma(*shape, *w, offsets, sorted, mtile, tiles, h, o, false, st, se.start(4), se.stop(4)));
         MOE_TRY(around(se, 5, st, [&] { return launch_combine_rows(*shape, o, y, st); }));
         return MOE_OK;
     }
@@ -241,7 +242,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
     MOE_TRY(around(se, 2, st, [&] {
         return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), nullptr,
-                             kGroupedTileM, err, st);
+                             nullptr, kGroupedTileM, err, st);
     }));
     MOE_TRY(around(se, 3, st, [&] {
         return launch_decode_gateup(*shape, x, *w, offsets, sorted, active, nullptr, h, st);

@@ -23,10 +23,14 @@ constexpr int kFusedMaxTokens = 8;
 
 inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
+// upper bound of the number of m-tiles of P pairs over E experts:
+// sum over experts of ceil(count / tile) <= P / tile + (number of nonempty experts)
+inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM + (P < E ? P : E); }
+
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word, the rest zero between calls.
 struct WsLayout {
-    size_t ctrl, tagged, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, gcounts, h, o, total;
+    size_t ctrl, tagged, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, tiles, gcounts, h, o, total;
 };
 
 inline WsLayout ws_layout(const moe_shape &s) {
@@ -49,6 +53,7 @@ inline WsLayout ws_layout(const moe_shape &s) {
     L.slot_pos = take(P * 4);
     L.active = take((E + 1) * 4);
     L.mtile = take((E + 1) * 4);
+    L.tiles = take(grouped_tile_bound(P, E) * 16);
     L.gcounts = take((P > 0 ? (P + 4095) / 4096 : 1) * E * 4);
     L.h = take(P * I * act_bytes(s.act_dtype));
     L.o = take(P * H * 4);
@@ -64,11 +69,12 @@ hipError_t launch_router_logits(const moe_shape &s, const void *x, const void *w
 // top-k + softmax (+ renorm) over logits rows -> ids [T][k] ascending, w [T][k]
 hipError_t launch_topk(const moe_shape &s, const float *logits, int32_t *ids, float *w, hipStream_t st);
 // multi-block stable grouping (chunks of 4096 slots): counts [chunks][E] scratch;
-// mtile_off (optional) receives the m-tile offsets for tiles of mtile_rows rows
+// mtile_off (optional) receives the m-tile offsets for tiles of mtile_rows rows, and
+// tiles (with mtile_off) one {first row, end row of the expert, expert, 0} int4 per m-tile
 int group_chunks(int P);
 hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offsets, int32_t *sorted, int32_t *slot_pos,
-                         int32_t *active, int32_t *counts, int32_t *mtile_off, int mtile_rows, int32_t *err,
-                         hipStream_t st);
+                         int32_t *active, int32_t *counts, int32_t *mtile_off, int32_t *tiles, int mtile_rows,
+                         int32_t *err, hipStream_t st);
 // active = [count, nonempty experts ascending] from existing offsets
 hipError_t launch_active(const moe_shape &s, const int32_t *offsets, int32_t *active, hipStream_t st);
 // h[p][i] = (wts ? wts[slot] : 1) * silu(Wg[e,i].x_t) * (Wu[e,i].x_t), act dtype, sorted order
@@ -93,15 +99,27 @@ bool grouped_supported(const moe_shape &s);
 bool router_mfma_supported(const moe_shape &s);
 hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, hipStream_t st);
+// m-tile offsets and the tile table from existing expert offsets
+hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
+                                hipStream_t st);
 // h'[p][i] = (wts ? wts[slot] : 1) * silu(g) * u, bf16, sorted order
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
-                              const int32_t *sorted, const int32_t *mtile_off, const float *wts, void *h,
-                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+                              const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const float *wts,
+                              void *h, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
 // f32_sorted: o[p][n] fp32 in sorted order; else o'[slot][n] bf16 in slot (token-major) order
 hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, const int32_t *offsets,
-                            const int32_t *sorted, const int32_t *mtile_off, const void *h, void *o, bool f32_sorted,
-                            hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+                            const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const void *h,
+                            void *o, bool f32_sorted, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+// large-tile bf16 variants of the two expert GEMMs (see grouped_gemm_wide.hip); the
+// launchers above route to them when the shape allows
+bool wide_gateup_supported(const moe_shape &s);
+bool wide_down_supported(const moe_shape &s);
+hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
+                              const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
+                              hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, const int32_t *sorted,
+                            const int32_t *mtile_off, const int32_t *tiles, const void *h, void *o, hipStream_t st,
+                            hipEvent_t ev0, hipEvent_t ev1);
 // y[t] = sum_j o'[t*k+j] (bf16 rows)
 hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st);
 

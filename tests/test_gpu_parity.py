@@ -335,6 +335,19 @@ def test_forward_grouped_ragged_zipf():
     compare_forward(li, got, label="grouped ragged zipf")
 
 
+@pytest.mark.parametrize("T,H,E,K,I,beta", [(333, 512, 16, 4, 256, 2.0), (1000, 1024, 32, 8, 512, 1.0)])
+def test_forward_grouped_wide_tiles_ragged(T, H, E, K, I, beta):
+    """Shapes that take the large-tile kernels for both expert GEMMs (I a multiple of
+    256, H of 512): skewed groups with partial m-tiles, several n-tiles, K of 4+ stages."""
+    note(f"grouped wide T={T} H={H} E={E} K={K} I={I}")
+    sh_ = synth.Shape(T, H, E, K, I, "bf16", "bf16", bias="zipf")
+    li = synth.make_layer(sh_, beta=beta)
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    counts = np.bincount(got["ids"].ravel(), minlength=E)
+    note(f"  group sizes max {counts.max()} empty {(counts == 0).sum()}")
+    compare_forward(li, got, label=f"grouped wide T={T}")
+
+
 def test_staged_expert_ffn_grouped_path():
     """moe_expert_ffn on the grouped family: fp32 expert outputs in sorted order."""
     li = layer_of(synth.Shape(77, 256, 16, 4, 128, "bf16", "bf16", bias="normal"))
