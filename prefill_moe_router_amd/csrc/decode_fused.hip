@@ -167,26 +167,28 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 // kept in ascending expert id until k are kept (ties go to the lower id).
 // Writes ids (ascending) and weights (softmax over all E at the kept ids,
 // renormalised over the kept set when renorm) to ids[0..k) / w[0..k).
-// Wait (one wave) until the n logit words [0, n) carry this call's tag, polling
-// words[first, first + n_first) alone before that, and copy the values to lg (LDS).
-// All the work-group's pollers share a few memory lines with the router's stores, so
-// the polls back off (up to ~0.4 us apart) to leave those lines to the writers.
-// Bounded: MOE_DEVERR_TIMEOUT on expiry.
+// Wait (one wave) until the n logit words [0, n) carry this call's tag, and copy the
+// values to lg (LDS).  Up to 1024 words (16 per lane) are loaded per poll round trip,
+// all loads issued before any is checked.  All the work-groups' pollers share a few
+// memory lines with the router's stores, so the polls back off (up to ~0.4 us apart)
+// to leave those lines to the writers.  Bounded: MOE_DEVERR_TIMEOUT on expiry.
 __device__ __forceinline__ bool poll_words(const uint64_t *words, int n, uint32_t tag, float *lg, uint64_t t0,
                                            int32_t *err) {
+    constexpr int NJ = 16;
     const int lane = threadIdx.x & 63;
-    for (int base = 0; base < n; base += 4 * WAVE) {
-        uint64_t wd[4];
+    for (int base = 0; base < n; base += NJ * WAVE) {
+        uint64_t wd[NJ];
         int nap = 1;
         for (;;) {
             bool ready = true;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 const int i = base + lane + WAVE * j;
                 wd[j] = i < n ? __hip_atomic_load(words + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                               : ((uint64_t)tag << 32);
-                ready = ready && (uint32_t)(wd[j] >> 32) == tag;
             }
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ready = ready && (uint32_t)(wd[j] >> 32) == tag;
             if (__ballot(!ready) == 0ull) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
                 if (lane == 0) atomicOr(err, MOE_DEVERR_TIMEOUT);
@@ -195,12 +197,10 @@ __device__ __forceinline__ bool poll_words(const uint64_t *words, int n, uint32_
             for (int z = 0; z < nap; ++z) __builtin_amdgcn_s_sleep(2);
             nap = nap < 8 ? nap * 2 : 8;
         }
-        if (lg) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int i = base + lane + WAVE * j;
-                if (i < n) lg[i] = __uint_as_float((uint32_t)wd[j]);
-            }
+        for (int j = 0; j < NJ; ++j) {
+            const int i = base + lane + WAVE * j;
+            if (i < n) lg[i] = __uint_as_float((uint32_t)wd[j]);
         }
     }
     return true;
@@ -365,9 +365,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     float *s_lg = reinterpret_cast<float *>(smem + lg_off);   // [T][E], after the staged x
     if (wave == 0) {
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        // the router stores a row's words in token order: its last token's words first
-        bool ok = T == 1 || poll_words(p.logits + (size_t)(T - 1) * E, E, s_tag, nullptr, t0, p.err);
-        if (ok) poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
+        poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
     }
     __syncthreads();
     if (wave < T) {
