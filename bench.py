@@ -45,9 +45,12 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 # of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
 # the counters were taken on (sha1 of the listed files); otherwise traffic is null.
 COUNTED_TRAFFIC = {
-    "decode1": dict(kernel="decode_fused", fetch_kib=37561.3125, write_kib=244.0625, fetch_scale=2.0,
+    "decode1": dict(kernel="decode_fused", fetch_kib=37463.2, write_kib=240.1, fetch_scale=2.0,
                     write_scale=1.0, sources={"prefill_moe_router_amd/csrc/decode_fused.hip":
-                                              "6ea87f5014871c9feb7527477f0384caf9b044da"}),
+                                              "6ea4269931b6e8905ac2de0307cc5cbb8552afcf"}),
+    "prefill8192": dict(kernel="gate_up", fetch_kib=995592.0, write_kib=98304.0, fetch_scale=2.0,
+                        write_scale=1.0, sources={"prefill_moe_router_amd/csrc/grouped_gemm_wide.hip":
+                                                  "b513a1d6466c358ddb4093754110def32ef941fd"}),
 }
 
 
@@ -247,7 +250,7 @@ def main():
     else:
         achieved = gateup_flops / kern_s / 1e12
         roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=None,
+                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=counted_traffic(args.config, dom_name),
                         kernel="gate_up (grouped expert gate/up + SwiGLU)", kernel_us=round(kern_s * 1e6, 3),
                         kernel_us_median=round(float(np.median(durs)) * 1e6, 3), algorithmic_flops=gateup_flops)
     log(f"dominant kernel {dom_name}: {kern_s * 1e6:.2f} us avg over {len(durs)} launches")
