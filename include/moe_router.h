@@ -55,7 +55,8 @@ enum {
 /* element formats */
 enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 };
 
-/* expert-FFN kernel family; AUTO picks DECODE for T <= 8 and GROUPED above */
+/* expert-FFN kernel family; AUTO picks DECODE while T * top_k <= 3 * E (or T <= 8) and
+   GROUPED above (bf16 and MXFP4 experts with bf16 activations) */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
 /* device error bits reported by moe_check_device_error */

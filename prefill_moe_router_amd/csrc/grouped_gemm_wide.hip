@@ -51,7 +51,6 @@ constexpr int ROWB = BK * 2;            // bytes of one staged row
 // LDS ring depth and work-groups per CU.  Measured on the 8192-token chunk: 3 stages
 // with two work-groups per CU beat 4-6 stages with one (607 vs 675-680 us gate/up).
 constexpr int NSTAGE = MOE_WIDE_NSTAGE;
-constexpr int NTH = 256;                // 4 waves
 constexpr int GM = 8;                   // m-tiles per group of the tile order
 
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
@@ -101,10 +100,11 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 
 }  // namespace
 
-// WM x WN waves (WM * WN = 4); each wave owns BM/WM rows x 128 weight rows.
-template <int MODE, int WM, int WN>
-__global__ __launch_bounds__(NTH, (WM == 1 ? 1 : MOE_WIDE_OCC)) void grouped_gemm_wide_kernel(WideParams p) {
-    static_assert(WM * WN == 4, "four waves");
+// WM x WN waves (4 or 8); each wave owns BM/WM rows x 128 weight rows.
+template <int MODE, int WM, int WN, int OCC>
+__global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(WideParams p) {
+    constexpr int NTH = WM * WN * 64;
+    static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
     constexpr int BN = WN * WROWS;                   // weight rows per n-tile
     constexpr int RW = BM / WM;                      // rows per wave
     constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
@@ -243,9 +243,9 @@ __global__ __launch_bounds__(NTH, (WM == 1 ? 1 : MOE_WIDE_OCC)) void grouped_gem
     // index is clamped: near the end it reloads the last stage into a stage nobody
     // reads again, which keeps the step branch-free.
     constexpr int NMF = MI * NJ, NRD = 2 * (MI + NJ);
-    auto step = [&](int kt, auto cur_c, auto vm_c) WG_INLINE {
+    auto step = [&](int kt, auto cur_c, auto vm_c, auto refill_c) WG_INLINE {
         using Next = std::integral_constant<int, 1 - decltype(cur_c)::value>;
-        constexpr bool refill = decltype(vm_c)::value != 0;
+        constexpr bool refill = decltype(refill_c)::value;
         mfma_sub(cur_c, C0{});
         __builtin_amdgcn_sched_barrier(0);
         wait_vm<decltype(vm_c)::value>();
@@ -265,11 +265,13 @@ __global__ __launch_bounds__(NTH, (WM == 1 ? 1 : MOE_WIDE_OCC)) void grouped_gem
     };
     using VL = std::integral_constant<int, (NSTAGE - 2) * LOADS>;
     using V0 = std::integral_constant<int, 0>;
+    using RF = std::true_type;
+    using NR = std::false_type;
     for (int kt = 0; kt < KT - 2; kt += 2) {
-        step(kt, C0{}, VL{});
-        step(kt + 1, C1{}, VL{});
+        step(kt, C0{}, VL{}, RF{});
+        step(kt + 1, C1{}, VL{}, RF{});
     }
-    step(KT - 2, C0{}, V0{});
+    step(KT - 2, C0{}, V0{}, NR{});
     mfma_sub(C1{}, C0{});
     mfma_sub(C1{}, C1{});
 
@@ -304,27 +306,23 @@ __global__ __launch_bounds__(NTH, (WM == 1 ? 1 : MOE_WIDE_OCC)) void grouped_gem
             *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
         }
     } else {
-        // wave's o' tile: RW rows x 128 columns, in passes of 64 rows
+        // wave's o' tile: RW rows x 128 columns, in passes of 32 rows
         constexpr int PITCH = 128 + 8;
-        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * 64 * PITCH;
+        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * 32 * PITCH;
         const int col0 = n_tile * BN + WROWS * wn;
 #pragma unroll
-        for (int half = 0; half < RW / 64; ++half) {
+        for (int i = 0; i < MI; ++i) {
 #pragma unroll
-            for (int ii = 0; ii < 2; ++ii) {
-                const int i = 2 * half + ii;
+            for (int r = 0; r < 16; ++r) {
+                const int ml = 8 * (r >> 2) + 4 * hh + (r & 3);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ml = 32 * ii + 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-                    for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-                }
+                for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
             }
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
-            for (int q = lane; q < 64 * 16; q += 64) {
+            for (int q = lane; q < 32 * 16; q += 64) {
                 const int ml = q >> 4, ch = q & 15;
-                const int m = wm * RW + 64 * half + ml;
+                const int m = wm * RW + 32 * i + ml;
                 if (m0 + m >= m_end) continue;
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
                 *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[m] * p.N + col0 +
@@ -343,14 +341,17 @@ namespace {
 #ifndef MOE_WIDE_WM
 #define MOE_WIDE_WM 2
 #endif
-constexpr int CWM = MOE_WIDE_WM, CWN = 4 / MOE_WIDE_WM;
+#ifndef MOE_WIDE_WN
+#define MOE_WIDE_WN 2
+#endif
+constexpr int CWM = MOE_WIDE_WM, CWN = MOE_WIDE_WN, CNTH = CWM * CWN * 64;
 constexpr int CBN = CWN * WROWS;
 constexpr int RING = NSTAGE * (BM + CBN) * ROWB;
 
 template <int MODE>
 hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN>;
+    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN, MOE_WIDE_OCC>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, RING);
@@ -360,9 +361,9 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(NTH), RING, st, ev0, ev1, 0, prm);
+        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), RING, st, ev0, ev1, 0, prm);
     else
-        hipLaunchKernelGGL(kern, dim3(nblk), dim3(NTH), RING, st, prm);
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), RING, st, prm);
     return hipGetLastError();
 }
 

@@ -58,13 +58,19 @@ moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
 moe_status check_path(const moe_shape *s) {
     // the grouped MFMA family covers bf16 experts; fp32 runs on the decode family
     if (s->path == MOE_PATH_GROUPED && !grouped_supported(*s)) return MOE_ERR_UNSUPPORTED;
+    if (!stream_ffn_supported(*s)) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
-// kernel family for the expert FFN: AUTO takes the grouped MFMA GEMMs above 8 tokens
+// kernel family for the expert FFN: AUTO takes the grouped MFMA GEMMs once the pairs
+// exceed three per expert on average (measured crossover on the H=2048, E=128, k=8
+// bf16 layer: the streaming GEMV family is faster up to 48 tokens, the GEMMs from 64
+// tokens on; on the H=4096, E=256 MXFP4 layer the two meet near 128 tokens); up to 8
+// tokens the fused single-launch kernel runs
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    return s.path == MOE_PATH_AUTO && s.num_tokens > 8 && grouped_supported(s);
+    return s.path == MOE_PATH_AUTO && s.num_tokens > 8 && (long)s.num_tokens * s.top_k > 3L * s.num_experts &&
+           grouped_supported(s);
 }
 
 template <class T>

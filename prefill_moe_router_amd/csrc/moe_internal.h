@@ -77,6 +77,8 @@ hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offset
                          int32_t *err, hipStream_t st);
 // active = [count, nonempty experts ascending] from existing offsets
 hipError_t launch_active(const moe_shape &s, const int32_t *offsets, int32_t *active, hipStream_t st);
+// the streaming expert FFN (decode_ffn.hip) covers the shape
+bool stream_ffn_supported(const moe_shape &s);
 // h[p][i] = (wts ? wts[slot] : 1) * silu(Wg[e,i].x_t) * (Wu[e,i].x_t), act dtype, sorted order
 hipError_t launch_decode_gateup(const moe_shape &s, const void *x, const moe_expert_weights &w,
                                 const int32_t *offsets, const int32_t *sorted, const int32_t *active,
