@@ -314,6 +314,23 @@ def test_forward_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+# ---- streaming GEMV family beyond 8 tokens (medium batches) -------------------------------------
+
+@pytest.mark.parametrize("T,w,path", [(24, "bf16", pm.PATH_AUTO), (48, "bf16", pm.PATH_DECODE),
+                                      (40, "mxfp4", pm.PATH_AUTO), (20, "mxfp4", pm.PATH_DECODE)])
+def test_forward_medium_batch_streaming(T, w, path):
+    """Tens of tokens on the streaming family (tokens staged in LDS, MXFP4 decoded once
+    per row, several row passes per work-group): ids exact, y sampled against the oracle."""
+    note(f"medium batch T={T} {w}")
+    if w == "bf16":
+        sh_ = synth.Shape(T, 2048, 128, 8, 768, "bf16", "bf16", bias="normal")
+    else:
+        sh_ = synth.Shape(T, 4096, 256, 8, 1024, "bf16", "mxfp4")
+    li = layer_of(sh_, batch=70 + T)
+    got = run_forward(DevLayer(li), path=path)
+    compare_forward(li, got, tokens=_sample(T, 16), label=f"medium T={T} {w}")
+
+
 # ---- grouped MFMA family ----------------------------------------------------------------------
 
 @pytest.mark.parametrize("T", [1, 8, 129])
