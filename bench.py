@@ -48,9 +48,9 @@ COUNTED_TRAFFIC = {
     "decode1": dict(kernel="decode_fused", fetch_kib=37463.2, write_kib=240.1, fetch_scale=2.0,
                     write_scale=1.0, sources={"prefill_moe_router_amd/csrc/decode_fused.hip":
                                               "6ea4269931b6e8905ac2de0307cc5cbb8552afcf"}),
-    "prefill8192": dict(kernel="gate_up", fetch_kib=995592.0, write_kib=98304.0, fetch_scale=2.0,
+    "prefill8192": dict(kernel="gate_up", fetch_kib=989666.7, write_kib=98304.0, fetch_scale=2.0,
                         write_scale=1.0, sources={"prefill_moe_router_amd/csrc/grouped_gemm_wide.hip":
-                                                  "b513a1d6466c358ddb4093754110def32ef941fd"}),
+                                                  "fb49e4421611e604edbf300f3a608250a14c6b0a"}),
 }
 
 
