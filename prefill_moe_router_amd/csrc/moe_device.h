@@ -21,16 +21,15 @@ __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v 
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even (NaN kept quiet)
+// fp32 -> bf16, round to nearest even: the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32) in the default round-to-nearest-even mode
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+    const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // lo*lo' + hi*hi' + c on packed bf16 pairs, fp32 accumulate (v_dot2_f32_bf16)
@@ -48,8 +47,12 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t packed, float scale
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(packed, scale, SEL));
 }
 
-// silu(g) * u
-__device__ __forceinline__ float swiglu(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u = g * u / (1 + e^-g), with the hardware reciprocal (v_rcp_f32, 1 ulp)
+// instead of a correctly rounded division: the result is stored as bf16 (or compared at
+// 1e-5 relative in fp32), far above that error.  g -> -inf gives g * rcp(inf) = -0.
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // streaming (non-temporal) 16-byte load: weights are read once per call
 __device__ __forceinline__ uint4 ld_stream16(const void *p) {

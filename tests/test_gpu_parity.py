@@ -200,6 +200,30 @@ def test_combine_parity_random():
     assert np.all(np.abs(yg - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
 
 
+def test_bf16_store_rounds_to_nearest_even():
+    """The kernels store bf16 through the hardware conversion; with k = 1 and weight 1 the
+    combine is a pure fp32 -> bf16 store, which must equal round-to-nearest-even bit for
+    bit, ties and subnormals included."""
+    rng = np.random.default_rng(5)
+    T, H = 4, 512
+    hi = rng.integers(0, 1 << 16, size=T * H, dtype=np.uint32)
+    lo = rng.integers(0, 1 << 16, size=T * H, dtype=np.uint32)
+    lo[::4] = 0x8000                      # exact ties
+    lo[1::8] = 0x7fff
+    lo[2::8] = 0x8001
+    hi = np.where((hi & 0x7f80) == 0x7f80, hi & 0x807f, hi)   # finite values only
+    hi[3::16] &= 0x807f                   # subnormals
+    bits = (hi << 16) | lo
+    o = bits.view(np.float32).reshape(T, H)
+    sh = pm.LayerShape(T, H, 16, 1, 64, act_dtype=pm.BF16, weight_dtype=pm.BF16)
+    y = torch.empty(T, H, dtype=torch.int16, device="cuda")
+    pm.combine(sh, tdev(o), tdev(np.ones((T, 1), np.float32)), tdev(np.arange(T, dtype=np.int32)), y)
+    torch.cuda.synchronize()
+    want = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16).astype(np.uint16).reshape(T, H)
+    got = y.cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want), np.argwhere(got != want)[:8]
+
+
 # ---- whole layer ----------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name", ["c0_tiny_f32", "c1_decode1_bf16", "c2_decode8_bf16"])
