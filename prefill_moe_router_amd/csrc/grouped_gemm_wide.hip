@@ -117,16 +117,20 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     __shared__ int s_slot[BM];
     __shared__ float s_scale[BM];
 
-    // ---- which tile: groups of GM m-tiles swept n-tile by n-tile, each XCD a
-    // contiguous range of that order (blocks are dealt to XCDs round-robin)
-    const int per_xcd = gridDim.x / NXCD;
-    const int L = (blockIdx.x % NXCD) * per_xcd + blockIdx.x / NXCD;
-    const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
-    const int n_tile = in_grp / GM, mt = grp * GM + in_grp % GM;
-    if (mt >= p.mt_max) return;
+    // ---- which tile: groups of GM m-tiles swept n-tile by n-tile (the last group holds
+    // the remaining m-tiles), each XCD a contiguous, equal share of that order (blocks are
+    // dealt to XCDs round-robin).  The share comes from the tile count the grouping wrote,
+    // so the grid's slack past it (sized for the worst case) exits at once.
     const int n_mt = p.mtile_off[p.E];
+    const int total = n_mt * p.nt;
+    const int per_xcd = (total + NXCD - 1) / NXCD;
+    const int slot = blockIdx.x / NXCD;
+    const int L = (blockIdx.x % NXCD) * per_xcd + slot;
+    if (slot >= per_xcd || L >= total) return;
+    const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
+    const int gm = min(GM, n_mt - grp * GM);          // m-tiles in this group
+    const int n_tile = in_grp / gm, mt = grp * GM + in_grp % gm;
     const int4 tinfo = p.tiles[mt];
-    if (mt >= n_mt) return;
     const int m0 = tinfo.x, m_end = tinfo.y, e = tinfo.z;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
