@@ -62,7 +62,8 @@ struct WideParams {
     const int32_t *sorted;     // sorted slots [P]
     const int32_t *mtile_off;  // m-tile offsets [E+1] (only [E], the tile count, is read)
     const int4 *tiles;         // per m-tile {first row, end row of the expert, expert, 0}
-    const uint8_t *b0, *b1;    // weights [E][N][K] bf16 (b1: up, GATEUP only)
+    const uint8_t *b0, *b1;    // weights [E][N][K] bf16 or MXFP4 codes [E][N][K/2] (b1: up, GATEUP only)
+    const uint8_t *s0, *s1;    // MXFP4 E8M0 scales [E][N][K/32]
     const float *wts;          // gate weight per slot (GATEUP) or null
     uint8_t *out;
     int N, K, topk, E;         // N: weight rows per expert (GATEUP: I, DOWN: H)
@@ -101,14 +102,20 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 }  // namespace
 
 // WM x WN waves (4 or 8); each wave owns BM/WM rows x 128 weight rows.
-template <int MODE, int WM, int WN, int OCC>
+// MX: the weights are MXFP4.  A stage then holds each B row's 16 bytes of E2M1 codes
+// (32 K elements; row stride 16 bytes, which 4-byte operand reads of 16 consecutive
+// rows take without bank conflicts), the tile's E8M0 scales for the whole K sit in an
+// LDS table loaded once, and each B operand is decoded to bf16 as it is read from LDS
+// (v_cvt_scalef32_pk_bf16_fp4): a quarter of the LDS bytes of bf16 weights.
+template <int MODE, int WM, int WN, int OCC, bool MX>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(WideParams p) {
     constexpr int NTH = WM * WN * 64;
     static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
     constexpr int BN = WN * WROWS;                   // weight rows per n-tile
     constexpr int RW = BM / WM;                      // rows per wave
     constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
-    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * ROWB;
+    constexpr int B_ROWB = MX ? BK / 2 : ROWB;       // bytes of one staged B row
+    constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * B_ROWB;
     constexpr int STAGE = A_BYTES + B_BYTES;
     constexpr int A_LOADS = A_BYTES / 16 / NTH, B_LOADS = B_BYTES / 16 / NTH;   // per thread and stage
     constexpr int LOADS = A_LOADS + B_LOADS;
@@ -135,7 +142,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
-    const size_t krow = (size_t)p.K * 2;
+    const size_t krow = (size_t)p.K * 2;           // bytes of one A row
     const int KT = p.K / BK;   // stages; even and >= 4 (wide_*_supported)
 
     for (int m = tid; m < BM; m += NTH) {
@@ -162,22 +169,26 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     // range are gate columns c0 + 64 * (q / 128) + (0..63), rows 64-127 the same up
     // columns (c0 = the n-tile's first intermediate column).  DOWN: output column
     // n0 + q.
+    // global weight row of LDS B row r, and whether it belongs to the second matrix (up)
+    auto brow_of = [&](int r, bool &second) WG_INLINE {
+        if (MODE == WG_GATEUP) {
+            const int rl = r % WROWS;
+            second = rl >= 64;
+            return (size_t)e * p.N + (size_t)n_tile * NCOL + 64 * (r / WROWS) + (rl & 63);
+        }
+        second = false;
+        return (size_t)e * p.N + (size_t)n_tile * BN + r;
+    };
+    const size_t brow_bytes = MX ? (size_t)p.K / 2 : krow;   // bytes of one global B row
     const uint8_t *bsrc[B_LOADS];
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-        const int r = 16 * (wave * B_LOADS + q) + lrow;
-        const int kc = (lane & 3) ^ swz(r);
-        size_t wrow;
-        const uint8_t *base;
-        if (MODE == WG_GATEUP) {
-            const int rl = r % WROWS;
-            base = rl < 64 ? p.b0 : p.b1;
-            wrow = (size_t)e * p.N + (size_t)n_tile * NCOL + 64 * (r / WROWS) + (rl & 63);
-        } else {
-            base = p.b0;
-            wrow = (size_t)e * p.N + (size_t)n_tile * BN + r;
-        }
-        bsrc[q] = base + wrow * krow + kc * 16;
+        // bf16: 16 rows of 4 swizzled chunks per wave-wide load; MX: 64 rows of one chunk
+        const int r = MX ? 64 * (wave * B_LOADS + q) + lane : 16 * (wave * B_LOADS + q) + lrow;
+        const int kc = MX ? 0 : (lane & 3) ^ swz(r);
+        bool second;
+        const size_t wrow = brow_of(r, second);
+        bsrc[q] = (second ? p.b1 : p.b0) + wrow * brow_bytes + kc * 16;
     }
     auto issue = [&](int kt, int stage) WG_INLINE {
         uint8_t *sa = lds + stage * STAGE;
@@ -187,7 +198,19 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
             load_lds16(asrc[q] + ko, sa + (wave * A_LOADS + q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_LOADS; ++q)
-            load_lds16(bsrc[q] + ko, sa + A_BYTES + (wave * B_LOADS + q) * 1024);
+            load_lds16(bsrc[q] + (size_t)kt * B_ROWB, sa + A_BYTES + (wave * B_LOADS + q) * 1024);
+    };
+    // MX: the tile's scale table [BN][K/32] bytes at SC_OFF, loaded once (K % 512 == 0)
+    constexpr int SC_OFF = NSTAGE * STAGE;
+    const int spr = p.K / 32;                       // scale bytes per B row
+    auto issue_scales = [&]() WG_INLINE {
+        const int cpr = spr / 16;                   // 16-byte chunks per row
+        for (int c0 = wave * WAVE; c0 < BN * cpr; c0 += NTH) {
+            const int c = c0 + lane, r = c / cpr, w = c - r * cpr;
+            bool second;
+            const size_t wrow = brow_of(r, second);
+            load_lds16((second ? p.s1 : p.s0) + wrow * spr + w * 16, lds + SC_OFF + (size_t)c0 * 16);
+        }
     };
 
     // ---- operand reads: lane reads row (32 * blk + lane % 32), logical chunk 2s + lane / 32
@@ -196,17 +219,39 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     const int opoff1 = lr * ROWB + (((2 + hh) ^ swz(lr)) * 16);
     bf16x8_t av[2][2][MI], bv[2][2][NJ];   // [buffer][k16 sub-step][block]
     // buf is a compile-time constant (std::integral_constant) so the operand arrays stay in registers
-    auto read_ops = [&](int stage, auto buf_c) WG_INLINE {
+    auto read_ops = [&](int kt, int stage, auto buf_c) WG_INLINE {
         constexpr int buf = decltype(buf_c)::value;
         const uint8_t *sa = lds + stage * STAGE + wm * RW * ROWB;
-        const uint8_t *sb = lds + stage * STAGE + A_BYTES + wn * WROWS * ROWB;
+        const uint8_t *sb = lds + stage * STAGE + A_BYTES + wn * WROWS * B_ROWB;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int o = s ? opoff1 : opoff0;
 #pragma unroll
             for (int i = 0; i < MI; ++i) av[buf][s][i] = *reinterpret_cast<const bf16x8_t *>(sa + i * 32 * ROWB + o);
+            if constexpr (!MX) {
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) bv[buf][s][j] = *reinterpret_cast<const bf16x8_t *>(sb + j * 32 * ROWB + o);
+                for (int j = 0; j < NJ; ++j)
+                    bv[buf][s][j] = *reinterpret_cast<const bf16x8_t *>(sb + j * 32 * ROWB + o);
+            }
+        }
+        if constexpr (MX) {
+            // lane (lr, hh) of sub-step s takes K elements 16s + 8hh .. +8 of its row: bytes
+            // 8s + 4hh of the row's 16 staged code bytes; one E8M0 scale per row and stage
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int q = wn * WROWS + 32 * j + lr;
+                const float sc = e8m0_to_f32(lds[SC_OFF + (size_t)q * spr + kt]);
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint32_t cw = *reinterpret_cast<const uint32_t *>(sb + (32 * j + lr) * B_ROWB + 8 * s + 4 * hh);
+                    u32x4_t o4;
+                    o4[0] = fp4x2_to_bf16x2<0>(cw, sc);
+                    o4[1] = fp4x2_to_bf16x2<1>(cw, sc);
+                    o4[2] = fp4x2_to_bf16x2<2>(cw, sc);
+                    o4[3] = fp4x2_to_bf16x2<3>(cw, sc);
+                    bv[buf][s][j] = __builtin_bit_cast(bf16x8_t, o4);
+                }
+            }
         }
     };
 
@@ -230,11 +275,12 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
     // prologue: stages 0..2 in flight, stage 0 landed for every wave, its operands read
+    if constexpr (MX) issue_scales();   // older than the stage loads: retired by the first wait
 #pragma unroll
     for (int st = 0; st < NSTAGE; ++st) issue(min(st, KT - 1), st);
     wait_vm<(NSTAGE - 1) * LOADS>();
     barrier_nofence();
-    read_ops(0, C0{});
+    read_ops(0, 0, C0{});
 
     // Step kt (operands of kt in register buffer kt&1, stages kt+1 .. kt+NSTAGE-1 in
     // flight): MFMAs of the first K16 half; wait until this wave's loads of kt+1 landed
@@ -246,7 +292,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     // LDS reads and MFMAs of the second half are interleaved after it.  The refill
     // index is clamped: near the end it reloads the last stage into a stage nobody
     // reads again, which keeps the step branch-free.
-    constexpr int NMF = MI * NJ, NRD = 2 * (MI + NJ);
+    constexpr int NMF = MI * NJ, NRD = MX ? 2 * MI + 3 * NJ : 2 * (MI + NJ);
     auto step = [&](int kt, auto cur_c, auto vm_c, auto refill_c) WG_INLINE {
         using Next = std::integral_constant<int, 1 - decltype(cur_c)::value>;
         constexpr bool refill = decltype(refill_c)::value;
@@ -257,7 +303,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
         barrier_nofence();
         __builtin_amdgcn_sched_barrier(0);
         if (refill) issue(min(kt + NSTAGE, KT - 1), kt % NSTAGE);
-        read_ops((kt + 1) % NSTAGE, Next{});
+        read_ops(kt + 1, (kt + 1) % NSTAGE, Next{});
         mfma_sub(cur_c, C1{});
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
@@ -350,24 +396,27 @@ namespace {
 #endif
 constexpr int CWM = MOE_WIDE_WM, CWN = MOE_WIDE_WN, CNTH = CWM * CWN * 64;
 constexpr int CBN = CWN * WROWS;
-constexpr int RING = NSTAGE * (BM + CBN) * ROWB;
+constexpr int MX_MAX_K = 4096;   // MXFP4: the tile's scale table (CBN x K/32 bytes) stays <= 32 KB
 
-template <int MODE>
+template <int MODE, bool MX>
 hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
+    constexpr size_t ring = (size_t)NSTAGE * (BM * ROWB + CBN * (MX ? BK / 2 : ROWB));
+    constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN, MOE_WIDE_OCC>;
+    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN, MOE_WIDE_OCC, MX>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, RING);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
         if (r != hipSuccess) return r;
         attr_done = true;
     }
+    const size_t lds = ring + (MX ? (size_t)CBN * prm.K / 32 : 0);
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), RING, st, ev0, ev1, 0, prm);
+        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), lds, st, ev0, ev1, 0, prm);
     else
-        hipLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), RING, st, prm);
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), lds, st, prm);
     return hipGetLastError();
 }
 
@@ -380,14 +429,22 @@ int mt_max_wide(const moe_shape &s) {
 
 static_assert(BM == kGroupedTileM, "m-tiles follow the grouping");
 
-// K must be a whole even number of stages, at least 4
+// K must be a whole even number of stages, at least 4; MXFP4 also wants K a multiple of
+// 512 (whole 16-byte chunks of scales per row) and at most MX_MAX_K
+static bool wide_k_ok(const moe_shape &s, int K) {
+    if (K % (2 * BK) || K < 4 * BK) return false;
+    return s.weight_dtype == MOE_BF16 || (K % 512 == 0 && K <= MX_MAX_K);
+}
+// MXFP4 gate/up stays on the register-staged kernel (grouped_gemm.hip): on the 4096-token
+// chunk (H=4096, E=256, k=8, I=1024) it measured 1085-1092 us against 1196-1200 us here,
+// while the MXFP4 down projection runs here (438-444 us against ~656 us)
 bool wide_gateup_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.intermediate % (CBN / 2) == 0 &&
-           s.hidden % (2 * BK) == 0 && s.hidden >= 4 * BK;
+           wide_k_ok(s, s.hidden);
 }
 bool wide_down_supported(const moe_shape &s) {
-    return s.act_dtype == MOE_BF16 && s.weight_dtype == MOE_BF16 && s.hidden % CBN == 0 &&
-           s.intermediate % (2 * BK) == 0 && s.intermediate >= 4 * BK;
+    return s.act_dtype == MOE_BF16 && (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4) &&
+           s.hidden % CBN == 0 && wide_k_ok(s, s.intermediate);
 }
 
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
@@ -400,6 +457,8 @@ hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_exper
     prm.tiles = reinterpret_cast<const int4 *>(tiles);
     prm.b0 = static_cast<const uint8_t *>(w.w_gate);
     prm.b1 = static_cast<const uint8_t *>(w.w_up);
+    prm.s0 = w.s_gate;
+    prm.s1 = w.s_up;
     prm.wts = wts;
     prm.out = static_cast<uint8_t *>(h);
     prm.N = s.intermediate;
@@ -408,7 +467,8 @@ hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_exper
     prm.E = s.num_experts;
     prm.mt_max = mt_max_wide(s);
     prm.nt = s.intermediate / (CBN / 2);
-    return wide_launch<WG_GATEUP>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXFP4) return wide_launch<WG_GATEUP, true>(prm, st, ev0, ev1);
+    return wide_launch<WG_GATEUP, false>(prm, st, ev0, ev1);
 }
 
 hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, const int32_t *sorted,
@@ -420,6 +480,7 @@ hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, con
     prm.mtile_off = mtile_off;
     prm.tiles = reinterpret_cast<const int4 *>(tiles);
     prm.b0 = static_cast<const uint8_t *>(w.w_down);
+    prm.s0 = w.s_down;
     prm.out = static_cast<uint8_t *>(o);
     prm.N = s.hidden;
     prm.K = s.intermediate;
@@ -427,7 +488,8 @@ hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, con
     prm.E = s.num_experts;
     prm.mt_max = mt_max_wide(s);
     prm.nt = s.hidden / CBN;
-    return wide_launch<WG_DOWN>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXFP4) return wide_launch<WG_DOWN, true>(prm, st, ev0, ev1);
+    return wide_launch<WG_DOWN, false>(prm, st, ev0, ev1);
 }
 
 }  // namespace moe

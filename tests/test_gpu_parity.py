@@ -389,6 +389,17 @@ def test_forward_grouped_wide_tiles_ragged(T, H, E, K, I, beta):
     compare_forward(li, got, label=f"grouped wide T={T}")
 
 
+@pytest.mark.parametrize("T,H,E,K,I", [(300, 1024, 32, 4, 512), (160, 2048, 16, 8, 1024)])
+def test_forward_grouped_wide_tiles_mxfp4(T, H, E, K, I):
+    """MXFP4 experts on the large-tile kernels (codes and scales loaded straight into LDS,
+    decoded per operand read): skewed groups, partial m-tiles, several n-tiles."""
+    note(f"grouped wide mxfp4 T={T} H={H} E={E} K={K} I={I}")
+    sh_ = synth.Shape(T, H, E, K, I, "bf16", "mxfp4", bias="zipf")
+    li = synth.make_layer(sh_, beta=1.0)
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    compare_forward(li, got, tokens=_sample(T, 48), label=f"grouped wide mxfp4 T={T}")
+
+
 def test_staged_expert_ffn_grouped_path():
     """moe_expert_ffn on the grouped family: fp32 expert outputs in sorted order."""
     li = layer_of(synth.Shape(77, 256, 16, 4, 128, "bf16", "bf16", bias="normal"))
