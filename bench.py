@@ -70,6 +70,9 @@ WORKLOADS = {
     "decode8": ("c2_decode8_bf16", "decode, 8 tokens, bf16, router bias N(0,0.5): H=2048, E=128, top-8, I=768"),
     "prefill8192": ("c3_prefill8192_bf16",
                     "prefill chunk, 8192 tokens, bf16, Zipf(1) router bias: H=2048, E=128, top-8, I=768"),
+    "mixed8192_8": ("c3_mixed8200_bf16",
+                    "prefill chunk of 8192 tokens plus 8 decode rows in one call, bf16, Zipf(1) router bias: "
+                    "H=2048, E=128, top-8, I=768"),
     "mxfp4_decode1": ("c4_mxfp4_decode1", "decode, 1 token, MXFP4 experts, bf16 acts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_decode8": ("c4_mxfp4_decode8", "decode, 8 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_prefill4096": ("c4_mxfp4_prefill4096",

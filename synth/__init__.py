@@ -63,6 +63,8 @@ CONFIGS: Dict[str, Shape] = {
     "c1_decode1_bf16": Shape(1, 2048, 128, 8, 768, "bf16", "bf16"),
     "c2_decode8_bf16": Shape(8, 2048, 128, 8, 768, "bf16", "bf16", bias="normal"),
     "c3_prefill8192_bf16": Shape(8192, 2048, 128, 8, 768, "bf16", "bf16", bias="zipf"),
+    # the prefill chunk with 8 decode rows appended: one call carries both
+    "c3_mixed8200_bf16": Shape(8200, 2048, 128, 8, 768, "bf16", "bf16", bias="zipf"),
     "c4_mxfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "mxfp4"),
     "c4_mxfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "mxfp4"),
     "c4_mxfp4_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "mxfp4"),

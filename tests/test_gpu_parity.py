@@ -338,6 +338,35 @@ def test_forward_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
+def test_forward_mixed_prefill_and_decode_rows_in_one_graph():
+    """A prefill chunk with decode rows appended, in one captured moe_forward: the decode
+    rows ride the chunk's expert GEMMs.  Every replay equals the eager run, and the decode
+    rows (and a sample of the chunk) match the oracle."""
+    li = layer("c3_mixed8200_bf16")
+    dl = DevLayer(li)
+    sh = lshape(li)
+    T = li.shape.T
+    ws = pm.alloc_workspace(sh)
+    y = torch.empty(T, li.shape.H, dtype=torch.int16, device="cuda")
+    ids = torch.empty(T, li.shape.K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, li.shape.K, dtype=torch.float32, device="cuda")
+    pm.forward(sh, dl.x, dl.wr, dl.bias, dl.weights, y, ws, ids, w)
+    torch.cuda.synchronize()
+    eager = (y.clone(), ids.clone(), w.clone())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pm.forward(sh, dl.x, dl.wr, dl.bias, dl.weights, y, ws, ids, w)
+    for r in range(3):
+        y.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager[0]) and torch.equal(ids, eager[1]) and torch.equal(w, eager[2]), f"replay {r}"
+    got = dict(y=y, ids=ids.cpu().numpy(), w=w.cpu().numpy())
+    toks = np.unique(np.concatenate([_sample(T - 8, 24), np.arange(T - 8, T)]))
+    compare_forward(li, got, tokens=toks, label="mixed 8192 + 8")
+
+
 # ---- streaming GEMV family beyond 8 tokens (medium batches) -------------------------------------
 
 @pytest.mark.parametrize("T,w,path", [(24, "bf16", pm.PATH_AUTO), (48, "bf16", pm.PATH_DECODE),
