@@ -156,17 +156,7 @@ __device__ __forceinline__ void store_act_sc1(uint8_t *base, size_t idx, float v
                            __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint64_t lanemask_lt() {
-    const int l = threadIdx.x & 63;
-    return l ? (~0ull >> (64 - l)) : 0ull;
-}
 
-// Top-k of one token's E (<= 1024) logits in one wave, by radix selection on
-// order-preserving keys: the k-th largest key is found bit by bit from the
-// top with ballot counts, keys above it are kept, and keys equal to it are
-// kept in ascending expert id until k are kept (ties go to the lower id).
-// Writes ids (ascending) and weights (softmax over all E at the kept ids,
-// renormalised over the kept set when renorm) to ids[0..k) / w[0..k).
 // Wait (one wave) until the n logit words [0, n) carry this call's tag, and copy the
 // values to lg (LDS).  Up to 1024 words (16 per lane) are loaded per poll round trip,
 // all loads issued before any is checked.  All the work-groups' pollers share a few
@@ -204,82 +194,6 @@ __device__ __forceinline__ bool poll_words(const uint64_t *words, int n, uint32_
         }
     }
     return true;
-}
-
-// top-k of one token's logits lg[0, E) (LDS), one wave
-template <int NJ>
-__device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int renorm, int *ids, float *w,
-                                          int32_t *ids_g, float *w_g) {
-    const int lane = threadIdx.x & 63;
-    float v[NJ];
-    uint32_t key[NJ];
-    float m = -__builtin_inff();
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const int e = lane + 64 * j;
-        const bool ok = e < E;
-        v[j] = ok ? lg[e] : -__builtin_inff();
-        key[j] = ok ? f32_order_key(v[j]) : 0u;
-        m = fmaxf(m, v[j]);
-    }
-    m = wave_max_u(m);
-    // Bit by bit from the top: `avail` keys share the prefix chosen so far, `need` of
-    // them are still to be kept.  Once they are equal, every key sharing the prefix is
-    // kept and the remaining bits need not be looked at (the common case after a dozen
-    // bits); otherwise the walk ends at bit 0 with the threshold key itself.
-    uint32_t prefix = 0;
-    int need = K, avail = E;
-    int b = 31;
-    for (; b >= 0; --b) {
-        const uint32_t cand = prefix | (1u << b);
-        const uint32_t hi = cand >> b;   // odd, so the key 0 of a padding lane never matches
-        int cnt = 0;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot((key[j] >> b) == hi));
-        if (cnt >= need) {
-            prefix = cand;
-            avail = cnt;
-        } else {
-            need -= cnt;
-            avail -= cnt;
-        }
-        if (avail == need) break;
-    }
-    const int sh = b < 0 ? 0 : b;        // keys are compared on bits [sh, 32)
-    const uint32_t pfx = prefix >> sh;
-    // kept: top bits above the prefix, or equal to it among the first `need` such in id
-    // order (all of them when the walk stopped early)
-    const uint64_t lt = lanemask_lt();
-    int eq_before = 0, sel_before = 0;
-    float z = 0.f;
-    float pe[NJ];
-    bool sel[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const bool valid = key[j] != 0u;
-        const uint32_t top = key[j] >> sh;
-        const bool eq = valid && top == pfx;
-        const uint64_t eqm = __ballot(eq);
-        const int eq_rank = eq_before + __popcll(eqm & lt);
-        eq_before += __popcll(eqm);
-        sel[j] = valid && (top > pfx || (eq && eq_rank < need));
-        pe[j] = valid ? __expf(v[j] - m) : 0.f;
-        if (!renorm || sel[j]) z += pe[j];
-    }
-    const float denom = wave_sum_u(z);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-        const uint64_t sm = __ballot(sel[j]);
-        const int pos = sel_before + __popcll(sm & lt);
-        sel_before += __popcll(sm);
-        if (sel[j]) {
-            const int e = lane + 64 * j;
-            ids[pos] = e;
-            w[pos] = pe[j] / denom;
-            if (ids_g) ids_g[pos] = e;
-            if (w_g) w_g[pos] = pe[j] / denom;
-        }
-    }
 }
 
 // ---- the kernel ------------------------------------------------------------------------

@@ -12,25 +12,40 @@
 
 namespace moe {
 
-// Block-wide exclusive scan of n (<= a few thousand) LDS ints in place;
-// returns the total.  tmp holds blockDim.x ints.
+// Block-wide exclusive scan of n (<= a few thousand) LDS ints in place; returns the
+// total.  Each thread sums a run of consecutive entries, the runs are scanned inside
+// each wave with shuffles and across the (<= 16) waves by the first wave, and each
+// thread then rewrites its run: two work-group barriers in all.  tmp holds blockDim.x
+// ints (only the first 32 are used).
 __device__ int block_exclusive_scan(int *data, int n, int *tmp) {
     const int tid = threadIdx.x, nth = blockDim.x;
+    const int lane = tid & 63, wave = tid >> 6, nw = (nth + 63) >> 6;
     const int per = (n + nth - 1) / nth;
-    const int b = tid * per, e = min(n, b + per);
+    const int b = min(n, tid * per), e = min(n, b + per);
     int local = 0;
     for (int i = b; i < e; ++i) local += data[i];
-    tmp[tid] = local;
-    __syncthreads();
-    for (int off = 1; off < nth; off <<= 1) {
-        const int v = tid >= off ? tmp[tid - off] : 0;
-        __syncthreads();
-        tmp[tid] += v;
-        __syncthreads();
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
     }
-    const int total = tmp[nth - 1];
-    int run = tmp[tid] - local;
+    if (lane == 63) tmp[wave] = incl;
     __syncthreads();
+    if (wave == 0) {
+        const int wt = lane < nw ? tmp[lane] : 0;
+        int wi = wt;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            const int v = __shfl_up(wi, off, 64);
+            if (lane >= off) wi += v;
+        }
+        if (lane < nw) tmp[16 + lane] = wi - wt;   // exclusive wave offsets
+        if (lane == nw - 1) tmp[32] = wi;          // total
+    }
+    __syncthreads();
+    int run = tmp[16 + wave] + incl - local;
+    const int total = tmp[32];
     for (int i = b; i < e; ++i) {
         const int c = data[i];
         data[i] = run;
@@ -53,6 +68,44 @@ __global__ __launch_bounds__(1024) void active_kernel(const int32_t *__restrict_
     for (int e = tid; e < E; e += nth)
         if (offsets[e + 1] > offsets[e]) active[1 + flags[e]] = e;
     if (tid == 0) active[0] = nact;
+}
+
+// Block-wide tail of the grouping, run by every thread of one block: tot[E] holds the
+// exclusive expert offsets, flags[E] marks the nonempty experts (both LDS), total is
+// the number of grouped slots.  Writes the offsets, -1 into the unused tail of sorted,
+// the list of nonempty experts and, when asked, the m-tile offsets and tile table of
+// the grouped GEMM (tiles of mtile_rows rows).
+__device__ void finish_grouping(int *tot, int *flags, int *tmp, int total, int E, int P, int32_t *__restrict__ offsets,
+                                int32_t *__restrict__ sorted, int32_t *__restrict__ active,
+                                int32_t *__restrict__ mtile_off, int4 *__restrict__ tiles, int mtile_rows) {
+    const int tid = threadIdx.x, nth = blockDim.x;
+    for (int e = tid; e < E; e += nth) offsets[e] = tot[e];
+    if (tid == 0) offsets[E] = total;
+    for (int q = total + tid; q < P; q += nth) sorted[q] = -1;
+    // nonempty experts, ascending
+    const int nact = block_exclusive_scan(flags, E, tmp);
+    for (int e = tid; e < E; e += nth) {
+        const int next = (e + 1 < E) ? tot[e + 1] : total;
+        if (next > tot[e]) active[1 + flags[e]] = e;
+    }
+    if (tid == 0) active[0] = nact;
+    if (mtile_off) {
+        __syncthreads();
+        for (int e = tid; e < E; e += nth) {
+            const int next = (e + 1 < E) ? tot[e + 1] : total;
+            flags[e] = (next - tot[e] + mtile_rows - 1) / mtile_rows;
+        }
+        __syncthreads();
+        const int nt = block_exclusive_scan(flags, E, tmp);
+        for (int e = tid; e < E; e += nth) {
+            mtile_off[e] = flags[e];
+            if (!tiles) continue;
+            const int next = (e + 1 < E) ? tot[e + 1] : total;
+            const int t_end = (e + 1 < E) ? flags[e + 1] : nt;
+            for (int t = flags[e]; t < t_end; ++t) tiles[t] = make_int4(tot[e] + (t - flags[e]) * mtile_rows, next, e, 0);
+        }
+        if (tid == 0) mtile_off[E] = nt;
+    }
 }
 
 // ---- multi-block grouping: per-chunk stable ranks, then a scan and a scatter ---------------
@@ -153,33 +206,101 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
         }
     }
     if (b != 0) return;
-    for (int e = tid; e < E; e += nth) offsets[e] = tot[e];
-    if (tid == 0) offsets[E] = total;
-    for (int q = total + tid; q < P; q += nth) sorted[q] = -1;
-    // nonempty experts, ascending
-    const int nact = block_exclusive_scan(flags, E, tmp);
-    for (int e = tid; e < E; e += nth) {
-        const int next = (e + 1 < E) ? tot[e + 1] : total;
-        if (next > tot[e]) active[1 + flags[e]] = e;
-    }
-    if (tid == 0) active[0] = nact;
-    if (mtile_off) {
-        __syncthreads();
-        for (int e = tid; e < E; e += nth) {
-            const int next = (e + 1 < E) ? tot[e + 1] : total;
-            flags[e] = (next - tot[e] + mtile_rows - 1) / mtile_rows;
+    finish_grouping(tot, flags, tmp, total, E, P, offsets, sorted, active, mtile_off, tiles, mtile_rows);
+}
+
+// ---- grouping from the router's per-block counts -----------------------------------------
+
+// One block: counts[b][e] (slots of router block b that chose e) become the base of
+// router block b inside expert e's group, offsets[e] + sum over b' < b of counts[b'][e];
+// then the offsets, active list and tile table as above.  nsub = blockDim.x / E threads
+// per expert each take a contiguous range of router blocks.
+__global__ __launch_bounds__(1024) void group_scan_kernel(int32_t *__restrict__ counts, int nb, int E, int P,
+                                                          int32_t *__restrict__ offsets, int32_t *__restrict__ sorted,
+                                                          int32_t *__restrict__ active, int32_t *__restrict__ mtile_off,
+                                                          int4 *__restrict__ tiles, int mtile_rows) {
+    extern __shared__ int smem[];
+    const int nth = blockDim.x, tid = threadIdx.x;
+    const int nsub = nth / E;
+    int *tot = smem;            // [E]
+    int *flags = tot + E;       // [E]
+    int *tmp = flags + E;       // [nth]
+    int *part = tmp + nth;      // [nsub][E]
+    const int sub = tid / E, e = tid % E;
+    const bool mine = sub < nsub;
+    const int per = (nb + nsub - 1) / nsub;
+    const int b0 = min(nb, sub * per), b1 = min(nb, b0 + per);
+    // the thread's counts are loaded in batches of SCAN_BATCH independent loads (kept in
+    // registers for the second pass when the whole range fits one batch)
+    constexpr int SCAN_BATCH = 32;
+    int cv[SCAN_BATCH];
+    if (mine) {
+        int local = 0;
+        for (int b = b0; b < b1; b += SCAN_BATCH) {
+#pragma unroll
+            for (int j = 0; j < SCAN_BATCH; ++j) cv[j] = b + j < b1 ? counts[(size_t)(b + j) * E + e] : 0;
+#pragma unroll
+            for (int j = 0; j < SCAN_BATCH; ++j) local += cv[j];
         }
-        __syncthreads();
-        const int nt = block_exclusive_scan(flags, E, tmp);
-        for (int e = tid; e < E; e += nth) {
-            mtile_off[e] = flags[e];
-            if (!tiles) continue;
-            const int next = (e + 1 < E) ? tot[e + 1] : total;
-            const int t_end = (e + 1 < E) ? flags[e + 1] : nt;
-            for (int t = flags[e]; t < t_end; ++t) tiles[t] = make_int4(tot[e] + (t - flags[e]) * mtile_rows, next, e, 0);
-        }
-        if (tid == 0) mtile_off[E] = nt;
+        part[sub * E + e] = local;
     }
+    __syncthreads();
+    for (int x = tid; x < E; x += nth) {
+        int t = 0;
+        for (int s2 = 0; s2 < nsub; ++s2) t += part[s2 * E + x];
+        tot[x] = t;
+        flags[x] = t > 0 ? 1 : 0;
+    }
+    __syncthreads();
+    const int total = block_exclusive_scan(tot, E, tmp);
+    if (mine) {
+        int base = tot[e];
+        for (int s2 = 0; s2 < sub; ++s2) base += part[s2 * E + e];
+        for (int b = b0; b < b1; b += SCAN_BATCH) {
+            if (b1 - b0 > SCAN_BATCH) {
+#pragma unroll
+                for (int j = 0; j < SCAN_BATCH; ++j) cv[j] = b + j < b1 ? counts[(size_t)(b + j) * E + e] : 0;
+            }
+#pragma unroll
+            for (int j = 0; j < SCAN_BATCH; ++j) {
+                if (b + j < b1) counts[(size_t)(b + j) * E + e] = base;
+                base += cv[j];
+            }
+        }
+    }
+    finish_grouping(tot, flags, tmp, total, E, P, offsets, sorted, active, mtile_off, tiles, mtile_rows);
+}
+
+// Slot p of router block b = (p / k) / rows: position = base[b][e] + rank of p inside
+// the block (slot_pos holds the rank on entry and the position on exit).
+__global__ __launch_bounds__(256) void group_place_kernel(const int32_t *__restrict__ ids, int P, int k, int rows,
+                                                          int E, const int32_t *__restrict__ base,
+                                                          int32_t *__restrict__ slot_pos,
+                                                          int32_t *__restrict__ sorted) {
+    const int p = blockIdx.x * 256 + threadIdx.x;
+    if (p >= P) return;
+    const int id = ids[p];
+    const int b = (p / k) / rows;
+    const int pos = base[(size_t)b * E + id] + slot_pos[p];
+    sorted[pos] = p;
+    slot_pos[p] = pos;
+}
+
+hipError_t launch_group_from_router(const moe_shape &s, const int32_t *ids, int32_t *counts, int32_t *offsets,
+                                    int32_t *sorted, int32_t *slot_pos, int32_t *active, int32_t *mtile_off,
+                                    int32_t *tiles, int mtile_rows, hipStream_t st) {
+    const int E = s.num_experts, P = s.num_tokens * s.top_k;
+    const int nb = (s.num_tokens + kRouterRows - 1) / kRouterRows;
+    const int nth = 1024;
+    const int nsub = nth / E;
+    hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(nth), (size_t)(2 * E + nth + nsub * E) * 4, st, counts, nb, E,
+                       P, offsets, sorted, active, mtile_off, mtile_off ? reinterpret_cast<int4 *>(tiles) : nullptr,
+                       mtile_rows);
+    hipError_t r = hipGetLastError();
+    if (r != hipSuccess) return r;
+    hipLaunchKernelGGL(group_place_kernel, dim3((P + 255) / 256), dim3(256), 0, st, ids, P, s.top_k, kRouterRows, E,
+                       counts, slot_pos, sorted);
+    return hipGetLastError();
 }
 
 constexpr int GROUP_CHUNK = 4096;

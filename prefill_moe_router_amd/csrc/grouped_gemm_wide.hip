@@ -55,7 +55,6 @@ constexpr int GM = 8;                   // m-tiles per group of the tile order
 
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
 
-typedef __attribute__((address_space(3))) void lds_ptr_t;
 
 struct WideParams {
     const uint8_t *a;          // x [T][K] (GATEUP) or h' [P][K] (DOWN), bf16
@@ -77,25 +76,8 @@ struct WideParams {
 // 4-way unswizzled.
 __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
 
-// one wave-wide direct load: 16 bytes per lane from g into LDS at l + 16 * lane (l
-// wave-uniform).  A plain (non-template) function keeps the builtin out of the host
-// pass's instantiation of the kernel template.
-__device__ __forceinline__ void load_lds16(const void *g, uint8_t *l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t *)l, 16, 0, 0);
-}
 
-// work-group barrier with no memory fence; "memory" keeps the compiler from moving
-// memory accesses across it (the waits before it are explicit)
-__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
 
 #define WG_INLINE __attribute__((always_inline))
 

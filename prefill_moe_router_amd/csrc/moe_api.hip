@@ -108,6 +108,11 @@ moe_status moe_router_topk(const moe_shape *shape, const void *x, const void *w_
     MOE_CHECK(check_ws(shape, ws, ws_bytes));
     const WsLayout L = ws_layout(*shape);
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (router_topk_mfma_supported(*shape)) {
+        MOE_TRY(launch_router_topk_mfma(*shape, x, w_router, bias, topk_ids, topk_w, nullptr, nullptr, st, nullptr,
+                                        nullptr));
+        return MOE_OK;
+    }
     MOE_TRY(launch_router_logits(*shape, x, w_router, bias, at<float>(ws, L.logits), st));
     MOE_TRY(launch_topk(*shape, at<float>(ws, L.logits), topk_ids, topk_w, st));
     return MOE_OK;
@@ -177,6 +182,7 @@ namespace {
 const char *const kStagesStaged = "router_logits,topk,group,gate_up,down,combine";
 const char *const kStagesFused = "decode_fused";
 const char *const kStagesGrouped = "router_logits,topk,group,gate_up,down,combine";
+const char *const kStagesGroupedFusedRouter = "router_topk,group,gate_up,down,combine";
 
 bool use_fused(const moe_shape &s) {
     return !use_grouped(s) && s.num_tokens <= 8 && decode_fused_supported(s);
@@ -229,19 +235,37 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     int32_t *err = at<int32_t>(ws, L.ctrl);
     if (use_grouped(*shape)) {
         int32_t *mtile = at<int32_t>(ws, L.mtile), *tiles = at<int32_t>(ws, L.tiles);
-        if (router_mfma_supported(*shape)) {
-            MOE_TRY(launch_router_mfma(*shape, x, w_router, bias, logits, st, se.start(0), se.stop(0)));
+        int si = 0;   // stage index, in the order moe_forward_stages names them
+        if (router_topk_mfma_supported(*shape)) {
+            // router, top-k and the per-block half of the grouping in one kernel
+            int32_t *counts = at<int32_t>(ws, L.gcounts);
+            MOE_TRY(launch_router_topk_mfma(*shape, x, w_router, bias, ids, wts, slot_pos, counts, st, se.start(si),
+                                            se.stop(si)));
+            ++si;
+            MOE_TRY(around(se, si++, st, [&] {
+                return launch_group_from_router(*shape, ids, counts, offsets, sorted, slot_pos, active, mtile, tiles,
+                                                kGroupedTileM, st);
+            }));
         } else {
-            MOE_TRY(around(se, 0, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
+            if (router_mfma_supported(*shape)) {
+                MOE_TRY(launch_router_mfma(*shape, x, w_router, bias, logits, st, se.start(si), se.stop(si)));
+                ++si;
+            } else {
+                MOE_TRY(around(se, si++, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
+            }
+            MOE_TRY(around(se, si++, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
+            MOE_TRY(around(se, si++, st, [&] {
+                return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), mtile,
+                                     tiles, kGroupedTileM, err, st);
+            }));
         }
-        MOE_TRY(around(se, 1, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
-        MOE_TRY(around(se, 2, st, [&] {
-            return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), mtile,
-                                 tiles, kGroupedTileM, err, st);
-        }));
-        MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, tiles, wts, h, st, se.start(3), se.stop(3)));
-        MOE_TRY(launch_down_mfma(*shape, *w, offsets, sorted, mtile, tiles, h, o, false, st, se.start(4), se.stop(4)));
-        MOE_TRY(around(se, 5, st, [&] { return launch_combine_rows(*shape, o, y, st); }));
+        MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, tiles, wts, h, st, se.start(si),
+                                   se.stop(si)));
+        ++si;
+        MOE_TRY(launch_down_mfma(*shape, *w, offsets, sorted, mtile, tiles, h, o, false, st, se.start(si),
+                                 se.stop(si)));
+        ++si;
+        MOE_TRY(around(se, si, st, [&] { return launch_combine_rows(*shape, o, y, st); }));
         return MOE_OK;
     }
     MOE_TRY(around(se, 0, st, [&] { return launch_router_logits(*shape, x, w_router, bias, logits, st); }));
@@ -281,7 +305,7 @@ moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *
 
 const char *moe_forward_stages(const moe_shape *shape) {
     if (check_shape(shape) != MOE_OK) return "";
-    if (use_grouped(*shape)) return kStagesGrouped;
+    if (use_grouped(*shape)) return router_topk_mfma_supported(*shape) ? kStagesGroupedFusedRouter : kStagesGrouped;
     return use_fused(*shape) ? kStagesFused : kStagesStaged;
 }
 

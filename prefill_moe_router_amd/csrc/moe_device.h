@@ -60,6 +60,30 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---- waits, barriers and direct-to-LDS loads ----------------------------------------
+
+typedef __attribute__((address_space(3))) void lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+
+// one wave-wide direct load: 16 bytes per lane from g into LDS at l + 16 * lane (l
+// wave-uniform).  A plain (non-template) function keeps the builtin out of the host
+// pass's instantiation of the kernel template.
+__device__ __forceinline__ void load_lds16(const void *g, uint8_t *l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_ptr_t *)l, 16, 0, 0);
+}
+
+// work-group barrier with no memory fence; "memory" keeps the compiler from moving
+// memory accesses across it (the waits before it are explicit)
+__device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" ::: "memory"); }
+
 // ---- wave64 reductions -----------------------------------------------------------
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -115,6 +139,98 @@ __device__ __forceinline__ uint32_t f32_order_key(float f) {
     uint32_t u = __float_as_uint(f);
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// lanes below this one
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const int l = threadIdx.x & 63;
+    return l ? (~0ull >> (64 - l)) : 0ull;
+}
+
+// Top-k of one token's E (<= 1024) logits in one wave, by radix selection on
+// order-preserving keys: the k-th largest key is found bit by bit from the
+// top with ballot counts, keys above it are kept, and keys equal to it are
+// kept in ascending expert id until k are kept (ties go to the lower id).
+// Writes ids (ascending) and weights (softmax over all E at the kept ids,
+// renormalised over the kept set when renorm) to ids[0..k) / w[0..k) (LDS) and
+// ids_g / w_g (global), each when given, and ORs sel_bit into sel_mask[e] (LDS)
+// for every kept expert e.
+template <int NJ>
+__device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int renorm, int *ids, float *w,
+                                          int32_t *ids_g, float *w_g, uint32_t *sel_mask = nullptr,
+                                          uint32_t sel_bit = 0) {
+    const int lane = threadIdx.x & 63;
+    float v[NJ];
+    uint32_t key[NJ];
+    float m = -__builtin_inff();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + 64 * j;
+        const bool ok = e < E;
+        v[j] = ok ? lg[e] : -__builtin_inff();
+        key[j] = ok ? f32_order_key(v[j]) : 0u;
+        m = fmaxf(m, v[j]);
+    }
+    m = wave_max_u(m);
+    // Bit by bit from the top: `avail` keys share the prefix chosen so far, `need` of
+    // them are still to be kept.  Once they are equal, every key sharing the prefix is
+    // kept and the remaining bits need not be looked at (the common case after a dozen
+    // bits); otherwise the walk ends at bit 0 with the threshold key itself.
+    uint32_t prefix = 0;
+    int need = K, avail = E;
+    int b = 31;
+    for (; b >= 0; --b) {
+        const uint32_t cand = prefix | (1u << b);
+        const uint32_t hi = cand >> b;   // odd, so the key 0 of a padding lane never matches
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot((key[j] >> b) == hi));
+        if (cnt >= need) {
+            prefix = cand;
+            avail = cnt;
+        } else {
+            need -= cnt;
+            avail -= cnt;
+        }
+        if (avail == need) break;
+    }
+    const int sh = b < 0 ? 0 : b;        // keys are compared on bits [sh, 32)
+    const uint32_t pfx = prefix >> sh;
+    // kept: top bits above the prefix, or equal to it among the first `need` such in id
+    // order (all of them when the walk stopped early)
+    const uint64_t lt = lanemask_lt();
+    int eq_before = 0, sel_before = 0;
+    float z = 0.f;
+    float pe[NJ];
+    bool sel[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const bool valid = key[j] != 0u;
+        const uint32_t top = key[j] >> sh;
+        const bool eq = valid && top == pfx;
+        const uint64_t eqm = __ballot(eq);
+        const int eq_rank = eq_before + __popcll(eqm & lt);
+        eq_before += __popcll(eqm);
+        sel[j] = valid && (top > pfx || (eq && eq_rank < need));
+        pe[j] = valid ? __expf(v[j] - m) : 0.f;
+        if (!renorm || sel[j]) z += pe[j];
+    }
+    const float denom = wave_sum_u(z);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const uint64_t sm = __ballot(sel[j]);
+        const int pos = sel_before + __popcll(sm & lt);
+        sel_before += __popcll(sm);
+        if (sel[j]) {
+            const int e = lane + 64 * j;
+            const float wt = pe[j] / denom;
+            if (ids) ids[pos] = e;
+            if (w) w[pos] = wt;
+            if (ids_g) ids_g[pos] = e;
+            if (w_g) w_g[pos] = wt;
+            if (sel_mask) atomicOr(sel_mask + e, sel_bit);
+        }
+    }
 }
 
 // ---- element formats -------------------------------------------------------------

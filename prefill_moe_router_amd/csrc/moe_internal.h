@@ -3,6 +3,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -29,6 +31,9 @@ inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM 
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word, the rest zero between calls.
+// tokens per work-group of the MFMA router (and per count row of its grouping output)
+constexpr int kRouterRows = 32;
+
 struct WsLayout {
     size_t ctrl, tagged, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, tiles, gcounts, h, o, total;
 };
@@ -54,7 +59,7 @@ inline WsLayout ws_layout(const moe_shape &s) {
     L.active = take((E + 1) * 4);
     L.mtile = take((E + 1) * 4);
     L.tiles = take(grouped_tile_bound(P, E) * 16);
-    L.gcounts = take((P > 0 ? (P + 4095) / 4096 : 1) * E * 4);
+    L.gcounts = take(std::max<size_t>(P > 0 ? (P + 4095) / 4096 : 1, (T + kRouterRows - 1) / kRouterRows) * E * 4);
     L.h = take(P * I * act_bytes(s.act_dtype));
     L.o = take(P * H * 4);
     L.total = off;
@@ -66,6 +71,17 @@ inline WsLayout ws_layout(const moe_shape &s) {
 // s[t,e] = bias[e] + x[t,:].w_router[e,:]  -> logits [T][E] fp32
 hipError_t launch_router_logits(const moe_shape &s, const void *x, const void *wr, const float *bias,
                                 float *logits, hipStream_t st);
+// router GEMM + top-k in one kernel (bf16, E % 32 == 0, E <= 128, H % 512 == 0): ids / w as
+// launch_topk; with slot_rank and counts (both or neither) also each slot's rank inside its
+// block of kRouterRows tokens and counts[block][E] for launch_group_from_router
+bool router_topk_mfma_supported(const moe_shape &s);
+hipError_t launch_router_topk_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias,
+                                   int32_t *ids, float *w, int32_t *slot_rank, int32_t *counts, hipStream_t st,
+                                   hipEvent_t ev0, hipEvent_t ev1);
+// grouping from the router's per-block counts and ranks: same outputs as launch_group2
+hipError_t launch_group_from_router(const moe_shape &s, const int32_t *ids, int32_t *counts, int32_t *offsets,
+                                    int32_t *sorted, int32_t *slot_pos, int32_t *active, int32_t *mtile_off,
+                                    int32_t *tiles, int mtile_rows, hipStream_t st);
 // top-k + softmax (+ renorm) over logits rows -> ids [T][k] ascending, w [T][k]
 hipError_t launch_topk(const moe_shape &s, const float *logits, int32_t *ids, float *w, hipStream_t st);
 // multi-block stable grouping (chunks of 4096 slots): counts [chunks][E] scratch;

@@ -8,6 +8,8 @@
 //   kept sum when renormalising.
 #include <float.h>
 
+#include <hip/hip_ext.h>
+
 #include "moe_device.h"
 #include "moe_internal.h"
 
@@ -63,76 +65,417 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint8_t *__res
     }
 }
 
-// One wave per token.  E <= 1024: each lane holds up to 16 scores (expert
-// lane + 64*j).  k rounds of a wave arg-max under the total order (score desc,
-// id asc) select the kept set; the kept ids are then ranked to ascending order.
+// One wave per token (E <= 1024): radix top-k selection of the token's logits row,
+// ids ascending, softmax weights (renormalised over the kept set when asked).
+template <int NJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int32_t *__restrict__ ids,
                                                    float *__restrict__ w, int T, int E, int k, int renorm) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
-    const float *s = logits + (size_t)t * E;
-    float v[16];
-    float m = -FLT_MAX;
+    wave_topk<NJ>(logits + (size_t)t * E, E, k, renorm, nullptr, nullptr, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+// ---- router GEMM + top-k in one kernel (bf16 activations, MFMA) --------------------------
+//
+// A work-group takes kRouterRows (32) tokens and all E (a multiple of 32, <= 128)
+// experts, so the top-k of each token is taken in the same work-group.  The k loop
+// runs in 64-wide steps: each step's 32 token rows and E expert rows (128 bytes of
+// each) are staged in an LDS ring by direct-to-LDS loads in which eight lanes read
+// one whole 128-byte line (whole-line requests: reading half lines or less per
+// request measured ~2.6x slower from L2 on gfx950).  Wave w computes the 32 x 16
+// expert tiles w and w + 4 with v_mfma_f32_16x16x32_bf16, so every logit is one
+// fp32 accumulation over k in a fixed order; bias is added once at the end.  Each
+// wave then selects the top-k of eight tokens.
+//
+// With grouping outputs the kernel also produces the first half of the stable counting
+// sort by expert: the number of the block's slots that chose each expert
+// (counts[block][e]) and each slot's rank among the block's slots with the same expert
+// (slot_rank[p]); the slots of a block are consecutive and each token chooses an expert
+// at most once, so the rank is the number of earlier tokens of the block that chose it.
+constexpr int RM_MAXNT = 8;   // expert tiles of 16
+
+struct RouterTopkParams {
+    const uint8_t *x, *wr;
+    const float *bias;
+    int32_t *ids;
+    float *w;
+    int32_t *slot_rank, *counts;   // both null without grouping outputs
+    int T, H, E, K, renorm;
+};
+
+// Top-k of NTOK tokens at once in one wave (lg: the tokens' logits rows, E apart; E <=
+// 64*NJ), with the selection and weights of wave_topk: the K largest logits, ties to the
+// lower expert id, ids ascending, softmax weights (renormalised over the kept set when
+// asked).  Two ways to select, both exact:
+//  - ROUNDS (small K): K rounds of a wave arg-max over the logits not yet kept (DPP max,
+//    then the lowest id holding it), about 17 instructions per round;
+//  - otherwise the radix walk of wave_topk without its early exit: the K-th largest
+//    order-preserving key tau is built bit by bit (keep a bit when at least K keys are
+//    >= the candidate), keys above tau are kept, keys equal to tau in ascending id.
+// The tokens' chains run in lockstep with no token-dependent branch, so they overlap.
+// Token tk writes ids / weights to ids_g / w_g + tk*K and s_ids + tk*K, and ORs bit
+// (bit0 + tk) into sel_mask[e] for each kept expert when sel_mask is given.  Tokens >=
+// nvalid are computed but not written.
+// DPP reductions of N independent values per lane at once, written step by step across
+// the N values so that their chains interleave; each result is read from lane 63 and is
+// wave-uniform.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ void wave_umax_n(uint32_t (&v)[N]) {
+#define MOE_UMAX_STEP(CTRL, RM)                                                     \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u<CTRL, RM>(v[i], 0u));
+    MOE_UMAX_STEP(0x111, 0xf)   // row_shr:1
+    MOE_UMAX_STEP(0x112, 0xf)   // row_shr:2
+    MOE_UMAX_STEP(0x114, 0xf)   // row_shr:4
+    MOE_UMAX_STEP(0x118, 0xf)   // row_shr:8
+    MOE_UMAX_STEP(0x142, 0xa)   // row_bcast:15 into rows 1 and 3
+    MOE_UMAX_STEP(0x143, 0xc)   // row_bcast:31 into rows 2 and 3
+#undef MOE_UMAX_STEP
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-        const int e = lane + WAVE * j;
-        v[j] = e < E ? s[e] : -FLT_MAX;
-        if (e < E) m = fmaxf(m, v[j]);
-    }
+    for (int i = 0; i < N; ++i) v[i] = (uint32_t)__builtin_amdgcn_readlane((int)v[i], 63);
+}
+template <int N>
+__device__ __forceinline__ void wave_fsum_n(float (&v)[N]) {
+#define MOE_FSUM_STEP(CTRL, RM) _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL, RM>(v[i], 0.f);
+    MOE_FSUM_STEP(0x111, 0xf)
+    MOE_FSUM_STEP(0x112, 0xf)
+    MOE_FSUM_STEP(0x114, 0xf)
+    MOE_FSUM_STEP(0x118, 0xf)
+    MOE_FSUM_STEP(0x142, 0xa)
+    MOE_FSUM_STEP(0x143, 0xc)
+#undef MOE_FSUM_STEP
 #pragma unroll
-    for (int msk = 32; msk >= 1; msk >>= 1) m = fmaxf(m, __shfl_xor(m, msk, WAVE));
-    uint32_t taken = 0;
-    int sel_e = 0x7fffffff;
-    float sel_v = -FLT_MAX;
-    for (int r = 0; r < k; ++r) {
-        float bv = -FLT_MAX;
-        int be = 0x7fffffff;
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
+// inverse of f32_order_key
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Top-k of NTOK tokens at once in one wave (lg: the tokens' logits rows, E apart; E <=
+// 64*NJ), with the selection and weights of wave_topk: the K largest logits, ties to the
+// lower expert id, ids ascending, softmax weights (renormalised over the kept set when
+// asked).  Logits are compared as order-preserving keys (-0 and +0 equal).  Two ways to
+// select, both exact:
+//  - ROUNDS (small K): K rounds of a wave arg-max over the keys not yet kept (DPP max,
+//    then the lowest id holding it);
+//  - otherwise the radix walk of wave_topk without its early exit: the K-th largest key
+//    tau is built bit by bit (keep a bit when at least K keys are >= the candidate), keys
+//    above tau are kept, keys equal to tau in ascending id.
+// The tokens' chains run in lockstep with no branch, so they overlap.  Token tk's ids and
+// weights go to s_ids / s_w + tk*K (LDS; the caller copies them out), and bit (bit0 + tk)
+// is ORed into sel_mask[e] (LDS) for each kept expert of the tokens below nvalid.  s_trash:
+// 64 words of LDS that lanes with nothing to write write to instead.
+template <int NJ, int NTOK, bool ROUNDS>
+__device__ __forceinline__ void wave_topk_multi(const float *lg, int E, int K, int renorm, int nvalid, int *s_ids,
+                                                float *s_w, uint32_t *sel_mask, int bit0, uint32_t *s_trash) {
+    const int lane = threadIdx.x & 63;
+    float v[NTOK][NJ];
+    uint32_t key[NTOK][NJ];
+    bool sel[NTOK][NJ];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = lane + WAVE * j;
-            if (e < E && !((taken >> j) & 1u) && (v[j] > bv || be == 0x7fffffff)) {
-                bv = v[j];
-                be = e;
+    for (int tk = 0; tk < NTOK; ++tk)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int e = lane + 64 * j;
+            v[tk][j] = e < E ? lg[tk * E + e] : 0.f;
+            key[tk][j] = e < E ? f32_order_key(v[tk][j]) : 0u;   // 0: no expert (below every key)
+            sel[tk][j] = false;
+        }
+    uint32_t mkey[NTOK];
+    if constexpr (ROUNDS) {
+        uint32_t kt[NTOK][NJ];
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) kt[tk][j] = key[tk][j];
+        for (int round = 0; round < K; ++round) {
+            uint32_t M[NTOK];
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                M[tk] = kt[tk][0];
+#pragma unroll
+                for (int j = 1; j < NJ; ++j) M[tk] = max(M[tk], kt[tk][j]);
+            }
+            wave_umax_n(M);
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                mkey[tk] = round == 0 ? M[tk] : mkey[tk];
+                // lowest id holding M (ids lane + 64j: the first j with a hit, then its
+                // lowest lane), by selects only
+                uint64_t hit = __ballot(kt[tk][NJ - 1] == M[tk]);
+                int wj = NJ - 1;
+#pragma unroll
+                for (int j = NJ - 2; j >= 0; --j) {
+                    const uint64_t hj = __ballot(kt[tk][j] == M[tk]);
+                    wj = hj ? j : wj;
+                    hit = hj ? hj : hit;
+                }
+                const int wl = __builtin_ctzll(hit | (1ull << 63));
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const bool win = lane == wl && j == wj;
+                    kt[tk][j] = win ? 0u : kt[tk][j];
+                    sel[tk][j] = sel[tk][j] || win;
+                }
             }
         }
-#pragma unroll
-        for (int msk = 32; msk >= 1; msk >>= 1) {
-            const float ov = __shfl_xor(bv, msk, WAVE);
-            const int oe = __shfl_xor(be, msk, WAVE);
-            if (ov > bv || (ov == bv && oe < be)) {
-                bv = ov;
-                be = oe;
-            }
-        }
-        if (lane == r) {
-            sel_e = be;
-            sel_v = bv;
-        }
-        if ((be & 63) == lane) taken |= 1u << (be >> 6);
-    }
-    float p = 0.f;
-    if (lane < k) p = __expf(sel_v - m);
-    float denom;
-    if (renorm) {
-        denom = wave_sum(p);
     } else {
-        float z = 0.f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = lane + WAVE * j;
-            if (e < E) z += __expf(v[j] - m);
+        for (int tk = 0; tk < NTOK; ++tk) {
+            mkey[tk] = key[tk][0];
+#pragma unroll
+            for (int j = 1; j < NJ; ++j) mkey[tk] = max(mkey[tk], key[tk][j]);
         }
-        denom = wave_sum(z);
+        wave_umax_n(mkey);
+        uint32_t tau[NTOK];
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk) tau[tk] = 0u;
+        for (int b = 31; b >= 0; --b) {
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                const uint32_t cand = tau[tk] | (1u << b);
+                int cnt = 0;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[tk][j] >= cand));
+                tau[tk] = cnt >= K ? cand : tau[tk];
+            }
+        }
+        const uint64_t lt = lanemask_lt();
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk) {
+            int n_gt = 0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) n_gt += __popcll(__ballot(key[tk][j] > tau[tk]));
+            const int need = K - n_gt;
+            int eq_before = 0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool eq = key[tk][j] != 0u && key[tk][j] == tau[tk];
+                const uint64_t eqm = __ballot(eq);
+                const int eq_rank = eq_before + __popcll(eqm & lt);
+                eq_before += __popcll(eqm);
+                sel[tk][j] = key[tk][j] != 0u && (key[tk][j] > tau[tk] || (eq && eq_rank < need));
+            }
+        }
     }
-    int rank = 0;
-    for (int r = 0; r < k; ++r) {
-        const int oe = __shfl(sel_e, r, WAVE);
-        rank += oe < sel_e ? 1 : 0;
+    const uint64_t lt = lanemask_lt();
+    float pe[NTOK][NJ];
+    float z[NTOK];
+#pragma unroll
+    for (int tk = 0; tk < NTOK; ++tk) {
+        const float m = f32_from_order_key(mkey[tk]);
+        z[tk] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            pe[tk][j] = key[tk][j] != 0u ? __expf(v[tk][j] - m) : 0.f;
+            z[tk] += (!renorm || sel[tk][j]) ? pe[tk][j] : 0.f;
+        }
     }
-    if (lane < k) {
-        ids[(size_t)t * k + rank] = sel_e;
-        w[(size_t)t * k + rank] = p / denom;
+    wave_fsum_n(z);
+#pragma unroll
+    for (int tk = 0; tk < NTOK; ++tk) {
+        int sel_before = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const uint64_t sm = __ballot(sel[tk][j]);
+            const int pos = sel_before + __popcll(sm & lt);
+            sel_before += __popcll(sm);
+            const int e = lane + 64 * j;
+            const bool s = sel[tk][j];
+            *(s ? reinterpret_cast<uint32_t *>(s_ids + tk * K + pos) : s_trash + lane) = (uint32_t)e;
+            *(s ? reinterpret_cast<uint32_t *>(s_w + tk * K + pos) : s_trash + lane) =
+                __float_as_uint(pe[tk][j] / z[tk]);
+            atomicOr(sel_mask + (e < E ? e : 0), s && tk < nvalid ? 1u << (bit0 + tk) : 0u);
+        }
+    }
+}
+
+#ifndef MOE_RT_NSTAGE
+#define MOE_RT_NSTAGE 4
+#endif
+constexpr int RT_NSTAGE = MOE_RT_NSTAGE;   // LDS ring depth (64-wide k steps)
+#ifndef MOE_RT_WAVES
+#define MOE_RT_WAVES 8
+#endif
+constexpr int RT_WAVES = MOE_RT_WAVES;    // 4 or 8: each computes NT / RT_WAVES expert tiles
+constexpr int RT_ROUNDS_MAX_K = 12;       // arg-max rounds up to this k, radix walk above
+
+// The 16-byte chunk c of staged row R sits at chunk slot c ^ rt_swz(R) of the row's 128
+// bytes: the 16 rows read by one 16-lane group of an MFMA operand load then fall on
+// distinct 16-byte bank groups (rows two apart share banks and differ in the key).
+__device__ __forceinline__ int rt_swz(int row) { return (row >> 1) & 7; }
+
+template <int NT>
+__global__ __launch_bounds__(64 * RT_WAVES) void router_topk_mfma_kernel(RouterTopkParams p) {
+    constexpr int E = 16 * NT;
+    constexpr int ROWS = kRouterRows + E;          // staged rows per step: tokens, then experts
+    constexpr int STAGE = ROWS * 128;
+    constexpr int NLOAD = ROWS / 8;                // 1 KB direct loads per step (8 rows each)
+    constexpr int UPW = NLOAD / 4;                 // per loading wave (waves 0-3; NT even: NLOAD % 4 == 0)
+    constexpr int NJW = (NT + RT_WAVES - 1) / RT_WAVES;   // expert tiles per wave
+    constexpr int TPW = kRouterRows / RT_WAVES;    // tokens per wave in the top-k
+    static_assert(NT % 2 == 0 && NLOAD % 4 == 0, "E must be a multiple of 32");
+    extern __shared__ __attribute__((aligned(16))) uint8_t rsm[];   // ring; then logits [32][E] fp32
+    __shared__ int s_ids[kRouterRows * 32];
+    __shared__ float s_w[kRouterRows * 32];
+    __shared__ uint32_t s_trash[RT_WAVES * 64];
+    __shared__ uint32_t s_mask[E];
+    __shared__ float s_bias[E];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int H = p.H;
+    if (threadIdx.x < E) {
+        s_mask[threadIdx.x] = 0u;
+        s_bias[threadIdx.x] = p.bias ? p.bias[threadIdx.x] : 0.f;
+    }
+    const int t0 = blockIdx.x * kRouterRows;
+    const int rows = min(kRouterRows, p.T - t0);
+    // this lane's source in each of the wave's loads: staged row R = 8j + lane/8 (padding
+    // token rows of a ragged block read the last token), chunk slot lane%8
+    const bool loader = wave < 4;
+    const uint8_t *src[UPW];
+#pragma unroll
+    for (int u = 0; u < UPW; ++u) {
+        const int R = min(8 * (wave + 4 * u) + (lane >> 3), ROWS - 1);
+        const int c = (lane & 7) ^ rt_swz(R);
+        src[u] = (R < kRouterRows ? p.x + (size_t)(t0 + min(R, rows - 1)) * H * 2
+                                  : p.wr + (size_t)(R - kRouterRows) * H * 2) + c * 16;
+    }
+    auto issue = [&](int step, int slot) __attribute__((always_inline)) {
+        if (loader) {
+#pragma unroll
+            for (int u = 0; u < UPW; ++u)
+                load_lds16(src[u] + (size_t)step * 128, rsm + slot * STAGE + (wave + 4 * u) * 1024);
+        }
+    };
+    f32x4_t acc[2][NJW];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int r16 = lane & 15, q = lane >> 4;
+    auto compute = [&](int slot) __attribute__((always_inline)) {
+        const uint8_t *st = rsm + slot * STAGE;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int c = 4 * s + q;
+            bf16x8_t a[2], b[NJW];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int R = 16 * i + r16;
+                a[i] = *reinterpret_cast<const bf16x8_t *>(st + R * 128 + ((c ^ rt_swz(R)) << 4));
+            }
+#pragma unroll
+            for (int j = 0; j < NJW; ++j) {
+                const int n = wave + RT_WAVES * j;
+                const int R = kRouterRows + 16 * min(n, NT - 1) + r16;
+                b[j] = *reinterpret_cast<const bf16x8_t *>(st + R * 128 + ((c ^ rt_swz(R)) << 4));
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < NJW; ++j)
+                    if (wave + RT_WAVES * j < NT)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+        }
+    };
+    const int nsteps = H / 64;   // >= RT_NSTAGE (H % 512 == 0)
+#pragma unroll
+    for (int s = 0; s < RT_NSTAGE - 1; ++s) issue(s, s);
+    for (int t = 0; t < nsteps; ++t) {
+        // this wave's loads of step t are done once at most the later issued steps' remain
+        const int later = min(RT_NSTAGE - 2, nsteps - 1 - t);
+        if (later >= RT_NSTAGE - 2) wait_vm<(RT_NSTAGE - 2) * UPW>();
+        else if (later == 4) wait_vm<4 * UPW>();
+        else if (later == 3) wait_vm<3 * UPW>();
+        else if (later == 2) wait_vm<2 * UPW>();
+        else if (later == 1) wait_vm<UPW>();
+        else wait_vm<0>();
+        barrier_nofence();   // everyone's loads of step t are in; step t-1's slot is free
+        if (t + RT_NSTAGE - 1 < nsteps) issue(t + RT_NSTAGE - 1, (t + RT_NSTAGE - 1) % RT_NSTAGE);
+        compute(t % RT_NSTAGE);
+    }
+    static_assert(RT_NSTAGE >= 3 && RT_NSTAGE <= 7 && (RT_NSTAGE - 2) * UPW < 64, "ring depth the waits cover");
+    wait_lgkm0();
+    barrier_nofence();   // all operand reads are done: the ring becomes the logits table
+    float *lg = reinterpret_cast<float *>(rsm);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < NJW; ++j) {
+            const int n = wave + RT_WAVES * j;
+            if (n < NT) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    lg[(16 * i + 4 * q + g) * E + 16 * n + r16] = acc[i][j][g] + s_bias[16 * n + r16];
+            }
+        }
+    __syncthreads();
+
+    const int K = p.K, rr0 = wave * TPW;
+    if (K <= RT_ROUNDS_MAX_K)
+        wave_topk_multi<(E + 63) / 64, TPW, true>(lg + rr0 * E, E, K, p.renorm, rows - rr0, s_ids + rr0 * K,
+                                                s_w + rr0 * K, s_mask, rr0, s_trash + wave * 64);
+    else
+        wave_topk_multi<(E + 63) / 64, TPW, false>(lg + rr0 * E, E, K, p.renorm, rows - rr0, s_ids + rr0 * K,
+                                                 s_w + rr0 * K, s_mask, rr0, s_trash + wave * 64);
+    __syncthreads();
+    // the block's ids and weights are one contiguous run of rows * K slots
+    const size_t g0 = (size_t)t0 * K;
+    for (int i = threadIdx.x; i < rows * K; i += 64 * RT_WAVES) {
+        p.ids[g0 + i] = s_ids[i];
+        p.w[g0 + i] = s_w[i];
+    }
+    if (!p.counts) return;
+    if (threadIdx.x < E) p.counts[(size_t)blockIdx.x * E + threadIdx.x] = __popc(s_mask[threadIdx.x]);
+    for (int i = threadIdx.x; i < rows * K; i += 64 * RT_WAVES) {
+        const int rr = i / K;
+        p.slot_rank[g0 + i] = __popc(s_mask[s_ids[i]] & ((1u << rr) - 1u));
+    }
+}
+
+bool router_topk_mfma_supported(const moe_shape &s) {
+    return s.act_dtype == MOE_BF16 && s.num_experts % 32 == 0 && s.num_experts <= 16 * RM_MAXNT &&
+           s.hidden % 512 == 0 && s.top_k <= 32;
+}
+
+int router_topk_blocks(const moe_shape &s) { return (s.num_tokens + kRouterRows - 1) / kRouterRows; }
+
+template <int NT>
+static hipError_t router_topk_go(const RouterTopkParams &prm, int blocks, hipStream_t st, hipEvent_t ev0,
+                                 hipEvent_t ev1) {
+    constexpr size_t lds = (size_t)RT_NSTAGE * (kRouterRows + 16 * NT) * 128;
+    static bool attr_done = false;
+    if (!attr_done) {
+        const hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(router_topk_mfma_kernel<NT>),
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (r != hipSuccess) return r;
+        attr_done = true;
+    }
+    if (ev0 || ev1)
+        hipExtLaunchKernelGGL(router_topk_mfma_kernel<NT>, dim3(blocks), dim3(64 * RT_WAVES), lds, st, ev0, ev1, 0,
+                              prm);
+    else
+        hipLaunchKernelGGL(router_topk_mfma_kernel<NT>, dim3(blocks), dim3(64 * RT_WAVES), lds, st, prm);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_topk_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias,
+                                   int32_t *ids, float *w, int32_t *slot_rank, int32_t *counts, hipStream_t st,
+                                   hipEvent_t ev0, hipEvent_t ev1) {
+    const RouterTopkParams prm{static_cast<const uint8_t *>(x), static_cast<const uint8_t *>(wr), bias, ids, w,
+                               slot_rank, counts, s.num_tokens, s.hidden, s.num_experts, s.top_k,
+                               s.renormalize ? 1 : 0};
+    const int nb = router_topk_blocks(s);
+    switch (s.num_experts / 32) {
+        case 1: return router_topk_go<2>(prm, nb, st, ev0, ev1);
+        case 2: return router_topk_go<4>(prm, nb, st, ev0, ev1);
+        case 3: return router_topk_go<6>(prm, nb, st, ev0, ev1);
+        default: return router_topk_go<8>(prm, nb, st, ev0, ev1);
     }
 }
 
@@ -165,8 +508,13 @@ hipError_t launch_router_logits(const moe_shape &s, const void *x, const void *w
 
 hipError_t launch_topk(const moe_shape &s, const float *logits, int32_t *ids, float *w, hipStream_t st) {
     const int T = s.num_tokens;
-    hipLaunchKernelGGL(topk_kernel, dim3((T + 3) / 4), dim3(256), 0, st, logits, ids, w, T, s.num_experts,
-                       s.top_k, s.renormalize ? 1 : 0);
+    const int E = s.num_experts, k = s.top_k, rn = s.renormalize ? 1 : 0;
+    const dim3 grid((T + 3) / 4), blk(256);
+    if (E <= 64) hipLaunchKernelGGL(topk_kernel<1>, grid, blk, 0, st, logits, ids, w, T, E, k, rn);
+    else if (E <= 128) hipLaunchKernelGGL(topk_kernel<2>, grid, blk, 0, st, logits, ids, w, T, E, k, rn);
+    else if (E <= 256) hipLaunchKernelGGL(topk_kernel<4>, grid, blk, 0, st, logits, ids, w, T, E, k, rn);
+    else if (E <= 512) hipLaunchKernelGGL(topk_kernel<8>, grid, blk, 0, st, logits, ids, w, T, E, k, rn);
+    else hipLaunchKernelGGL(topk_kernel<16>, grid, blk, 0, st, logits, ids, w, T, E, k, rn);
     return hipGetLastError();
 }
 

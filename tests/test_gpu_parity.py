@@ -69,6 +69,48 @@ def test_router_exact_ties_pick_lower_id():
     np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
 
 
+@pytest.mark.parametrize("T,H,E,K,renorm,bias", [(1, 512, 32, 1, True, "none"), (31, 512, 32, 8, False, "normal"),
+                                                 (33, 1024, 64, 8, True, "zipf"), (100, 512, 96, 32, True, "normal"),
+                                                 (257, 2048, 128, 8, False, "zipf"), (64, 512, 128, 32, True, "none")])
+def test_router_topk_mfma_shapes(T, H, E, K, renorm, bias):
+    """Router GEMM + top-k in one MFMA kernel (E a multiple of 32 up to 128, H a multiple of
+    512): ragged last token block, k from 1 to 32, with and without renormalisation and bias."""
+    note(f"router mfma T={T} H={H} E={E} K={K} renorm={renorm} bias={bias}")
+    li = layer_of(synth.Shape(T, H, E, K, 64, "bf16", "bf16", bias=bias, renorm=renorm), seed=T + E)
+    dl = DevLayer(li)
+    sh = lshape(li)
+    ws = pm.alloc_workspace(sh)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
+    w = torch.full((T, K), -7.0, dtype=torch.float32, device="cuda")
+    pm.router_topk(sh, dl.x, dl.wr, dl.bias, ids, w, ws)
+    torch.cuda.synchronize()
+    ref = oracle.router(oracle_layer(li))
+    gids, gw = ids.cpu().numpy(), w.cpu().numpy()
+    mism = (gids != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
+    ok = ~mism
+    assert max_abs(gw[ok], ref["w"][ok]) <= 1e-6
+    assert np.all(np.diff(gids, axis=1) > 0) and gids.min() >= 0 and gids.max() < E
+    note(f"  near-ties {int(ref['near'].sum())}, id mismatches {int(mism.sum())}")
+
+
+def test_router_mfma_exact_ties_pick_lower_id():
+    """Identical router rows give bit-identical logits in the MFMA router too; the lower id wins."""
+    sh_ = synth.Shape(40, 512, 32, 3, 64, "bf16", "bf16")
+    li = layer_of(sh_)
+    popular = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(li.wr[2]) * 4)
+    for e in (2, 5, 9, 20):
+        li.wr[e] = popular
+    dl = DevLayer(li)
+    sh = lshape(li)
+    ws = pm.alloc_workspace(sh)
+    ids = torch.empty(40, 3, dtype=torch.int32, device="cuda")
+    w = torch.empty(40, 3, dtype=torch.float32, device="cuda")
+    pm.router_topk(sh, dl.x, dl.wr, None, ids, w, ws)
+    ref = oracle.router(oracle_layer(li))
+    np.testing.assert_array_equal(ids.cpu().numpy(), ref["ids"])
+
+
 # ---- grouping ----------------------------------------------------------------------------
 
 def _group_gpu(ids_np, E, T, K):
