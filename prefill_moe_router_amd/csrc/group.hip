@@ -113,10 +113,9 @@ __device__ void finish_grouping(int *tot, int *flags, int *tmp, int total, int E
 // Block b takes slots [b*chunk, (b+1)*chunk): ballot-matched stable ranks inside the
 // chunk (written to slot_pos, made absolute by the scatter) and per-expert counts of
 // the chunk (counts[b][E]).
-__global__ __launch_bounds__(1024) void group_count_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
-                                                           int32_t *__restrict__ counts,
-                                                           int32_t *__restrict__ slot_pos, int32_t *__restrict__ err) {
-    extern __shared__ int smem[];
+__device__ __forceinline__ void group_count_body(const int32_t *__restrict__ ids, int P, int E, int chunk,
+                                                 int32_t *__restrict__ counts, int32_t *__restrict__ slot_pos,
+                                                 int32_t *__restrict__ err, int blk, int *smem) {
     const int nth = blockDim.x, nw = nth / WAVE;
     int *cnt = smem;
     int *wcnt = cnt + E;
@@ -125,7 +124,7 @@ __global__ __launch_bounds__(1024) void group_count_kernel(const int32_t *__rest
     while ((1 << nbits) < E) ++nbits;
     for (int e = tid; e < E; e += nth) cnt[e] = 0;
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int c0 = blockIdx.x * chunk, c1 = min(P, c0 + chunk);
+    const int c0 = blk * chunk, c1 = min(P, c0 + chunk);
     const int rounds = (c1 - c0 + nth - 1) / nth;
     for (int r = 0; r < rounds; ++r) {
         for (int i = tid; i < nw * E; i += nth) wcnt[i] = 0;
@@ -159,28 +158,31 @@ __global__ __launch_bounds__(1024) void group_count_kernel(const int32_t *__rest
         }
         __syncthreads();
     }
-    for (int e = tid; e < E; e += nth) counts[(size_t)blockIdx.x * E + e] = cnt[e];
+    for (int e = tid; e < E; e += nth) counts[(size_t)blk * E + e] = cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void group_count_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
+                                                           int32_t *__restrict__ counts,
+                                                           int32_t *__restrict__ slot_pos, int32_t *__restrict__ err) {
+    extern __shared__ int smem[];
+    group_count_body(ids, P, E, chunk, counts, slot_pos, err, blockIdx.x, smem);
 }
 
 // Every block rebuilds the expert offsets from the chunk counts (exclusive scan of the
 // totals) and its own base per expert (offset + counts of the earlier chunks), then
 // places its chunk's slots.  Block 0 also writes the offsets, the list of nonempty
 // experts and, when asked, the m-tile offsets of the grouped GEMM (tiles of mtile_rows).
-__global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
-                                                             int nb, const int32_t *__restrict__ counts,
-                                                             int32_t *__restrict__ offsets,
-                                                             int32_t *__restrict__ sorted,
-                                                             int32_t *__restrict__ slot_pos,
-                                                             int32_t *__restrict__ active,
-                                                             int32_t *__restrict__ mtile_off,
-                                                             int4 *__restrict__ tiles, int mtile_rows) {
-    extern __shared__ int smem[];
+__device__ __forceinline__ void group_scatter_body(const int32_t *__restrict__ ids, int P, int E, int chunk, int nb,
+                                                   const int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ sorted, int32_t *__restrict__ slot_pos,
+                                                   int32_t *__restrict__ active, int32_t *__restrict__ mtile_off,
+                                                   int4 *__restrict__ tiles, int mtile_rows, int blk, int *smem) {
     const int nth = blockDim.x;
     int *tot = smem;            // [E] totals, then exclusive offsets
     int *base = tot + E;        // [E] this block's base
     int *flags = base + E;      // [E]
     int *tmp = flags + E;       // [nth]
-    const int tid = threadIdx.x, b = blockIdx.x;
+    const int tid = threadIdx.x, b = blk;
     for (int e = tid; e < E; e += nth) {
         int t = 0, pre = 0;
         for (int b2 = 0; b2 < nb; ++b2) {
@@ -207,6 +209,36 @@ __global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__re
     }
     if (b != 0) return;
     finish_grouping(tot, flags, tmp, total, E, P, offsets, sorted, active, mtile_off, tiles, mtile_rows);
+}
+
+__global__ __launch_bounds__(1024) void group_scatter_kernel(const int32_t *__restrict__ ids, int P, int E, int chunk,
+                                                             int nb, const int32_t *__restrict__ counts,
+                                                             int32_t *__restrict__ offsets,
+                                                             int32_t *__restrict__ sorted,
+                                                             int32_t *__restrict__ slot_pos,
+                                                             int32_t *__restrict__ active,
+                                                             int32_t *__restrict__ mtile_off,
+                                                             int4 *__restrict__ tiles, int mtile_rows) {
+    extern __shared__ int smem[];
+    group_scatter_body(ids, P, E, chunk, nb, counts, offsets, sorted, slot_pos, active, mtile_off, tiles, mtile_rows,
+                       blockIdx.x, smem);
+}
+
+// All slots in one chunk: the count and the scatter of the two-kernel grouping run in
+// one work-group (the chunk's counts pass through global memory inside the work-group).
+__global__ __launch_bounds__(1024) void group_single_kernel(const int32_t *__restrict__ ids, int P, int E,
+                                                            int32_t *__restrict__ counts,
+                                                            int32_t *__restrict__ offsets,
+                                                            int32_t *__restrict__ sorted,
+                                                            int32_t *__restrict__ slot_pos,
+                                                            int32_t *__restrict__ active,
+                                                            int32_t *__restrict__ mtile_off, int4 *__restrict__ tiles,
+                                                            int mtile_rows, int32_t *__restrict__ err) {
+    extern __shared__ int smem[];
+    group_count_body(ids, P, E, P, counts, slot_pos, err, 0, smem);
+    __syncthreads();
+    group_scatter_body(ids, P, E, P, 1, counts, offsets, sorted, slot_pos, active, mtile_off, tiles, mtile_rows, 0,
+                       smem);
 }
 
 // ---- grouping from the router's per-block counts -----------------------------------------
@@ -315,6 +347,13 @@ hipError_t launch_group2(const moe_shape &s, const int32_t *ids, int32_t *offset
     const int nb = group_chunks(P);
     int nw = 16;
     while (nw > 1 && ((size_t)(1 + nw) * E) * 4 > 65536) nw >>= 1;
+    if (nb == 1) {
+        const size_t lds = std::max((size_t)(1 + nw) * E, (size_t)3 * E + nw * WAVE) * 4;
+        hipLaunchKernelGGL(group_single_kernel, dim3(1), dim3(nw * WAVE), lds, st, ids, P, E, counts, offsets, sorted,
+                           slot_pos, active, mtile_off, mtile_off ? reinterpret_cast<int4 *>(tiles) : nullptr,
+                           mtile_rows, err);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(group_count_kernel, dim3(nb), dim3(nw * WAVE), (size_t)(1 + nw) * E * 4, st, ids, P, E,
                        GROUP_CHUNK, counts, slot_pos, err);
     hipError_t r = hipGetLastError();

@@ -67,10 +67,21 @@ moe_status check_path(const moe_shape *s) {
 // bf16 layer: the streaming GEMV family is faster up to 48 tokens, the GEMMs from 64
 // tokens on; on the H=4096, E=256 MXFP4 layer the two meet near 128 tokens); up to 8
 // tokens the fused single-launch kernel runs
+// The grouped family's routing: the one-kernel router (router GEMM, top-k and block counts)
+// whenever the shape allows it.  Measured on the 8192-token shape's layer, it beats the
+// router GEMV + top-k + grouping kernels at every T from 32 up, even when its one
+// work-group per 32 tokens leaves most of the chip idle.
+bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
+
+// AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
+// experts, four with MXFP4 (whose streaming kernels read a quarter of the bytes); measured
+// crossovers on the decode shapes: bf16 T = 24..32 (k = 8, E = 128), MXFP4 above T = 64
+// (k = 8, E = 256)
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    return s.path == MOE_PATH_AUTO && s.num_tokens > 8 && (long)s.num_tokens * s.top_k > 3L * s.num_experts &&
-           grouped_supported(s);
+    const long per_expert = s.weight_dtype == MOE_MXFP4 ? 4L : 2L;
+    return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
+           (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
 }
 
 template <class T>
@@ -108,7 +119,7 @@ moe_status moe_router_topk(const moe_shape *shape, const void *x, const void *w_
     MOE_CHECK(check_ws(shape, ws, ws_bytes));
     const WsLayout L = ws_layout(*shape);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (router_topk_mfma_supported(*shape)) {
+    if (fused_router(*shape)) {
         MOE_TRY(launch_router_topk_mfma(*shape, x, w_router, bias, topk_ids, topk_w, nullptr, nullptr, st, nullptr,
                                         nullptr));
         return MOE_OK;
@@ -236,7 +247,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     if (use_grouped(*shape)) {
         int32_t *mtile = at<int32_t>(ws, L.mtile), *tiles = at<int32_t>(ws, L.tiles);
         int si = 0;   // stage index, in the order moe_forward_stages names them
-        if (router_topk_mfma_supported(*shape)) {
+        if (fused_router(*shape)) {
             // router, top-k and the per-block half of the grouping in one kernel
             int32_t *counts = at<int32_t>(ws, L.gcounts);
             MOE_TRY(launch_router_topk_mfma(*shape, x, w_router, bias, ids, wts, slot_pos, counts, st, se.start(si),
@@ -305,7 +316,7 @@ moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *
 
 const char *moe_forward_stages(const moe_shape *shape) {
     if (check_shape(shape) != MOE_OK) return "";
-    if (use_grouped(*shape)) return router_topk_mfma_supported(*shape) ? kStagesGroupedFusedRouter : kStagesGrouped;
+    if (use_grouped(*shape)) return fused_router(*shape) ? kStagesGroupedFusedRouter : kStagesGrouped;
     return use_fused(*shape) ? kStagesFused : kStagesStaged;
 }
 

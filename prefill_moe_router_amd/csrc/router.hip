@@ -17,9 +17,47 @@ namespace moe {
 
 constexpr int RT_TOK = 8;  // tokens per router wave tile
 
+// DPP reductions of N independent values per lane at once, written step by step across
+// the N values so that their chains interleave; each result is read from lane 63 and is
+// wave-uniform.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ void wave_umax_n(uint32_t (&v)[N]) {
+#define MOE_UMAX_STEP(CTRL, RM)                                                     \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u<CTRL, RM>(v[i], 0u));
+    MOE_UMAX_STEP(0x111, 0xf)   // row_shr:1
+    MOE_UMAX_STEP(0x112, 0xf)   // row_shr:2
+    MOE_UMAX_STEP(0x114, 0xf)   // row_shr:4
+    MOE_UMAX_STEP(0x118, 0xf)   // row_shr:8
+    MOE_UMAX_STEP(0x142, 0xa)   // row_bcast:15 into rows 1 and 3
+    MOE_UMAX_STEP(0x143, 0xc)   // row_bcast:31 into rows 2 and 3
+#undef MOE_UMAX_STEP
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (uint32_t)__builtin_amdgcn_readlane((int)v[i], 63);
+}
+template <int N>
+__device__ __forceinline__ void wave_fsum_n(float (&v)[N]) {
+#define MOE_FSUM_STEP(CTRL, RM) _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL, RM>(v[i], 0.f);
+    MOE_FSUM_STEP(0x111, 0xf)
+    MOE_FSUM_STEP(0x112, 0xf)
+    MOE_FSUM_STEP(0x114, 0xf)
+    MOE_FSUM_STEP(0x118, 0xf)
+    MOE_FSUM_STEP(0x142, 0xa)
+    MOE_FSUM_STEP(0x143, 0xc)
+#undef MOE_FSUM_STEP
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
 // One wave per (token tile of up to 8 tokens, expert).  The wave holds the
 // expert's router row in registers (CPL 16-byte chunks per lane, K split over
-// the 64 lanes, coalesced) and dots it with each token row.
+// the 64 lanes, coalesced) and dots it with each token row.  Every token row of
+// the tile is loaded before any product (rows past the end repeat the last
+// token and are not written), and the eight sums are reduced together through
+// DPP, so the tile costs about one memory round trip.
 template <class F, int CPL>
 __global__ __launch_bounds__(256) void router_logits_kernel(const uint8_t *__restrict__ x,
                                                             const uint8_t *__restrict__ wr,
@@ -35,18 +73,45 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint8_t *__res
     const size_t row_bytes = (size_t)nch * 16;
     for (int e = e_begin + wave; e < e_end; e += 4) {
         uint4 wq[CPL];
-#pragma unroll
-        for (int c = 0; c < CPL; ++c) {
-            const int ch = lane + WAVE * c;
-            wq[c] = ch < nch ? *reinterpret_cast<const uint4 *>(wr + (size_t)e * row_bytes + (size_t)ch * 16)
-                             : make_uint4(0, 0, 0, 0);
-        }
         float acc[RT_TOK];
+        if constexpr (CPL <= 8) {
+            // chunks past the row end (lanes beyond nch) read the last chunk with zero
+            // weights, so no load or product sits behind a branch; tokens in batches of TB
+            // so that a batch's activation chunks fit in registers
 #pragma unroll
-        for (int tt = 0; tt < RT_TOK; ++tt) {
-            acc[tt] = 0.f;
-            if (tt < nt) {
-                const uint8_t *xr = x + (size_t)(t0 + tt) * row_bytes;
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + WAVE * c;
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(wr + (size_t)e * row_bytes + (size_t)min(ch, nch - 1) * 16);
+                wq[c] = ch < nch ? v : make_uint4(0, 0, 0, 0);
+            }
+            constexpr int TB = CPL >= 8 ? 2 : RT_TOK;
+#pragma unroll
+            for (int t8 = 0; t8 < RT_TOK; t8 += TB) {
+#pragma unroll
+                for (int tt = t8; tt < t8 + TB; ++tt) {
+                    acc[tt] = 0.f;
+                    const uint8_t *xr = x + (size_t)(t0 + min(tt, nt - 1)) * row_bytes;
+#pragma unroll
+                    for (int c = 0; c < CPL; ++c) {
+                        const int ch = min(lane + WAVE * c, nch - 1);
+                        acc[tt] = chunk_dot<F>(wq[c], 0, xr + (size_t)ch * F::XB, acc[tt]);
+                    }
+                }
+                if (TB < RT_TOK) __builtin_amdgcn_sched_barrier(0);   // keep the batches apart
+            }
+        } else {
+            // very wide rows: guarded chunks, one token at a time (fits the register file)
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+                const int ch = lane + WAVE * c;
+                wq[c] = ch < nch ? *reinterpret_cast<const uint4 *>(wr + (size_t)e * row_bytes + (size_t)ch * 16)
+                                 : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int tt = 0; tt < RT_TOK; ++tt) {
+                acc[tt] = 0.f;
+                const uint8_t *xr = x + (size_t)(t0 + min(tt, nt - 1)) * row_bytes;
 #pragma unroll
                 for (int c = 0; c < CPL; ++c) {
                     const int ch = lane + WAVE * c;
@@ -54,13 +119,13 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const uint8_t *__res
                 }
             }
         }
+        wave_fsum_n(acc);
         const float b = bias ? bias[e] : 0.f;
+        if (lane < nt) {
+            float v = acc[0];
 #pragma unroll
-        for (int tt = 0; tt < RT_TOK; ++tt) {
-            if (tt < nt) {
-                const float v = wave_sum(acc[tt]);
-                if (lane == 0) logits[(size_t)(t0 + tt) * E + e] = v + b;
-            }
+            for (int tt = 1; tt < RT_TOK; ++tt) v = lane == tt ? acc[tt] : v;
+            logits[(size_t)(t0 + lane) * E + e] = v + b;
         }
     }
 }
@@ -116,41 +181,6 @@ struct RouterTopkParams {
 // Token tk writes ids / weights to ids_g / w_g + tk*K and s_ids + tk*K, and ORs bit
 // (bit0 + tk) into sel_mask[e] for each kept expert when sel_mask is given.  Tokens >=
 // nvalid are computed but not written.
-// DPP reductions of N independent values per lane at once, written step by step across
-// the N values so that their chains interleave; each result is read from lane 63 and is
-// wave-uniform.
-template <int CTRL, int ROW_MASK = 0xf>
-__device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t fill) {
-    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
-}
-template <int N>
-__device__ __forceinline__ void wave_umax_n(uint32_t (&v)[N]) {
-#define MOE_UMAX_STEP(CTRL, RM)                                                     \
-    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u<CTRL, RM>(v[i], 0u));
-    MOE_UMAX_STEP(0x111, 0xf)   // row_shr:1
-    MOE_UMAX_STEP(0x112, 0xf)   // row_shr:2
-    MOE_UMAX_STEP(0x114, 0xf)   // row_shr:4
-    MOE_UMAX_STEP(0x118, 0xf)   // row_shr:8
-    MOE_UMAX_STEP(0x142, 0xa)   // row_bcast:15 into rows 1 and 3
-    MOE_UMAX_STEP(0x143, 0xc)   // row_bcast:31 into rows 2 and 3
-#undef MOE_UMAX_STEP
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = (uint32_t)__builtin_amdgcn_readlane((int)v[i], 63);
-}
-template <int N>
-__device__ __forceinline__ void wave_fsum_n(float (&v)[N]) {
-#define MOE_FSUM_STEP(CTRL, RM) _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL, RM>(v[i], 0.f);
-    MOE_FSUM_STEP(0x111, 0xf)
-    MOE_FSUM_STEP(0x112, 0xf)
-    MOE_FSUM_STEP(0x114, 0xf)
-    MOE_FSUM_STEP(0x118, 0xf)
-    MOE_FSUM_STEP(0x142, 0xa)
-    MOE_FSUM_STEP(0x143, 0xc)
-#undef MOE_FSUM_STEP
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
-}
-
 // inverse of f32_order_key
 __device__ __forceinline__ float f32_from_order_key(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);

@@ -94,6 +94,29 @@ def test_router_topk_mfma_shapes(T, H, E, K, renorm, bias):
     note(f"  near-ties {int(ref['near'].sum())}, id mismatches {int(mism.sum())}")
 
 
+@pytest.mark.parametrize("T,H,E,K,act", [(12, 4096, 8, 2, "f32"), (9, 6144, 16, 4, "bf16"), (13, 1024, 48, 5, "bf16"),
+                                         (3, 2048, 64, 8, "bf16")])
+def test_router_gemv_shapes(T, H, E, K, act):
+    """Router GEMV + top-k (the kernels used below the MFMA router's shapes): 1 to 16
+    chunks per lane, ragged 8-token tiles, bias, ids exact away from near-ties."""
+    note(f"router gemv T={T} H={H} E={E} K={K} {act}")
+    w = "f32" if act == "f32" else "bf16"
+    li = layer_of(synth.Shape(T, H, E, K, 64, act, w, bias="normal"), seed=H + E)
+    dl = DevLayer(li)
+    sh = lshape(li)
+    ws = pm.alloc_workspace(sh)
+    ids = torch.full((T, K), -7, dtype=torch.int32, device="cuda")
+    wt = torch.full((T, K), -7.0, dtype=torch.float32, device="cuda")
+    pm.router_topk(sh, dl.x, dl.wr, dl.bias, ids, wt, ws)
+    torch.cuda.synchronize()
+    ref = oracle.router(oracle_layer(li))
+    gids, gw = ids.cpu().numpy(), wt.cpu().numpy()
+    mism = (gids != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
+    assert max_abs(gw[~mism], ref["w"][~mism]) <= 1e-6
+    assert np.all(np.diff(gids, axis=1) > 0)
+
+
 def test_router_mfma_exact_ties_pick_lower_id():
     """Identical router rows give bit-identical logits in the MFMA router too; the lower id wins."""
     sh_ = synth.Shape(40, 512, 32, 3, 64, "bf16", "bf16")
