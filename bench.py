@@ -78,6 +78,9 @@ WORKLOADS = {
                     "H=2048, E=128, top-8, I=768"),
     "mxfp4_decode1": ("c4_mxfp4_decode1", "decode, 1 token, MXFP4 experts, bf16 acts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_decode8": ("c4_mxfp4_decode8", "decode, 8 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
+    "nvfp4_decode1": ("c5_nvfp4_decode1", "decode, 1 token, NVFP4 experts (E4M3 scale per 16), bf16 acts: "
+                      "H=4096, E=256, top-8, I=1024"),
+    "nvfp4_decode8": ("c5_nvfp4_decode8", "decode, 8 tokens, NVFP4 experts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_prefill4096": ("c4_mxfp4_prefill4096",
                           "prefill chunk, 4096 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
     "tiny": ("c0_tiny_f32", "tiny fp32: 4 tokens, H=256, E=8, top-2, I=128"),
@@ -89,7 +92,7 @@ def log(msg):
 
 
 def weight_bytes_per_elem(w: str) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0}[w]
+    return {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0, "nvfp4": 0.5 + 1.0 / 16.0}[w]
 
 
 def act_bytes(a: str) -> int:
@@ -139,13 +142,14 @@ def main():
             return None
         return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
 
-    w0 = dict(wg=dev(li.wg), wu=dev(li.wu), wd=dev(li.wd), sg=dev(li.sg), su=dev(li.su), sd=dev(li.sd))
-    wcopies = [w0] + [{k: (v.clone() if v is not None else None) for k, v in w0.items()} for _ in range(copies - 1)]
+    w0 = dict(wg=dev(li.wg), wu=dev(li.wu), wd=dev(li.wd), sg=dev(li.sg), su=dev(li.su), sd=dev(li.sd), ts=li.ts)
+    wcopies = [w0] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in w0.items()}
+                      for _ in range(copies - 1)]
     wr, bias = dev(li.wr), dev(li.bias)
     xs = [dev(synth.make_x(sh, seed=0, batch=b)) for b in range(copies)]
     shape = pm.LayerShape(sh.T, sh.H, sh.E, sh.K, sh.I, sh.renorm,
                           pm.F32 if sh.act == "f32" else pm.BF16,
-                          {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4}[sh.w], path)
+                          {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4}[sh.w], path)
     ws = pm.alloc_workspace(shape)
     ydt = torch.float32 if sh.act == "f32" else torch.int16
     ys = [torch.empty(sh.T, sh.H, dtype=ydt, device="cuda") for _ in range(copies)]
@@ -296,7 +300,8 @@ def cpu_baseline(li, sh, target_s: float) -> dict:
 
     def layer_for(x):
         return oracle.Layer(x=x, wr=li.wr, wg=li.wg, wu=li.wu, wd=li.wd, top_k=sh.K, renorm=sh.renorm,
-                            bias=li.bias, sg=li.sg, su=li.su, sd=li.sd)
+                            bias=li.bias, sg=li.sg, su=li.su, sd=li.sd,
+                            fmt="nvfp4" if sh.w == "nvfp4" else None, ts=li.ts)
 
     threads = oracle.num_threads()
     if sh.T <= 8:

@@ -27,7 +27,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
 
 
 class _Layer(ctypes.Structure):
@@ -38,6 +38,7 @@ class _Layer(ctypes.Structure):
         ("x", ctypes.c_void_p), ("wr", ctypes.c_void_p), ("bias", ctypes.c_void_p),
         ("wg", ctypes.c_void_p), ("wu", ctypes.c_void_p), ("wd", ctypes.c_void_p),
         ("sg", ctypes.c_void_p), ("su", ctypes.c_void_p), ("sd", ctypes.c_void_p),
+        ("tsg", ctypes.c_double), ("tsu", ctypes.c_double), ("tsd", ctypes.c_double),
     ]
 
 
@@ -59,6 +60,8 @@ def lib():
         L.orc_decode_e2m1.argtypes = [ctypes.c_uint]
         L.orc_decode_e8m0.restype = ctypes.c_double
         L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
+        L.orc_decode_e4m3.restype = ctypes.c_double
+        L.orc_decode_e4m3.argtypes = [ctypes.c_uint8]
         L.orc_router.restype = ctypes.c_int
         L.orc_router.argtypes = [P(_Layer), ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p,
                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
@@ -91,7 +94,9 @@ class Layer:
     x [T,H] and wr [E,H]: float32, or uint16 holding bf16 bits.
     wg, wu [E,I,H] and wd [E,H,I]: float32, uint16 (bf16 bits), or for MXFP4
     uint8 packed codes [E,I,H/2] / [E,H,I/2] with uint8 E8M0 scales sg, su
-    [E,I,H/32] and sd [E,H,I/32].  bias [E] float32 or None.
+    [E,I,H/32] and sd [E,H,I/32].  fmt="nvfp4": the same codes with uint8 E4M3
+    scales [E,I,H/16] / [E,H,I/16] and the tensor scales ts (gate, up, down).
+    bias [E] float32 or None.
     """
     x: np.ndarray
     wr: np.ndarray
@@ -104,6 +109,8 @@ class Layer:
     sg: Optional[np.ndarray] = None
     su: Optional[np.ndarray] = None
     sd: Optional[np.ndarray] = None
+    fmt: Optional[str] = None
+    ts: tuple = (1.0, 1.0, 1.0)
 
     @property
     def act_dtype(self) -> int:
@@ -115,13 +122,13 @@ class Layer:
             return F32
         if self.wg.dtype == np.uint16:
             return BF16
-        return MXFP4
+        return NVFP4 if self.fmt == "nvfp4" else MXFP4
 
     @property
     def dims(self):
         T, H = self.x.shape
         E = self.wr.shape[0]
-        I = self.wd.shape[2] * (2 if self.w_dtype == MXFP4 else 1)
+        I = self.wd.shape[2] * (2 if self.w_dtype in (MXFP4, NVFP4) else 1)
         return T, H, E, self.top_k, I
 
     def _struct(self) -> _Layer:
@@ -129,7 +136,8 @@ class Layer:
         self._keep = [self.x, self.wr, self.bias, self.wg, self.wu, self.wd, self.sg, self.su, self.sd]
         return _Layer(T, H, E, K, I, int(bool(self.renorm)), self.act_dtype, self.w_dtype,
                       _ptr(self.x), _ptr(self.wr), _ptr(self.bias), _ptr(self.wg), _ptr(self.wu),
-                      _ptr(self.wd), _ptr(self.sg), _ptr(self.su), _ptr(self.sd))
+                      _ptr(self.wd), _ptr(self.sg), _ptr(self.su), _ptr(self.sd),
+                      float(self.ts[0]), float(self.ts[1]), float(self.ts[2]))
 
 
 def _tokens(layer: Layer, tokens):
@@ -214,6 +222,10 @@ def decode_e2m1(code: int) -> float:
 
 def decode_e8m0(code: int) -> float:
     return lib().orc_decode_e8m0(code)
+
+
+def decode_e4m3(code: int) -> float:
+    return lib().orc_decode_e4m3(code)
 
 
 def num_threads() -> int:

@@ -37,6 +37,7 @@
 #define ORC_F32 0
 #define ORC_BF16 1
 #define ORC_MXFP4 2
+#define ORC_NVFP4 3
 
 typedef struct {
     int32_t T;          /* number of tokens */
@@ -46,16 +47,17 @@ typedef struct {
     int32_t I;          /* expert intermediate size */
     int32_t renorm;     /* 1: kept weights renormalised to sum 1 */
     int32_t act_dtype;  /* x and router weight: ORC_F32 or ORC_BF16 */
-    int32_t w_dtype;    /* expert weights: ORC_F32, ORC_BF16 or ORC_MXFP4 */
+    int32_t w_dtype;    /* expert weights: ORC_F32, ORC_BF16, ORC_MXFP4 or ORC_NVFP4 */
     const void *x;      /* [T][H] */
     const void *wr;     /* [E][H] */
     const float *bias;  /* [E] or NULL */
     const void *wg;     /* [E][I][H]   (MXFP4: [E][I][H/2] bytes) */
     const void *wu;     /* [E][I][H] */
     const void *wd;     /* [E][H][I]   (MXFP4: [E][H][I/2] bytes) */
-    const uint8_t *sg;  /* MXFP4 scales [E][I][H/32] */
-    const uint8_t *su;  /* [E][I][H/32] */
-    const uint8_t *sd;  /* [E][H][I/32] */
+    const uint8_t *sg;  /* MXFP4 scales [E][I][H/32]; NVFP4 [E][I][H/16] */
+    const uint8_t *su;  /* [E][I][H/32] or [E][I][H/16] */
+    const uint8_t *sd;  /* [E][H][I/32] or [E][H][I/16] */
+    double tsg, tsu, tsd; /* NVFP4 tensor scales of gate, up and down */
 } orc_layer;
 
 /* ---- exact decoders of the stored formats ------------------------------ */
@@ -85,22 +87,35 @@ double orc_decode_e8m0(uint8_t code)
     return ldexp(1.0, (int)code - 127);
 }
 
+/* OCP FP8 E4M3: sign bit 7, exponent bits 6..3 (bias 7), mantissa bits 2..0; exponent
+ * field 0 is subnormal (mantissa/8 * 2^-6); no infinities; S.1111.111 is NaN. */
+double orc_decode_e4m3(uint8_t code)
+{
+    unsigned s = (code >> 7) & 1u, e = (code >> 3) & 15u, m = code & 7u;
+    if (e == 15u && m == 7u) return NAN;
+    double v = (e == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return s ? -v : v;
+}
+
 static double act_at(const orc_layer *L, const void *base, size_t idx)
 {
     if (L->act_dtype == ORC_F32) return (double)((const float *)base)[idx];
     return orc_decode_bf16(((const uint16_t *)base)[idx]);
 }
 
-/* element (row, col) of an expert matrix stored row-major [rows][cols] */
-static double wt_at(const orc_layer *L, const void *w, const uint8_t *s,
+/* element (row, col) of an expert matrix stored row-major [rows][cols]; ts is the
+ * matrix's NVFP4 tensor scale */
+static double wt_at(const orc_layer *L, const void *w, const uint8_t *s, double ts,
                     size_t row, size_t cols, size_t col)
 {
     if (L->w_dtype == ORC_F32) return (double)((const float *)w)[row * cols + col];
     if (L->w_dtype == ORC_BF16) return orc_decode_bf16(((const uint16_t *)w)[row * cols + col]);
-    /* MXFP4: two codes per byte, the even element in the low nibble; one
-     * E8M0 scale per 32 consecutive elements of a row. */
+    /* MXFP4 and NVFP4: two codes per byte, the even element in the low nibble */
     uint8_t byte = ((const uint8_t *)w)[row * (cols / 2) + col / 2];
     unsigned code = (col & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
+    if (L->w_dtype == ORC_NVFP4) /* one E4M3 scale per 16 elements, then the tensor scale */
+        return orc_decode_e2m1(code) * orc_decode_e4m3(s[row * (cols / 16) + col / 16]) * ts;
+    /* MXFP4: one E8M0 scale per 32 consecutive elements of a row */
     return orc_decode_e2m1(code) * orc_decode_e8m0(s[row * (cols / 32) + col / 32]);
 }
 
@@ -237,21 +252,21 @@ int orc_group(int T, int k, int E, const int32_t *ids, int32_t *off, int32_t *so
 static void expert_apply(const orc_layer *L, int t, int e, double *o, double *a)
 {
     const int H = L->H, I = L->I;
-    const int mx = (L->w_dtype == ORC_MXFP4);
+    const int sc = (L->w_dtype == ORC_MXFP4 || L->w_dtype == ORC_NVFP4);
     const size_t rows_gu = (size_t)e * I, rows_d = (size_t)e * H;
     for (int i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
         for (int h = 0; h < H; ++h) {
             double xv = act_at(L, L->x, (size_t)t * H + h);
-            g += wt_at(L, L->wg, mx ? L->sg : NULL, rows_gu + i, (size_t)H, (size_t)h) * xv;
-            u += wt_at(L, L->wu, mx ? L->su : NULL, rows_gu + i, (size_t)H, (size_t)h) * xv;
+            g += wt_at(L, L->wg, sc ? L->sg : NULL, L->tsg, rows_gu + i, (size_t)H, (size_t)h) * xv;
+            u += wt_at(L, L->wu, sc ? L->su : NULL, L->tsu, rows_gu + i, (size_t)H, (size_t)h) * xv;
         }
         a[i] = g / (1.0 + exp(-g)) * u;
     }
     for (int n = 0; n < H; ++n) {
         double acc = 0.0;
         for (int i = 0; i < I; ++i)
-            acc += wt_at(L, L->wd, mx ? L->sd : NULL, rows_d + n, (size_t)I, (size_t)i) * a[i];
+            acc += wt_at(L, L->wd, sc ? L->sd : NULL, L->tsd, rows_d + n, (size_t)I, (size_t)i) * a[i];
         o[n] = acc;
     }
 }

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_router.so")
 # status codes
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 # element formats
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
 # expert FFN kernel family
 PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 # device error bits
@@ -49,7 +49,8 @@ class Shape(ctypes.Structure):
 
 class ExpertWeights(ctypes.Structure):
     _fields_ = [("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
-                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p),
+                ("ts_gate", ctypes.c_float), ("ts_up", ctypes.c_float), ("ts_down", ctypes.c_float)]
 
 
 _lib = None
@@ -142,8 +143,9 @@ def alloc_workspace(shape: LayerShape, device="cuda"):
     return torch.zeros(n, dtype=torch.uint8, device=device)
 
 
-def _weights(wg, wu, wd, sg=None, su=None, sd=None) -> ExpertWeights:
-    return ExpertWeights(_p(wg), _p(wu), _p(wd), _p(sg), _p(su), _p(sd))
+def _weights(wg, wu, wd, sg=None, su=None, sd=None, ts=(1.0, 1.0, 1.0)) -> ExpertWeights:
+    """ts: the NVFP4 tensor scales of gate, up and down (ignored for other formats)."""
+    return ExpertWeights(_p(wg), _p(wu), _p(wd), _p(sg), _p(su), _p(sd), float(ts[0]), float(ts[1]), float(ts[2]))
 
 
 def router_topk(shape: LayerShape, x, w_router, bias, topk_ids, topk_w, ws, stream=None):

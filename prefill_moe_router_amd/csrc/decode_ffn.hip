@@ -41,8 +41,9 @@ __device__ __forceinline__ float group_sum(float v) {
     return dpp_sum16(v);
 }
 
-// load chunk ch of a weight row (16 bytes, plus its E8M0 scale for MXFP4) and decode
-// it into W 16-byte words: bf16 pairs (bf16, MXFP4) or 4 fp32 (fp32)
+// load chunk ch of a weight row (16 bytes, plus its scale code for MXFP4 / NVFP4) and
+// decode it into W 16-byte words: bf16 pairs (bf16, MXFP4, NVFP4) or 4 fp32 (fp32).
+// NVFP4 elements are E2M1 codes times their 16-element block's E4M3 scale, exact in bf16.
 template <class F>
 __device__ __forceinline__ void load_chunk(const uint8_t *row, const uint8_t *srow, int ch, bool ok,
                                            u32x4_t (&w)[dec_words<F>()]) {
@@ -53,7 +54,22 @@ __device__ __forceinline__ void load_chunk(const uint8_t *row, const uint8_t *sr
         return;
     }
     const u32x4_t q = *reinterpret_cast<const u32x4_t *>(row + (size_t)ch * 16);
-    if constexpr (W == 4) {
+    if constexpr (W == 4 && F::SB == 2) {
+        // NVFP4: the power-of-two part of the block's E4M3 scale in the convert, then the
+        // remaining factor (the products are exact in bf16)
+        const uint32_t code = load_scale<F>(srow, ch);
+        float p2[2], fm[2];
+        e4m3_split(code & 0xffu, p2[0], fm[0]);
+        e4m3_split(code >> 8, p2[1], fm[1]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float s = p2[u >> 1], f = fm[u >> 1];
+            w[u][0] = bf16x2_mul_exact(fp4x2_to_bf16x2<0>(q[u], s), f);
+            w[u][1] = bf16x2_mul_exact(fp4x2_to_bf16x2<1>(q[u], s), f);
+            w[u][2] = bf16x2_mul_exact(fp4x2_to_bf16x2<2>(q[u], s), f);
+            w[u][3] = bf16x2_mul_exact(fp4x2_to_bf16x2<3>(q[u], s), f);
+        }
+    } else if constexpr (W == 4) {
         const float s = e8m0_to_f32(srow[ch]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -115,7 +131,8 @@ constexpr int passes() { return F::EPC == 32 ? 4 : 1; }
 struct StreamParams {
     const uint8_t *act;         // x [T][H] (gate/up) or h' [P][I] in sorted order (down)
     const uint8_t *w0, *w1;     // gate / up [E][I][H], or down [E][H][I] (w1 unused)
-    const uint8_t *s0, *s1;     // MXFP4 scales
+    const uint8_t *s0, *s1;     // MXFP4 / NVFP4 scales
+    float ts0, ts1;             // NVFP4 tensor scales of w0 / w1 (1 otherwise)
     const int32_t *offsets, *sorted, *active;
     const float *wts;           // gate weight per slot (gate/up) or null
     uint8_t *out;               // h' [P][I] (act dtype) or o [P][H] fp32
@@ -140,7 +157,7 @@ __global__ __launch_bounds__(SNT) void stream_ffn_kernel(StreamParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int grp = lane / LPR, li = lane % LPR;
     const int nch = p.K / F::EPC;
-    const size_t wrow = (size_t)nch * 16, srow = (size_t)nch;
+    const size_t wrow = (size_t)nch * 16, srow = (size_t)nch * (F::SCALED ? F::SB : 1);
     const int ab = p.act_f32 ? 4 : 2;
     const size_t xrow = (size_t)p.K * ab;                 // bytes of one activation row
 
@@ -203,8 +220,8 @@ __global__ __launch_bounds__(SNT) void stream_ffn_kernel(StreamParams p) {
 #pragma unroll
             for (int r = 0; r < RG; ++r) {
                 const int row = row0 + q * RPP + r * GPW * SWAVES;
-                const float s0 = group_sum<LPR>(acc[0][r]);
-                const float s1 = NMAT == 2 ? group_sum<LPR>(acc[NMAT - 1][r]) : 0.f;
+                const float s0 = group_sum<LPR>(acc[0][r]) * p.ts0;
+                const float s1 = NMAT == 2 ? group_sum<LPR>(acc[NMAT - 1][r]) * p.ts1 : 0.f;
                 if (li == LPR - 1 && row < p.N) {
                     if (GATEUP) {
                         const float sc = p.wts ? p.wts[p.sorted[pos]] : 1.f;
@@ -299,7 +316,7 @@ static hipError_t stream_launch(StreamParams prm, const moe_shape &s, hipStream_
 
 bool stream_ffn_supported(const moe_shape &s) {
     const size_t ab = act_bytes(s.act_dtype);
-    const int epc = s.weight_dtype == MOE_MXFP4 ? 32 : s.weight_dtype == MOE_BF16 ? 8 : 4;
+    const int epc = s.weight_dtype == MOE_BF16 ? 8 : s.weight_dtype == MOE_F32 ? 4 : 32;
     // one activation row must fit the staging area; rows of at most 16 chunks per lane
     return (size_t)s.hidden * ab <= STAGE_BYTES && (size_t)s.intermediate * ab <= STAGE_BYTES &&
            s.hidden / epc <= 64 * 16 && s.intermediate / epc <= 64 * 16;
@@ -314,6 +331,8 @@ hipError_t launch_decode_gateup(const moe_shape &s, const void *x, const moe_exp
     prm.w1 = static_cast<const uint8_t *>(w.w_up);
     prm.s0 = w.s_gate;
     prm.s1 = w.s_up;
+    prm.ts0 = s.weight_dtype == MOE_NVFP4 ? w.ts_gate : 1.f;
+    prm.ts1 = s.weight_dtype == MOE_NVFP4 ? w.ts_up : 1.f;
     prm.offsets = offsets;
     prm.sorted = sorted;
     prm.active = active;
@@ -326,6 +345,7 @@ hipError_t launch_decode_gateup(const moe_shape &s, const void *x, const moe_exp
     switch (s.weight_dtype) {
         case MOE_F32: return stream_launch<FmtF32, true>(prm, s, st);
         case MOE_BF16: return stream_launch<FmtBF16, true>(prm, s, st);
+        case MOE_NVFP4: return stream_launch<FmtNV4, true>(prm, s, st);
         default: return stream_launch<FmtMX4, true>(prm, s, st);
     }
 }
@@ -336,6 +356,8 @@ hipError_t launch_decode_down(const moe_shape &s, const moe_expert_weights &w, c
     prm.act = static_cast<const uint8_t *>(h);
     prm.w0 = static_cast<const uint8_t *>(w.w_down);
     prm.s0 = w.s_down;
+    prm.ts0 = s.weight_dtype == MOE_NVFP4 ? w.ts_down : 1.f;
+    prm.ts1 = 1.f;
     prm.offsets = offsets;
     prm.active = active;
     prm.out = reinterpret_cast<uint8_t *>(o);
@@ -346,6 +368,7 @@ hipError_t launch_decode_down(const moe_shape &s, const moe_expert_weights &w, c
     switch (s.weight_dtype) {
         case MOE_F32: return stream_launch<FmtF32, false>(prm, s, st);
         case MOE_BF16: return stream_launch<FmtBF16, false>(prm, s, st);
+        case MOE_NVFP4: return stream_launch<FmtNV4, false>(prm, s, st);
         default: return stream_launch<FmtMX4, false>(prm, s, st);
     }
 }

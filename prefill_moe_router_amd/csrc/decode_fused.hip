@@ -60,6 +60,7 @@ struct FusedParams {
     uint8_t *hbuf;    // workspace [P][I] (activation dtype)
     uint64_t *bar;    // workspace control word: grid-barrier arrivals (only grows)
     int32_t *err;
+    float tsg, tsu, tsd;   // tensor scales of the gate, up and down weights (1 unless NVFP4)
     int T, H, E, K, I, renorm, nblocks;
 };
 
@@ -111,7 +112,7 @@ __device__ __forceinline__ void load_chunks(const uint8_t *row, const uint8_t *s
         const int ch = lane0 + stride * c;
         const bool ok = ch < nch;
         q[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-        s[c] = (F::SCALED && ok) ? (uint32_t)srow[ch] : 0u;
+        s[c] = (F::SCALED && ok) ? load_scale<F>(srow, ch) : 0u;
     }
 }
 
@@ -343,8 +344,10 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         auto fetch = [&](int q, uint4 (&g)[CG], uint32_t (&gsc)[CG], uint4 (&u)[CG], uint32_t (&usc)[CG]) {
             const int uu = q / I, i = q - uu * I;
             const size_t rsel = (size_t)s_act_e[uu] * I + i;
-            load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * nch : nullptr, nch, lane, WAVE, g, gsc);
-            load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * nch : nullptr, nch, lane, WAVE, u, usc);
+            load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * nch * F::SB : nullptr, nch, lane, WAVE,
+                               g, gsc);
+            load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * nch * F::SB : nullptr, nch, lane, WAVE,
+                               u, usc);
         };
         auto consume = [&](int q, const uint4 (&g)[CG], const uint32_t (&gsc)[CG], const uint4 (&u)[CG],
                            const uint32_t (&usc)[CG]) {
@@ -354,8 +357,8 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             for (int c = 0; c < FMAX_T; ++c) {
                 if (c < cnt) {
                     const uint8_t *xa = smem + (size_t)s_tok[start + c] * xrow;
-                    const float gv = dpp_sum64(row_dot<F, CG>(g, gsc, xa, nch, lane, WAVE));
-                    const float uv = dpp_sum64(row_dot<F, CG>(u, usc, xa, nch, lane, WAVE));
+                    const float gv = dpp_sum64(row_dot<F, CG>(g, gsc, xa, nch, lane, WAVE)) * p.tsg;
+                    const float uv = dpp_sum64(row_dot<F, CG>(u, usc, xa, nch, lane, WAVE)) * p.tsu;
                     if (lane == 63)
                         store_act_sc1(p.hbuf, (size_t)(start + c) * I + i, s_wq[start + c] * swiglu(gv, uv), f32);
                 }
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             const int ch = li + LR * c;
             const bool ok = okr && ch < nchd;
             dq[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-            ds[c] = (F::SCALED && ok) ? (uint32_t)p.sd[rsel * nchd + ch] : 0u;
+            ds[c] = (F::SCALED && ok) ? load_scale<F>(p.sd, rsel * nchd + ch) : 0u;
         }
     };
     bar_arrive(p.bar);
@@ -450,7 +453,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                 const int t = s_tok[q];
                 const uint8_t *ha = smem + (size_t)q * hrow;
                 float d = row_dot<F, NC>(dq, ds, ha, nchd, li, LR);
-                d = lane_group_sum<LR>(d);
+                d = lane_group_sum<LR>(d) * p.tsd;
                 if (li == LR - 1) atomicAdd(part + t * FMAX_RT + rr, d);
             }
         };
@@ -595,6 +598,10 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     prm.sg = w.s_gate;
     prm.su = w.s_up;
     prm.sd = w.s_down;
+    const bool nv = s.weight_dtype == MOE_NVFP4;
+    prm.tsg = nv ? w.ts_gate : 1.f;
+    prm.tsu = nv ? w.ts_up : 1.f;
+    prm.tsd = nv ? w.ts_down : 1.f;
     prm.y = static_cast<uint8_t *>(y);
     prm.ids_out = ids_out;
     prm.w_out = w_out;
@@ -615,6 +622,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     switch (s.weight_dtype) {
         case MOE_F32: return fused_dispatch<FmtF32, FmtF32>(s, prm, lds, st, ev0, ev1);
         case MOE_BF16: return fused_dispatch<FmtBF16, FmtBF16>(s, prm, lds, st, ev0, ev1);
+        case MOE_NVFP4: return fused_dispatch<FmtNV4, FmtBF16>(s, prm, lds, st, ev0, ev1);
         default: return fused_dispatch<FmtMX4, FmtBF16>(s, prm, lds, st, ev0, ev1);
     }
 }

@@ -3,6 +3,7 @@
 // here touches device memory from the host or synchronises, except
 // moe_check_device_error.
 #include <algorithm>
+#include <cmath>
 
 #include "moe_internal.h"
 
@@ -24,7 +25,8 @@ moe_status check_shape(const moe_shape *s) {
     if (s->num_tokens < 0 || s->hidden <= 0 || s->intermediate <= 0 || s->num_experts <= 0) return MOE_ERR_INVALID_ARG;
     if (s->top_k < 1 || s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
     if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
-    if (s->weight_dtype != MOE_F32 && s->weight_dtype != MOE_BF16 && s->weight_dtype != MOE_MXFP4)
+    if (s->weight_dtype != MOE_F32 && s->weight_dtype != MOE_BF16 && s->weight_dtype != MOE_MXFP4 &&
+        s->weight_dtype != MOE_NVFP4)
         return MOE_ERR_INVALID_ARG;
     if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_GROUPED) return MOE_ERR_INVALID_ARG;
     const int epc = weight_epc(s->weight_dtype);
@@ -51,7 +53,16 @@ moe_status check_ws(const moe_shape *s, const void *ws, size_t ws_bytes) {
 moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
     if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down)) return MOE_ERR_INVALID_ARG;
-    if (s->weight_dtype == MOE_MXFP4 && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    const bool scaled = s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4;
+    if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    if (s->weight_dtype == MOE_NVFP4) {
+        // 2-byte scale pairs are read per 16-byte chunk of codes
+        if ((reinterpret_cast<uintptr_t>(w->s_gate) | reinterpret_cast<uintptr_t>(w->s_up) |
+             reinterpret_cast<uintptr_t>(w->s_down)) & 1u)
+            return MOE_ERR_INVALID_ARG;
+        if (!std::isfinite(w->ts_gate) || !std::isfinite(w->ts_up) || !std::isfinite(w->ts_down))
+            return MOE_ERR_INVALID_ARG;
+    }
     return MOE_OK;
 }
 
@@ -62,11 +73,6 @@ moe_status check_path(const moe_shape *s) {
     return MOE_OK;
 }
 
-// kernel family for the expert FFN: AUTO takes the grouped MFMA GEMMs once the pairs
-// exceed three per expert on average (measured crossover on the H=2048, E=128, k=8
-// bf16 layer: the streaming GEMV family is faster up to 48 tokens, the GEMMs from 64
-// tokens on; on the H=4096, E=256 MXFP4 layer the two meet near 128 tokens); up to 8
-// tokens the fused single-launch kernel runs
 // The grouped family's routing: the one-kernel router (router GEMM, top-k and block counts)
 // whenever the shape allows it.  Measured on the 8192-token shape's layer, it beats the
 // router GEMV + top-k + grouping kernels at every T from 32 up, even when its one
@@ -79,6 +85,7 @@ bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 // (k = 8, E = 256)
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
+    if (s.weight_dtype == MOE_NVFP4) return false;   // no grouped kernels for NVFP4
     const long per_expert = s.weight_dtype == MOE_MXFP4 ? 4L : 2L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
            (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);

@@ -242,17 +242,59 @@ struct FmtF32 {  // fp32 weights with fp32 activations
     static constexpr int EPC = 4;          // elements per 16-byte weight chunk
     static constexpr int XB = 16;          // activation bytes per chunk
     static constexpr bool SCALED = false;
+    static constexpr int SB = 0;
 };
 struct FmtBF16 {  // bf16 weights with bf16 activations
     static constexpr int EPC = 8;
     static constexpr int XB = 16;
     static constexpr bool SCALED = false;
+    static constexpr int SB = 0;
 };
 struct FmtMX4 {  // MXFP4 weights with bf16 activations
     static constexpr int EPC = 32;
     static constexpr int XB = 64;
     static constexpr bool SCALED = true;
+    static constexpr int SB = 1;           // scale bytes per chunk: one E8M0 per 32 elements
 };
+struct FmtNV4 {  // NVFP4 weights (E2M1 codes, one E4M3 scale per 16 elements) with bf16 activations
+    static constexpr int EPC = 32;
+    static constexpr int XB = 64;
+    static constexpr bool SCALED = true;
+    static constexpr int SB = 2;           // two E4M3 scales per chunk (elements 0-15, 16-31)
+};
+
+// the scale code of chunk idx of a scale row: one byte (MXFP4) or two (NVFP4, low byte
+// for the chunk's first 16 elements)
+template <class F>
+__device__ __forceinline__ uint32_t load_scale(const uint8_t *s, size_t idx) {
+    if constexpr (F::SB == 2) return reinterpret_cast<const uint16_t *>(s)[idx];
+    return s[idx];
+}
+
+// OCP FP8 E4M3 (bias 7, no infinities): normal codes (1 + m/8) * 2^(e-7), exponent field 0
+// m/8 * 2^-6.  The NaN codes (S.1111.111) are not valid block scales.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return __uint_as_float(__float_as_uint(v) | ((b & 0x80u) << 24));
+}
+
+// The same value as a power of two p2 times a factor f with at most 4 significant bits
+// (1 + m/8, or m for exponent field 0, signed).  v_cvt_scalef32_pk_bf16_fp4 applies only
+// the power-of-two part of its scale operand (measured on gfx950: a scale of 1.5 decodes
+// as 1.0), so E4M3 scales are applied as the instruction's p2 and then f.
+__device__ __forceinline__ void e4m3_split(uint32_t b, float &p2, float &f) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    p2 = e ? __uint_as_float((e + 120u) << 23) : 0.001953125f;
+    f = e ? 1.0f + 0.125f * (float)m : (float)m;
+    f = (b & 0x80u) ? -f : f;
+}
+
+// a bf16 pair times f, where each product is exact in bf16 (the repack truncates)
+__device__ __forceinline__ uint32_t bf16x2_mul_exact(uint32_t v, float f) {
+    const float lo = __uint_as_float(v << 16) * f, hi = __uint_as_float(v & 0xffff0000u) * f;
+    return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
 
 // partial dot of one weight chunk with the activation chunk at xp (XB bytes)
 template <class F>
@@ -295,6 +337,19 @@ __device__ __forceinline__ float chunk_dot<FmtMX4>(const uint4 &w, uint32_t scal
     acc = mx4_word_dot(w.z, s, x4[2], acc);
     acc = mx4_word_dot(w.w, s, x4[3], acc);
     return acc;
+}
+
+// NVFP4: each 16-element block is dotted with its codes' E2M1 values (decoded with a unit
+// scale, exact) and the block's E4M3 scale multiplies the block's partial sum
+template <>
+__device__ __forceinline__ float chunk_dot<FmtNV4>(const uint4 &w, uint32_t scale_code, const uint8_t *xp, float acc) {
+    const float s0 = e4m3_to_f32(scale_code & 0xffu), s1 = e4m3_to_f32(scale_code >> 8);
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(xp);
+    float a0 = mx4_word_dot(w.x, 1.0f, x4[0], 0.f);
+    a0 = mx4_word_dot(w.y, 1.0f, x4[1], a0);
+    float a1 = mx4_word_dot(w.z, 1.0f, x4[2], 0.f);
+    a1 = mx4_word_dot(w.w, 1.0f, x4[3], a1);
+    return fmaf(s1, a1, fmaf(s0, a0, acc));
 }
 
 }  // namespace moe

@@ -53,7 +53,7 @@ class Shape:
     K: int
     I: int
     act: str          # "f32" | "bf16"
-    w: str            # "f32" | "bf16" | "mxfp4"
+    w: str            # "f32" | "bf16" | "mxfp4" | "nvfp4"
     bias: str = "none"  # "none" | "normal" | "zipf"
     renorm: bool = True
 
@@ -68,6 +68,9 @@ CONFIGS: Dict[str, Shape] = {
     "c4_mxfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "mxfp4"),
     "c4_mxfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "mxfp4"),
     "c4_mxfp4_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "mxfp4"),
+    # the MXFP4 decode shapes with NVFP4 experts (E4M3 scales per 16 elements)
+    "c5_nvfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "nvfp4"),
+    "c5_nvfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "nvfp4"),
 }
 
 
@@ -147,6 +150,56 @@ def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     return val * np.repeat(X, 32, axis=1)
 
 
+# NVFP4 (E2M1 codes, one E4M3 scale per 16 elements, one fp32 scale per tensor).
+# Positive finite E4M3 values by code 0x00..0x7E (0x7F is NaN): exponent field 0 is
+# m/8 * 2^-6, otherwise (1 + m/8) * 2^(e-7).  Ascending in the code.
+_E4M3_POS = np.array([(c & 7) / 8.0 * 2.0 ** -6 if (c >> 3) == 0 else (1.0 + (c & 7) / 8.0) * 2.0 ** ((c >> 3) - 7)
+                      for c in range(0x7F)], np.float64)
+
+
+def nvfp4_tensor_scale(sigma: float) -> float:
+    """The tensor scale the generator uses for N(0, sigma) weights: the block scales of
+    blocks up to 6.5 sigma then stay within E4M3's 448."""
+    return float(np.float32(sigma * 6.5 / (6.0 * 448.0)))
+
+
+def nvfp4_quantize(w: np.ndarray, ts: float):
+    """Quantise fp32 rows [R, C] (C % 16 == 0) to NVFP4 along C with tensor scale ts.
+
+    Block scale: the E4M3 value nearest to amax / 6 / ts (at most 448); codes: nearest
+    E2M1 value of w / (scale * ts), ties to even, saturating at 6.  An all-zero block
+    gets scale code 0 and zero codes.  Returns (codes [R, C/2] uint8, even element in the
+    low nibble; scales [R, C/16] uint8)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, C = w.shape
+    assert C % 16 == 0
+    blk = w.reshape(R, C // 16, 16)
+    amax = np.abs(blk).max(axis=2).astype(np.float64)
+    target = np.minimum(amax / 6.0 / ts, _E4M3_POS[-1])
+    hi = np.clip(np.searchsorted(_E4M3_POS, target), 1, len(_E4M3_POS) - 1)
+    lo = hi - 1
+    pick_hi = (_E4M3_POS[hi] - target) < (target - _E4M3_POS[lo])
+    scode = np.where(pick_hi, hi, lo)
+    scode = np.where(amax > 0, np.maximum(scode, 1), 0).astype(np.uint8)
+    S = (_E4M3_POS[scode] * ts)[..., None]
+    mag = np.where(S > 0, np.abs(blk) / np.where(S > 0, S, 1.0), 0.0).astype(np.float32)
+    code = _e2m1_code_rne(mag) | np.where(blk < 0, np.uint8(8), np.uint8(0))
+    code = np.where((amax > 0)[..., None], code, np.uint8(0)).reshape(R, C)
+    packed = (code[:, 0::2] & 15) | ((code[:, 1::2] & 15) << 4)
+    return packed.astype(np.uint8), scode
+
+
+def nvfp4_dequantize(codes: np.ndarray, scales: np.ndarray, ts: float) -> np.ndarray:
+    """Inverse storage map used by tests on the quantiser: fp64 [R, C]."""
+    R = codes.shape[0]
+    c = np.empty((R, codes.shape[1] * 2), np.uint8)
+    c[:, 0::2] = codes & 15
+    c[:, 1::2] = codes >> 4
+    mag = _E2M1_GRID[c & 7]
+    val = np.where(c & 8, -mag, mag)
+    return val * np.repeat(_E4M3_POS[scales] * ts, 16, axis=1)
+
+
 # ---- tensors of one layer ------------------------------------------------------
 
 @dataclass
@@ -162,6 +215,7 @@ class LayerInputs:
     su: Optional[np.ndarray] = None
     sd: Optional[np.ndarray] = None
     meta: dict = field(default_factory=dict)
+    ts: tuple = (1.0, 1.0, 1.0)      # NVFP4 tensor scales of gate, up, down
 
 
 def _store(a64: np.ndarray, fmt: str) -> np.ndarray:
@@ -194,9 +248,10 @@ def make_bias(shape: Shape, seed: int = 0, beta: Optional[float] = None) -> Opti
 def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigma: float,
                    threads: int):
     E = shape.E
-    if shape.w == "mxfp4":
+    ts = nvfp4_tensor_scale(sigma)
+    if shape.w in ("mxfp4", "nvfp4"):
         codes = np.empty((E, rows, cols // 2), np.uint8)
-        scales = np.empty((E, rows, cols // 32), np.uint8)
+        scales = np.empty((E, rows, cols // (32 if shape.w == "mxfp4" else 16)), np.uint8)
     else:
         out = np.empty((E, rows, cols), np.float32 if shape.w == "f32" else np.uint16)
 
@@ -204,6 +259,8 @@ def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigm
         a32 = normal(seed, tag, (rows, cols), sigma, sub=e).astype(np.float32)
         if shape.w == "mxfp4":
             codes[e], scales[e] = mxfp4_quantize(a32)
+        elif shape.w == "nvfp4":
+            codes[e], scales[e] = nvfp4_quantize(a32, ts)
         elif shape.w == "bf16":
             out[e] = f32_to_bf16_bits(a32)
         else:
@@ -215,7 +272,7 @@ def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigm
     else:
         for e in range(E):
             one(e)
-    if shape.w == "mxfp4":
+    if shape.w in ("mxfp4", "nvfp4"):
         return codes, scales
     return out, None
 
@@ -238,4 +295,8 @@ def make_layer(name_or_shape, seed: int = 0, batch: int = 0, threads: Optional[i
     wd, sd = _expert_tensor(shape, seed, "wd", H, I, 1.0 / math.sqrt(I), threads)
     meta = dict(seed=seed, batch=batch, zipf_beta=(ZIPF_BETA if beta is None else beta)
                 if shape.bias == "zipf" else None)
-    return LayerInputs(shape, x, wr, bias, wg, wu, wd, sg, su, sd, meta)
+    ts = (1.0, 1.0, 1.0)
+    if shape.w == "nvfp4":
+        ts = (nvfp4_tensor_scale(1.0 / math.sqrt(H)), nvfp4_tensor_scale(1.0 / math.sqrt(H)),
+              nvfp4_tensor_scale(1.0 / math.sqrt(I)))
+    return LayerInputs(shape, x, wr, bias, wg, wu, wd, sg, su, sd, meta, ts)

@@ -15,6 +15,7 @@ from tests.helpers import max_abs, oracle_layer, rel_l2
 
 # tolerances of the layer output against the fp64 oracle
 TOL = {"bf16": dict(rel_l2=1e-2, max_abs=3e-2), "mxfp4": dict(rel_l2=2e-2, max_abs=None),
+       "nvfp4": dict(rel_l2=2e-2, max_abs=None),
        "f32": dict(rel_l2=1e-5, max_abs=1e-4)}
 W_TOL = 1e-6  # gate weights, max-abs (fp32 softmax on fp32 logits)
 
@@ -46,7 +47,7 @@ def act_code(s: synth.Shape) -> int:
 
 
 def w_code(s: synth.Shape) -> int:
-    return {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4}[s.w]
+    return {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4}[s.w]
 
 
 def lshape(li: synth.LayerInputs, path=pm.PATH_AUTO, T=None, K=None, renorm=None) -> pm.LayerShape:
@@ -66,7 +67,7 @@ class DevLayer:
         self.wr = tdev(li.wr)
         self.bias = tdev(li.bias) if li.bias is not None else None
         self.weights = dict(wg=tdev(li.wg), wu=tdev(li.wu), wd=tdev(li.wd), sg=tdev(li.sg), su=tdev(li.su),
-                            sd=tdev(li.sd))
+                            sd=tdev(li.sd), ts=li.ts)
 
     def act_torch(self):
         return torch.float32 if self.li.shape.act == "f32" else torch.int16
@@ -134,7 +135,7 @@ def compare_forward(li: synth.LayerInputs, got: dict, tokens=None, K=None, renor
         wref[mism] = forced["w"]
     werr = max_abs(gw, wref)
     assert werr <= W_TOL, f"{label}: gate weights max-abs {werr:.3e}"
-    fmt = li.shape.w if li.shape.w == "mxfp4" else li.shape.act
+    fmt = li.shape.w if li.shape.w in ("mxfp4", "nvfp4") else li.shape.act
     y = to_f64(got["y"], li.shape.act)[toks]
     r, m = rel_l2(y, yref), max_abs(y, yref)
     tol = TOL[fmt]

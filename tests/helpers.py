@@ -11,7 +11,8 @@ import synth
 def oracle_layer(li: synth.LayerInputs, **kw) -> oracle.Layer:
     return oracle.Layer(x=li.x, wr=li.wr, wg=li.wg, wu=li.wu, wd=li.wd, top_k=kw.get("top_k", li.shape.K),
                         renorm=kw.get("renorm", li.shape.renorm), bias=li.bias,
-                        sg=li.sg, su=li.su, sd=li.sd)
+                        sg=li.sg, su=li.su, sd=li.sd, fmt=li.shape.w if li.shape.w == "nvfp4" else None,
+                        ts=li.ts)
 
 
 def grouping_violations(ids: np.ndarray, E: int, off, srt, pos) -> list:

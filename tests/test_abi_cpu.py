@@ -100,6 +100,30 @@ def test_forward_validation():
                          pm.workspace_size(_shape(num_tokens=0)), None) == pm.OK
 
 
+def test_nvfp4_validation():
+    """NVFP4 experts: scale arrays required and 2-byte aligned, finite tensor scales, no
+    grouped GEMMs (MOE_ERR_UNSUPPORTED before anything launches)."""
+    L = pm.lib()
+    shp = _shape(weight_dtype=pm.NVFP4)
+    s = shp.c()
+    n = pm.workspace_size(shp)
+    def fwd(w, sh=s, nb=n):
+        return L.moe_forward(ctypes.byref(sh), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE, nb, None)
+    assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, None, None, None, 1.0, 1.0, 1.0)) == pm.ERR_INVALID_ARG
+    assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, 1.0, 1.0, 1.0)) == pm.ERR_INVALID_ARG
+    assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, float("inf"), 1.0)) == pm.ERR_INVALID_ARG
+    assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), 1.0, 1.0)) == pm.ERR_INVALID_ARG
+    shg = _shape(weight_dtype=pm.NVFP4, path=pm.PATH_GROUPED)
+    good = pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 1.0)
+    assert fwd(good, shg.c(), pm.workspace_size(shg)) == pm.ERR_UNSUPPORTED
+    # AUTO never takes the grouped family for NVFP4, at any T
+    for T in (9, 64, 4096):
+        stages = pm.forward_stages(_shape(weight_dtype=pm.NVFP4, num_tokens=T))
+        assert "gate_up" in stages and "router_topk" not in stages and "router_logits" in stages, (T, stages)
+    # with fp32 activations NVFP4 is not a supported pair
+    assert pm.workspace_size(_shape(weight_dtype=pm.NVFP4, act_dtype=pm.F32)) == 0
+
+
 def test_status_strings():
     for st in (pm.OK, pm.ERR_INVALID_ARG, pm.ERR_UNSUPPORTED, pm.ERR_WORKSPACE, pm.ERR_HIP, pm.ERR_DEVICE):
         assert pm.status_string(st) and pm.status_string(st) != "unknown status"

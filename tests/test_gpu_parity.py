@@ -326,6 +326,33 @@ def test_forward_parity_mxfp4_small_ragged():
     compare_forward(li, got, label="mxfp4 small")
 
 
+@pytest.mark.parametrize("name", ["c5_nvfp4_decode1", "c5_nvfp4_decode8"])
+def test_forward_parity_nvfp4_decode(name):
+    """NVFP4 experts (E4M3 scale per 16 elements, fp32 tensor scale) on the fused decode
+    launch: ids exact away from near-ties, y against the oracle."""
+    note(f"forward parity {name}")
+    li = layer(name)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=name)
+
+
+@pytest.mark.parametrize("T", [20, 64, 130])
+def test_forward_nvfp4_streaming(T):
+    """NVFP4 above 8 tokens runs on the streaming family at every T (no grouped kernels)."""
+    note(f"nvfp4 streaming T={T}")
+    li = layer_of(synth.Shape(T, 4096, 256, 8, 1024, "bf16", "nvfp4"), batch=90 + T)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, tokens=_sample(T, 12), label=f"nvfp4 T={T}")
+
+
+@pytest.mark.parametrize("T,H,E,K,I", [(3, 1024, 64, 4, 512), (12, 512, 32, 4, 256)])
+def test_forward_nvfp4_small_shapes(T, H, E, K, I):
+    """Other NVFP4 shapes: fused (T=3) and streaming (T=12, ragged rows per lane), bias."""
+    li = layer_of(synth.Shape(T, H, E, K, I, "bf16", "nvfp4", bias="normal"), seed=3)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=f"nvfp4 T={T} H={H} E={E}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13])
 def test_forward_token_sweep(T):
     note(f"token sweep T={T}")

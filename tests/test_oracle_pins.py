@@ -395,3 +395,82 @@ def test_forward_mxfp4_equals_dequantised_fp32():
     a, b = oracle.forward(L), oracle.forward(L32)
     np.testing.assert_array_equal(a["ids"], b["ids"])
     np.testing.assert_array_equal(a["y"], b["y"])
+
+
+# ---- NVFP4 (E2M1 codes, E4M3 block scales per 16 elements, fp32 tensor scale) ----------
+
+def test_e4m3_decode_matches_torch_exhaustive():
+    """All 256 E4M3 codes against torch's float8_e4m3fn (OCP FP8 E4M3), an independent
+    decoder; S.1111.111 is NaN in both."""
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    for code in range(256):
+        got = oracle.decode_e4m3(code)
+        if math.isnan(ref[code]):
+            assert math.isnan(got), code
+        else:
+            assert got == ref[code], (code, got, ref[code])
+
+
+def _nv_pack(codes: np.ndarray) -> np.ndarray:
+    """[R, C] codes 0..15 -> [R, C/2] bytes, the even element in the low nibble."""
+    return ((codes[:, 0::2] & 15) | ((codes[:, 1::2] & 15) << 4)).astype(np.uint8)
+
+
+def test_nvfp4_hand_case():
+    """One nonzero element per matrix, worked by hand from the format definition:
+    gate 3.0 (E2M1 0x5) x 2.0 (E4M3 0x40) x tensor scale 0.25 = 1.5; up 1.5 (0x3) x 1.0
+    (0x38) x 2.0 = 3.0; down -1.0 (0xA) x 4.0 (0x48) x 0.5 = -2.0, so with x = e_3 the
+    expert output is o[7] = -2 * silu(1.5) * 3.0 and zero elsewhere."""
+    H = I = 16
+    x = np.zeros((1, H), np.uint16)
+    x[0, 3] = 0x3F80                                   # bf16 1.0
+    cg = np.zeros((I, H), np.int64); cg[2, 3] = 0x5
+    cu = np.zeros((I, H), np.int64); cu[2, 3] = 0x3
+    cd = np.zeros((H, I), np.int64); cd[7, 2] = 0xA
+    sg = np.zeros((1, I, H // 16), np.uint8); sg[0, 2, 0] = 0x40
+    su = np.zeros((1, I, H // 16), np.uint8); su[0, 2, 0] = 0x38
+    sd = np.zeros((1, H, I // 16), np.uint8); sd[0, 7, 0] = 0x48
+    L = oracle.Layer(x=x, wr=np.zeros((1, H), np.uint16), wg=_nv_pack(cg)[None], wu=_nv_pack(cu)[None],
+                     wd=_nv_pack(cd)[None], top_k=1, sg=sg, su=su, sd=sd, fmt="nvfp4", ts=(0.25, 2.0, 0.5))
+    o = oracle.expert_pairs(L, [0], [0])[0]
+    want = np.zeros(H)
+    want[7] = -2.0 * (1.5 / (1.0 + math.exp(-1.5))) * 3.0
+    np.testing.assert_allclose(o, want, rtol=1e-15, atol=0)
+
+
+def test_forward_nvfp4_matches_numpy_on_dequantised_weights():
+    """The oracle's expert outputs on NVFP4 storage equal fp64 numpy matrix products on the
+    weights dequantised by the generator's own (independent) inverse map."""
+    li = synth.make_layer(synth.Shape(3, 64, 4, 2, 32, "bf16", "nvfp4"))
+    L = oracle_layer(li)
+    E, T = li.shape.E, li.shape.T
+    deq = {}
+    for name, sname, ts in (("wg", "sg", li.ts[0]), ("wu", "su", li.ts[1]), ("wd", "sd", li.ts[2])):
+        c, s = getattr(li, name), getattr(li, sname)
+        deq[name] = np.stack([synth.nvfp4_dequantize(c[e], s[e], ts) for e in range(E)])
+    x = synth.bf16_bits_to_f32(li.x).astype(np.float64)
+    tok = [t for t in range(T) for e in range(E)]
+    exp_ = [e for t in range(T) for e in range(E)]
+    got = oracle.expert_pairs(L, tok, exp_)
+    for p, (t, e) in enumerate(zip(tok, exp_)):
+        g = deq["wg"][e] @ x[t]
+        u = deq["wu"][e] @ x[t]
+        want = deq["wd"][e] @ (g / (1.0 + np.exp(-g)) * u)
+        np.testing.assert_allclose(got[p], want, rtol=1e-11, atol=1e-14)
+
+
+def test_nvfp4_quantiser_round_trip():
+    """The generator's NVFP4 quantiser: block scales are finite E4M3 codes, the stored
+    values are within half an E2M1 step (of the block's scale) of the inputs below the
+    saturation point, and all-zero blocks stay zero."""
+    rng = np.random.default_rng(5)
+    w = (rng.standard_normal((8, 64)) * 0.05).astype(np.float32)
+    w[3, 16:32] = 0.0
+    ts = synth.nvfp4_tensor_scale(0.05)
+    codes, scales = synth.nvfp4_quantize(w, ts)
+    assert scales.dtype == np.uint8 and np.all((scales & 0x7F) != 0x7F)
+    assert scales[3, 1] == 0 and np.all(codes[3, 8:16] == 0)
+    d = synth.nvfp4_dequantize(codes, scales, ts)
+    blk_scale = np.repeat(np.array([[oracle.decode_e4m3(int(c)) for c in row] for row in scales]) * ts, 16, axis=1)
+    ok = np.abs(w) <= 6.0 * blk_scale
+    assert np.all(np.abs(d - w)[ok] <= 1.0 * blk_scale[ok] + 1e-12)
