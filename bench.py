@@ -81,6 +81,8 @@ WORKLOADS = {
     "nvfp4_decode1": ("c5_nvfp4_decode1", "decode, 1 token, NVFP4 experts (E4M3 scale per 16), bf16 acts: "
                       "H=4096, E=256, top-8, I=1024"),
     "nvfp4_decode8": ("c5_nvfp4_decode8", "decode, 8 tokens, NVFP4 experts: H=4096, E=256, top-8, I=1024"),
+    "nvfp4_prefill4096": ("c5_nvfp4_prefill4096",
+                          "prefill chunk, 4096 tokens, NVFP4 experts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_prefill4096": ("c4_mxfp4_prefill4096",
                           "prefill chunk, 4096 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
     "tiny": ("c0_tiny_f32", "tiny fp32: 4 tokens, H=256, E=8, top-2, I=128"),

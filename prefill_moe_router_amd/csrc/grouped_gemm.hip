@@ -38,7 +38,8 @@ struct GemmParams {
     const int32_t *offsets;    // expert offsets [E+1]
     const int32_t *mtile_off;  // m-tile offsets [E+1] (tiles of BM rows per expert)
     const uint8_t *b0, *b1;    // weights [E][N][K] bf16, or MXFP4 codes [E][N][K/2] (b1: up, GATEUP only)
-    const uint8_t *s0, *s1;    // MXFP4 E8M0 scales [E][N][K/32]
+    const uint8_t *s0, *s1;    // MXFP4 E8M0 scales [E][N][K/32] or NVFP4 E4M3 scales [E][N][K/16]
+    float ts0, ts1;            // NVFP4 tensor scales of b0 / b1
     const float *wts;          // gate weight per slot (GATEUP)
     const float *bias;         // router bias [N] or null
     uint8_t *out;
@@ -59,7 +60,7 @@ __device__ __forceinline__ int find_expert(const int32_t *mtile_off, int E, int 
 // BM x BN output tile per matrix (NB = 2 matrices, gate and up, for GATEUP), K steps
 // of BK, WM x WN waves, each wave MI x NJ blocks of 32x32 per matrix.  LDS rows are
 // padded by 16 bytes so 16 consecutive rows read at one k offset hit distinct banks.
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX, bool NV = false>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p) {
     constexpr int NTH = WM * WN * 64;
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
@@ -140,7 +141,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         const int b = r / BN, rr = r % BN;
         const size_t grow = (size_t)e * p.N + n0 + rr;
         bqrow[i] = MX ? (b == 0 ? p.b0 : p.b1) + grow * (size_t)(p.K / 2) + c * 16 : nullptr;
-        bqsc[i] = MX ? (b == 0 ? p.s0 : p.s1) + grow * (size_t)(p.K / 32) + c : nullptr;
+        bqsc[i] = MX ? (b == 0 ? p.s0 : p.s1) + grow * (size_t)(p.K / (NV ? 16 : 32)) + c * (NV ? 2 : 1) : nullptr;
         bqlds[i] = (BM + r) * GROW + c * 64;
     }
 
@@ -156,7 +157,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         if constexpr (MX) {                                                                               \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
                 RQ[i] = *reinterpret_cast<const u32x4_t *>(bqrow[i] + (size_t)(kt) * (BK / 2));           \
-                RS[i] = bqsc[i][(kt) * CQ];                                                               \
+                RS[i] = NV ? (uint32_t) * reinterpret_cast<const uint16_t *>(bqsc[i] + (kt) * CQ * 2)      \
+                           : (uint32_t)bqsc[i][(kt) * CQ];                                                 \
             }                                                                                             \
         } else {                                                                                          \
             _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
@@ -169,7 +171,25 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         uint8_t *base_ = lds + (stage) * STAGE;                                                           \
         _Pragma("unroll") for (int i = 0; i < AR; ++i)                                                    \
             *reinterpret_cast<u32x4_t *>(base_ + (sr + RPP * i) * GROW + sc * 16) = RA[i];                \
-        if constexpr (MX) {                                                                               \
+        if constexpr (MX && NV) {                                                                         \
+            /* NVFP4: the power of two of each block's E4M3 scale in the convert, then the */              \
+            /* remaining factor (exact in bf16) */                                                          \
+            _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
+                float p2_[2], f_[2];                                                                      \
+                e4m3_split(RS[i] & 0xffu, p2_[0], f_[0]);                                                 \
+                e4m3_split(RS[i] >> 8, p2_[1], f_[1]);                                                    \
+                _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                           \
+                    const uint32_t cw = RQ[i][w];                                                         \
+                    const float s_ = p2_[w >> 1], f2_ = f_[w >> 1];                                       \
+                    u32x4_t o_;                                                                           \
+                    o_[0] = bf16x2_mul_exact(fp4x2_to_bf16x2<0>(cw, s_), f2_);                            \
+                    o_[1] = bf16x2_mul_exact(fp4x2_to_bf16x2<1>(cw, s_), f2_);                            \
+                    o_[2] = bf16x2_mul_exact(fp4x2_to_bf16x2<2>(cw, s_), f2_);                            \
+                    o_[3] = bf16x2_mul_exact(fp4x2_to_bf16x2<3>(cw, s_), f2_);                            \
+                    *reinterpret_cast<u32x4_t *>(base_ + bqlds[i] + w * 16) = o_;                         \
+                }                                                                                         \
+            }                                                                                             \
+        } else if constexpr (MX) {                                                                        \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
                 const float s_ = e8m0_to_f32(RS[i]);                                                      \
                 _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                           \
@@ -272,8 +292,13 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
                     float v;
-                    if (MODE == GM_GATEUP) v = s_scale[wm + ml] * swiglu(acc[0][i][j][r], acc[NB - 1][i][j][r]);
-                    else v = acc[0][i][j][r];
+                    float g_ = acc[0][i][j][r], u_ = acc[NB - 1][i][j][r];
+                    if constexpr (NV) {
+                        g_ *= p.ts0;
+                        u_ *= p.ts1;
+                    }
+                    if (MODE == GM_GATEUP) v = s_scale[wm + ml] * swiglu(g_, u_);
+                    else v = g_;
                     ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(v);
                 }
             }
@@ -303,7 +328,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
                     const float b = p.bias ? p.bias[n] : 0.f;
                     reinterpret_cast<float *>(p.out)[(size_t)(m0 + m) * p.N + n] = acc[0][i][j][r] + b;
                 } else {
-                    reinterpret_cast<float *>(p.out)[(size_t)(m0 + m) * p.N + n] = acc[0][i][j][r];
+                    reinterpret_cast<float *>(p.out)[(size_t)(m0 + m) * p.N + n] =
+                        NV ? acc[0][i][j][r] * p.ts0 : acc[0][i][j][r];
                 }
             }
         }
@@ -375,7 +401,8 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
 }
 
 bool grouped_supported(const moe_shape &s) {
-    return s.act_dtype == MOE_BF16 && (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4) &&
+    return s.act_dtype == MOE_BF16 &&
+           (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4 || s.weight_dtype == MOE_NVFP4) &&
            s.hidden % CfgDN::BN == 0 && s.hidden % CfgGU::BK == 0 && s.intermediate % CfgGU::BN == 0 &&
            s.intermediate % CfgDN::BK == 0;
 }
@@ -384,7 +411,7 @@ bool router_mfma_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 && s.num_experts % CfgR::BN == 0 && s.hidden % CfgR::BK == 0;
 }
 
-template <int MODE, class C, bool MX = false>
+template <int MODE, class C, bool MX = false, bool NV = false>
 static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
     constexpr size_t stage_bytes = C::NS * (size_t)(C::BM + NB * C::BN) * (C::BK * 2 + 16);
@@ -392,7 +419,7 @@ static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
     static_assert(lds <= 158 * 1024, "LDS budget");
     static bool attr_done = false;
-    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX>;
+    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX, NV>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -451,6 +478,8 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.b1 = static_cast<const uint8_t *>(w.w_up);
     prm.s0 = w.s_gate;
     prm.s1 = w.s_up;
+    prm.ts0 = w.ts_gate;
+    prm.ts1 = w.ts_up;
     prm.wts = wts;
     prm.out = static_cast<uint8_t *>(h);
     prm.M = s.num_tokens * s.top_k;
@@ -461,6 +490,7 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.mt_max = mt_max_of(s);
     prm.nt = s.intermediate / CfgGU::BN;
     if (s.weight_dtype == MOE_MXFP4) return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_NVFP4) return gemm_launch<GM_GATEUP, CfgGU, true, true>(prm, st, ev0, ev1);
     return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
 }
 
@@ -475,6 +505,7 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
     prm.mtile_off = mtile_off;
     prm.b0 = static_cast<const uint8_t *>(w.w_down);
     prm.s0 = w.s_down;
+    prm.ts0 = w.ts_down;
     prm.out = static_cast<uint8_t *>(o);
     prm.M = s.num_tokens * s.top_k;
     prm.N = s.hidden;
@@ -483,9 +514,11 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
     prm.E = s.num_experts;
     prm.mt_max = mt_max_of(s);
     prm.nt = s.hidden / CfgDN::BN;
-    const bool mx = s.weight_dtype == MOE_MXFP4;
-    if (f32_sorted) return mx ? gemm_launch<GM_DOWN_F32, CfgDN, true>(prm, st, ev0, ev1)
+    const bool mx = s.weight_dtype == MOE_MXFP4, nv = s.weight_dtype == MOE_NVFP4;
+    if (f32_sorted) return nv ? gemm_launch<GM_DOWN_F32, CfgDN, true, true>(prm, st, ev0, ev1)
+                         : mx ? gemm_launch<GM_DOWN_F32, CfgDN, true>(prm, st, ev0, ev1)
                               : gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
+    if (nv) return gemm_launch<GM_DOWN, CfgDN, true, true>(prm, st, ev0, ev1);
     return mx ? gemm_launch<GM_DOWN, CfgDN, true>(prm, st, ev0, ev1) : gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
 }
 

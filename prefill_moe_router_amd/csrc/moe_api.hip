@@ -80,13 +80,12 @@ moe_status check_path(const moe_shape *s) {
 bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 
 // AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
-// experts, four with MXFP4 (whose streaming kernels read a quarter of the bytes); measured
+// experts, four with MXFP4 / NVFP4 (whose streaming kernels read a quarter of the bytes); measured
 // crossovers on the decode shapes: bf16 T = 24..32 (k = 8, E = 128), MXFP4 above T = 64
 // (k = 8, E = 256)
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    if (s.weight_dtype == MOE_NVFP4) return false;   // no grouped kernels for NVFP4
-    const long per_expert = s.weight_dtype == MOE_MXFP4 ? 4L : 2L;
+    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : 4L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
            (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
 }

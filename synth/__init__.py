@@ -71,6 +71,7 @@ CONFIGS: Dict[str, Shape] = {
     # the MXFP4 decode shapes with NVFP4 experts (E4M3 scales per 16 elements)
     "c5_nvfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "nvfp4"),
     "c5_nvfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "nvfp4"),
+    "c5_nvfp4_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "nvfp4"),
 }
 
 

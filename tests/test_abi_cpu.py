@@ -101,8 +101,8 @@ def test_forward_validation():
 
 
 def test_nvfp4_validation():
-    """NVFP4 experts: scale arrays required and 2-byte aligned, finite tensor scales, no
-    grouped GEMMs (MOE_ERR_UNSUPPORTED before anything launches)."""
+    """NVFP4 experts: scale arrays required and 2-byte aligned, finite tensor scales; AUTO
+    takes the grouped GEMMs from four pairs per expert as for MXFP4."""
     L = pm.lib()
     shp = _shape(weight_dtype=pm.NVFP4)
     s = shp.c()
@@ -113,13 +113,10 @@ def test_nvfp4_validation():
     assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE + 1, FAKE, 1.0, 1.0, 1.0)) == pm.ERR_INVALID_ARG
     assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, float("inf"), 1.0)) == pm.ERR_INVALID_ARG
     assert fwd(pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, float("nan"), 1.0, 1.0)) == pm.ERR_INVALID_ARG
-    shg = _shape(weight_dtype=pm.NVFP4, path=pm.PATH_GROUPED)
-    good = pm.ExpertWeights(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1.0, 1.0, 1.0)
-    assert fwd(good, shg.c(), pm.workspace_size(shg)) == pm.ERR_UNSUPPORTED
-    # AUTO never takes the grouped family for NVFP4, at any T
-    for T in (9, 64, 4096):
+    # E = 128, k = 8: streaming below 64 tokens, grouped from 64
+    for T, grouped in ((9, False), (63, False), (64, True), (4096, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.NVFP4, num_tokens=T))
-        assert "gate_up" in stages and "router_topk" not in stages and "router_logits" in stages, (T, stages)
+        assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     # with fp32 activations NVFP4 is not a supported pair
     assert pm.workspace_size(_shape(weight_dtype=pm.NVFP4, act_dtype=pm.F32)) == 0
 

@@ -345,6 +345,20 @@ def test_forward_nvfp4_streaming(T):
     compare_forward(li, got, tokens=_sample(T, 12), label=f"nvfp4 T={T}")
 
 
+@pytest.mark.parametrize("T,H,E,K,I,path", [(130, 1024, 32, 4, 256, pm.PATH_GROUPED),
+                                            (512, 4096, 256, 8, 1024, pm.PATH_AUTO)])
+def test_forward_nvfp4_grouped(T, H, E, K, I, path):
+    """NVFP4 on the grouped MFMA GEMMs (codes dequantised into LDS with the split E4M3
+    scale, tensor scales in the epilogues): ragged m-tiles, and AUTO's choice at 512 tokens."""
+    note(f"nvfp4 grouped T={T} H={H} E={E}")
+    li = layer_of(synth.Shape(T, H, E, K, I, "bf16", "nvfp4", bias="normal"), seed=7)
+    sh = lshape(li, path)
+    assert "router_topk" in pm.forward_stages(sh) or "router_logits" in pm.forward_stages(sh)
+    assert "gate_up" in pm.forward_stages(sh)
+    got = run_forward(DevLayer(li), path=path)
+    compare_forward(li, got, tokens=_sample(T, 16), label=f"nvfp4 grouped T={T}")
+
+
 @pytest.mark.parametrize("T,H,E,K,I", [(3, 1024, 64, 4, 512), (12, 512, 32, 4, 256)])
 def test_forward_nvfp4_small_shapes(T, H, E, K, I):
     """Other NVFP4 shapes: fused (T=3) and streaming (T=12, ragged rows per lane), bias."""
