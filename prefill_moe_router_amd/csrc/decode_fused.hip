@@ -297,39 +297,85 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         else wave_topk<16>(lg, E, K, p.renorm, ii, ww, ig, wg);
     }
     __syncthreads();
-    const int P4 = (P + 3) >> 2;
-    int my_e = 0, my_less = 0, my_cnt = 0;
-    if (tid < P) {
-        my_e = s_ids[tid];
-        int before = 0;
-        const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
-#pragma unroll 4
-        for (int q4 = 0; q4 < P4; ++q4) {
-            const int4 v = ids4[q4];
-            const int q = q4 * 4;
-            my_less += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
-            my_cnt += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
-            before += (v.x == my_e && q < tid) + (v.y == my_e && q + 1 < tid) + (v.z == my_e && q + 2 < tid) +
-                      (v.w == my_e && q + 3 < tid);
+    if (P <= WAVE) {
+        // One wave holds every slot (lane = slot).  Ballots over the expert-id bits give
+        // each slot the lanes with its id (count, and its rank among them in slot order)
+        // and, from the top bit down, the number of slots and of first slots with a
+        // smaller id: the position of the slot and of its expert in the sorted order.
+        if (wave == 0) {
+            const bool valid = lane < P;
+            const int my_e = valid ? s_ids[lane] : 0;
+            int nbits = 1;
+            while ((1 << nbits) < E) ++nbits;
+            const uint64_t all = __ballot(valid);
+            uint64_t match = all;
+            for (int b = 0; b < nbits; ++b) {
+                const uint64_t B = __ballot(valid && ((my_e >> b) & 1));
+                match &= ((my_e >> b) & 1) ? B : ~B;
+            }
+            const uint64_t lt = lanemask_lt();
+            const int my_cnt = __popcll(match), before = __popcll(match & lt);
+            const uint64_t firsts = __ballot(valid && before == 0);
+            uint64_t eqa = all, eqf = firsts;
+            int my_less = 0, dl = 0;
+            for (int b = nbits - 1; b >= 0; --b) {
+                const uint64_t B = __ballot(valid && ((my_e >> b) & 1));
+                if ((my_e >> b) & 1) {
+                    my_less += __popcll(eqa & ~B);
+                    dl += __popcll(eqf & ~B);
+                    eqa &= B;
+                    eqf &= B;
+                } else {
+                    eqa &= ~B;
+                    eqf &= ~B;
+                }
+            }
+            if (valid) {
+                s_tok[my_less + before] = lane / K;
+                s_wq[my_less + before] = s_w[lane];
+                if (before == 0) {
+                    s_act_e[dl] = my_e;
+                    s_act_start[dl] = my_less;
+                    s_act_cnt[dl] = my_cnt;
+                }
+            }
+            if (lane == 0) s_nact = __popcll(firsts);
         }
-        s_tok[my_less + before] = tid / K;
-        s_wq[my_less + before] = s_w[tid];
-        s_first[tid] = before == 0 ? my_e : 0x7fffffff;   // first slot of its expert carries the id
-        const uint64_t firsts = __ballot(before == 0);      // distinct experts: one first slot each
-        if (lane == 0) atomicAdd(&s_nact, (int)__popcll(firsts));
-    }
-    __syncthreads();
-    if (tid < P && s_first[tid] == my_e) {
-        int dl = 0;
-        const int4 *f4 = reinterpret_cast<const int4 *>(s_first);
-#pragma unroll 4
-        for (int q4 = 0; q4 < P4; ++q4) {
-            const int4 v = f4[q4];
-            dl += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
+    } else {
+        const int P4 = (P + 3) >> 2;
+        int my_e = 0, my_less = 0, my_cnt = 0;
+        if (tid < P) {
+            my_e = s_ids[tid];
+            int before = 0;
+            const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
+    #pragma unroll 4
+            for (int q4 = 0; q4 < P4; ++q4) {
+                const int4 v = ids4[q4];
+                const int q = q4 * 4;
+                my_less += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
+                my_cnt += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
+                before += (v.x == my_e && q < tid) + (v.y == my_e && q + 1 < tid) + (v.z == my_e && q + 2 < tid) +
+                          (v.w == my_e && q + 3 < tid);
+            }
+            s_tok[my_less + before] = tid / K;
+            s_wq[my_less + before] = s_w[tid];
+            s_first[tid] = before == 0 ? my_e : 0x7fffffff;   // first slot of its expert carries the id
+            const uint64_t firsts = __ballot(before == 0);      // distinct experts: one first slot each
+            if (lane == 0) atomicAdd(&s_nact, (int)__popcll(firsts));
         }
-        s_act_e[dl] = my_e;
-        s_act_start[dl] = my_less;
-        s_act_cnt[dl] = my_cnt;
+        __syncthreads();
+        if (tid < P && s_first[tid] == my_e) {
+            int dl = 0;
+            const int4 *f4 = reinterpret_cast<const int4 *>(s_first);
+    #pragma unroll 4
+            for (int q4 = 0; q4 < P4; ++q4) {
+                const int4 v = f4[q4];
+                dl += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
+            }
+            s_act_e[dl] = my_e;
+            s_act_start[dl] = my_less;
+            s_act_cnt[dl] = my_cnt;
+        }
     }
     __syncthreads();
     const int U = s_nact;
