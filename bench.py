@@ -45,15 +45,15 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 # of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
 # the counters were taken on (sha1 of the listed files); otherwise traffic is null.
 COUNTED_TRAFFIC = {
-    "decode1": dict(kernel="decode_fused", fetch_kib=37445.1, write_kib=240.1, fetch_scale=2.0,
+    "decode1": dict(kernel="decode_fused", fetch_kib=37450.7, write_kib=240.1, fetch_scale=2.0,
                     write_scale=1.0, sources={
-                        "prefill_moe_router_amd/csrc/decode_fused.hip": "ff4313ed56b1814780b56857a8195d480671c1f9",
-                        "prefill_moe_router_amd/csrc/moe_device.h": "a4852e5f53b011ba193dff363104b6bb85c87294"}),
-    "prefill8192": dict(kernel="gate_up", fetch_kib=1114649.9, write_kib=98304.0, fetch_scale=2.0,
+                        "prefill_moe_router_amd/csrc/decode_fused.hip": "2eca5cb8dc38ff70a79a81ab942a99ce7feffdad",
+                        "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
+    "prefill8192": dict(kernel="gate_up", fetch_kib=1106509.3, write_kib=98304.0, fetch_scale=2.0,
                         write_scale=1.0, sources={
                             "prefill_moe_router_amd/csrc/grouped_gemm_wide.hip":
                                 "bf504b2bc762a837932ab82aca74f71b044e8a9a",
-                            "prefill_moe_router_amd/csrc/moe_device.h": "a4852e5f53b011ba193dff363104b6bb85c87294"}),
+                            "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
 }
 
 
