@@ -6,26 +6,29 @@
 //   DOWN   : o'[slot][n] = h'[p] . Wd[e][n]             (bf16, rows scattered to slot order)
 //
 // Design for gfx950:
-//  * A work-group of 4 waves owns a 128-row m-tile of one expert and 256 weight rows
-//    (GATEUP: 128 intermediate columns of both gate and up; DOWN: 256 output
-//    columns).  The waves form a 2 x 2 grid; each owns 64 rows x 128 weight rows,
-//    i.e. 8 independent 32x32 MFMA accumulators (128 registers), so one 16-deep K
-//    slice moves 6 KB of operands out of LDS per 8 MFMAs.  72 KB of LDS and <= 256
-//    registers per lane let two work-groups share a CU, so one group's tile start
-//    (metadata loads, pipeline fill) and epilogue hide under the other's MFMAs.
+//  * A work-group owns a 128-row m-tile of one expert and 256 weight rows (GATEUP: 128
+//    intermediate columns of both gate and up; DOWN: 256 output columns).  DOWN: 2 x 2
+//    waves of 64 rows x 128 weight rows, i.e. 8 independent 32x32 MFMA accumulators
+//    (128 registers), so one 16-deep K slice moves 6 KB of operands out of LDS per 8
+//    MFMAs; 72 KB of LDS and <= 256 registers per lane let two work-groups share a
+//    CU, so one group's tile start (metadata loads, pipeline fill) and epilogue hide
+//    under the other's MFMAs.  GATEUP: 4 x 2 waves of 32 x 128 in one work-group per
+//    CU, with 64-deep stages (below).
 //  * Each m-tile's rows come from a tile table the grouping writes ({first row, end
 //    row, expert} per tile): one load, no search over the m-tile offsets.
 //  * Operands go from global memory straight into LDS (global_load_lds_dwordx4: no
-//    staging registers, no VALU), 32 K elements per stage, in a ring of 3 stages, so
-//    two stages are in flight while one is consumed.
-//  * LDS rows are 64 bytes (four 16-byte chunks) with the chunk index XOR-swizzled
-//    by bits 2..3 of the row, so the 16-byte operand reads fall in distinct banks
-//    without padding (a direct LDS load writes 1 KB contiguously, which rules
-//    padding out).
+//    staging registers, no VALU), in a ring of 3 stages, so two stages are in flight
+//    while one is consumed.  A stage is 32 K elements (64-byte rows) or 64 (128-byte
+//    rows: each staged row piece is a whole line of its source row, which L2 serves
+//    faster per byte than half lines, at the price of 144 KB of ring).
+//  * LDS rows hold 16-byte chunks with the chunk index XOR-swizzled by a few row bits,
+//    so the 16-byte operand reads fall in distinct banks without padding (a direct LDS
+//    load writes 1 KB contiguously, which rules padding out).
 //  * Waits are explicit: vmcnt counts this wave's loads of the stages still in flight,
 //    and the work-group barrier carries no memory fence (a fence would drain the
-//    loads in flight).  The barrier of step kt lands after this step's operands are in
-//    registers, so the stage it frees is refilled three steps ahead.
+//    loads in flight).  The barrier that ends stage st lands after the next stage's
+//    first operands are in registers, so the slot it frees is refilled three stages
+//    ahead.
 #include <hip/hip_ext.h>
 
 #include <type_traits>
@@ -40,17 +43,7 @@ namespace {
 constexpr int NXCD = 8;
 constexpr int BM = 128;                 // rows per m-tile (the grouping's tile)
 constexpr int WROWS = 128;              // weight rows per wave
-constexpr int BK = 32;                  // K elements per stage
-constexpr int ROWB = BK * 2;            // bytes of one staged row
-#ifndef MOE_WIDE_NSTAGE
-#define MOE_WIDE_NSTAGE 3
-#endif
-#ifndef MOE_WIDE_OCC
-#define MOE_WIDE_OCC 2
-#endif
-// LDS ring depth and work-groups per CU.  Measured on the 8192-token chunk: 3 stages
-// with two work-groups per CU beat 4-6 stages with one (607 vs 675-680 us gate/up).
-constexpr int NSTAGE = MOE_WIDE_NSTAGE;
+constexpr int BK = 32;                  // K elements of one step (two 16-deep MFMA slices)
 constexpr int GM = 8;                   // m-tiles per group of the tile order
 
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
@@ -69,12 +62,16 @@ struct WideParams {
     int mt_max, nt;
 };
 
-// The 16-byte chunk kc of LDS row r sits at chunk slot kc ^ swz(r).  Measured on
+// The 16-byte chunk kc of LDS row r sits at chunk slot kc ^ swz<KH>(r).  Measured on
 // gfx950 (SQ_LDS_BANK_CONFLICT of an isolated read loop): with 64-byte rows, the
 // 16-byte MFMA operand reads (32 rows, two chunks per row per half-wave) are
 // conflict-free with bits 2..3 of the row as the XOR key, 2-way with bits 1..2,
-// 4-way unswizzled.
-__device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
+// 4-way unswizzled.  That fits 64 four-byte banks with 16 lanes of a 16-byte read
+// served together: the 16 rows a read pass touches must spread over the 16 chunk
+// positions of 256 bytes.  With 128-byte rows (two steps per stage) two rows share a
+// 256-byte span, so the key is bits 1..3 of the row over eight chunk slots.
+template <int KH>
+__device__ __forceinline__ int swz(int r) { return KH == 1 ? (r >> 2) & 3 : (r >> 1) & 7; }
 
 
 
@@ -84,18 +81,26 @@ __device__ __forceinline__ int swz(int r) { return (r >> 2) & 3; }
 }  // namespace
 
 // WM x WN waves (4 or 8); each wave owns BM/WM rows x 128 weight rows.
-// MX: the weights are MXFP4.  A stage then holds each B row's 16 bytes of E2M1 codes
-// (32 K elements; row stride 16 bytes, which 4-byte operand reads of 16 consecutive
-// rows take without bank conflicts), the tile's E8M0 scales for the whole K sit in an
-// LDS table loaded once, and each B operand is decoded to bf16 as it is read from LDS
-// (v_cvt_scalef32_pk_bf16_fp4): a quarter of the LDS bytes of bf16 weights.
-template <int MODE, int WM, int WN, int OCC, bool MX>
+// KH: steps (32 K elements each) per LDS stage.  KH = 2 stages 64 K elements, so every
+// staged row is one whole 128-byte line of the source row: L2 serves a CU's requests
+// line by line, and half-line requests take about as long as whole ones.  NS: stages
+// in the LDS ring.
+// MX: the weights are MXFP4 (KH = 1).  A stage then holds each B row's 16 bytes of E2M1
+// codes (32 K elements; row stride 16 bytes, which 4-byte operand reads of 16
+// consecutive rows take without bank conflicts), the tile's E8M0 scales for the whole K
+// sit in an LDS table loaded once, and each B operand is decoded to bf16 as it is read
+// from LDS (v_cvt_scalef32_pk_bf16_fp4): a quarter of the LDS bytes of bf16 weights.
+template <int MODE, int WM, int WN, int OCC, bool MX, int KH, int NS>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(WideParams p) {
     constexpr int NTH = WM * WN * 64;
     static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
+    static_assert(KH == 1 || (KH == 2 && !MX), "two-step stages are for bf16 weights");
+    static_assert(NS >= 2, "at least two stages");
     constexpr int BN = WN * WROWS;                   // weight rows per n-tile
     constexpr int RW = BM / WM;                      // rows per wave
     constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
+    constexpr int ROWB = 64 * KH;                    // bytes of one staged bf16 row
+    constexpr int LPR = ROWB / 16;                   // lanes per staged row in a direct load
     constexpr int B_ROWB = MX ? BK / 2 : ROWB;       // bytes of one staged B row
     constexpr int A_BYTES = BM * ROWB, B_BYTES = BN * B_ROWB;
     constexpr int STAGE = A_BYTES + B_BYTES;
@@ -125,7 +130,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
     const size_t krow = (size_t)p.K * 2;           // bytes of one A row
-    const int KT = p.K / BK;   // stages; even and >= 4 (wide_*_supported)
+    const int NST = p.K / (BK * KH);   // stages; KH == 1: even and >= 4, KH == 2: >= 2 (wide_*_supported)
 
     for (int m = tid; m < BM; m += NTH) {
         const int pos = min(m0 + m, m_end - 1);
@@ -136,14 +141,15 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     __syncthreads();
 
     // ---- sources of this lane's direct loads.  One wave-wide load fills 1 KB of LDS,
-    // 16 rows of 4 chunks; lane l lands in row 16g + l/4 at chunk slot l%4, which holds
-    // the row's logical chunk (l%4) ^ swz(row).
-    const int lrow = lane >> 2;
+    // 1024 / ROWB rows of LPR chunks; lane l lands in row (1024 / ROWB) g + l / LPR at
+    // chunk slot l % LPR, which holds the row's logical chunk (l % LPR) ^ swz(row).
+    constexpr int RPL = 1024 / ROWB;               // rows per wave-wide load
+    const int lrow = lane / LPR;
     const uint8_t *asrc[A_LOADS];
 #pragma unroll
     for (int q = 0; q < A_LOADS; ++q) {
-        const int r = 16 * (wave * A_LOADS + q) + lrow;
-        const int kc = (lane & 3) ^ swz(r);
+        const int r = RPL * (wave * A_LOADS + q) + lrow;
+        const int kc = (lane % LPR) ^ swz<KH>(r);
         const size_t row = MODE == WG_GATEUP ? (size_t)(s_slot[r] / p.topk) : (size_t)min(m0 + r, m_end - 1);
         asrc[q] = p.a + row * krow + kc * 16;
     }
@@ -165,25 +171,25 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     const uint8_t *bsrc[B_LOADS];
 #pragma unroll
     for (int q = 0; q < B_LOADS; ++q) {
-        // bf16: 16 rows of 4 swizzled chunks per wave-wide load; MX: 64 rows of one chunk
-        const int r = MX ? 64 * (wave * B_LOADS + q) + lane : 16 * (wave * B_LOADS + q) + lrow;
-        const int kc = MX ? 0 : (lane & 3) ^ swz(r);
+        // bf16: RPL rows of LPR swizzled chunks per wave-wide load; MX: 64 rows of one chunk
+        const int r = MX ? 64 * (wave * B_LOADS + q) + lane : RPL * (wave * B_LOADS + q) + lrow;
+        const int kc = MX ? 0 : (lane % LPR) ^ swz<KH>(r);
         bool second;
         const size_t wrow = brow_of(r, second);
         bsrc[q] = (second ? p.b1 : p.b0) + wrow * brow_bytes + kc * 16;
     }
-    auto issue = [&](int kt, int stage) WG_INLINE {
+    auto issue = [&](int st, int stage) WG_INLINE {
         uint8_t *sa = lds + stage * STAGE;
-        const size_t ko = (size_t)kt * ROWB;
+        const size_t ko = (size_t)st * ROWB;
 #pragma unroll
         for (int q = 0; q < A_LOADS; ++q)
             load_lds16(asrc[q] + ko, sa + (wave * A_LOADS + q) * 1024);
 #pragma unroll
         for (int q = 0; q < B_LOADS; ++q)
-            load_lds16(bsrc[q] + (size_t)kt * B_ROWB, sa + A_BYTES + (wave * B_LOADS + q) * 1024);
+            load_lds16(bsrc[q] + (size_t)st * B_ROWB, sa + A_BYTES + (wave * B_LOADS + q) * 1024);
     };
     // MX: the tile's scale table [BN][K/32] bytes at SC_OFF, loaded once (K % 512 == 0)
-    constexpr int SC_OFF = NSTAGE * STAGE;
+    constexpr int SC_OFF = NS * STAGE;
     const int spr = p.K / 32;                       // scale bytes per B row
     auto issue_scales = [&]() WG_INLINE {
         const int cpr = spr / 16;                   // 16-byte chunks per row
@@ -195,19 +201,24 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
         }
     };
 
-    // ---- operand reads: lane reads row (32 * blk + lane % 32), logical chunk 2s + lane / 32
+    // ---- operand reads: lane reads row (32 * blk + lane % 32), logical chunk 4h + 2s +
+    // lane / 32 for step half h of the stage and K16 sub-step s.  The chunk bits 0..1 and
+    // bit 2 do not mix under the key, so half h is the offset of half 0 with bit 6 flipped.
     const int lr = lane & 31, hh = lane >> 5;
-    const int opoff0 = lr * ROWB + ((hh ^ swz(lr)) * 16);
-    const int opoff1 = lr * ROWB + (((2 + hh) ^ swz(lr)) * 16);
+    const int opoff0 = lr * ROWB + ((hh ^ swz<KH>(lr)) * 16);
+    const int opoff1 = lr * ROWB + (((2 + hh) ^ swz<KH>(lr)) * 16);
     bf16x8_t av[2][2][MI], bv[2][2][NJ];   // [buffer][k16 sub-step][block]
-    // buf is a compile-time constant (std::integral_constant) so the operand arrays stay in registers
+    // kt: the step (32 K elements) whose operands are read, from ring slot `stage`.
+    // buf is a compile-time constant (std::integral_constant) so the operand arrays stay
+    // in registers; so is the step's half of its stage (KH == 2: the buffer).
     auto read_ops = [&](int kt, int stage, auto buf_c) WG_INLINE {
         constexpr int buf = decltype(buf_c)::value;
+        constexpr int hoff = KH == 2 ? 64 * buf : 0;
         const uint8_t *sa = lds + stage * STAGE + wm * RW * ROWB;
         const uint8_t *sb = lds + stage * STAGE + A_BYTES + wn * WROWS * B_ROWB;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int o = s ? opoff1 : opoff0;
+            const int o = (s ? opoff1 : opoff0) ^ hoff;
 #pragma unroll
             for (int i = 0; i < MI; ++i) av[buf][s][i] = *reinterpret_cast<const bf16x8_t *>(sa + i * 32 * ROWB + o);
             if constexpr (!MX) {
@@ -256,54 +267,74 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
 
     using C0 = std::integral_constant<int, 0>;
     using C1 = std::integral_constant<int, 1>;
-    // prologue: stages 0..2 in flight, stage 0 landed for every wave, its operands read
+    // prologue: stages 0..NS-1 in flight, stage 0 landed for every wave, its first step's
+    // operands read
     if constexpr (MX) issue_scales();   // older than the stage loads: retired by the first wait
 #pragma unroll
-    for (int st = 0; st < NSTAGE; ++st) issue(min(st, KT - 1), st);
-    wait_vm<(NSTAGE - 1) * LOADS>();
+    for (int st = 0; st < NS; ++st) issue(min(st, NST - 1), st);
+    wait_vm<(NS - 1) * LOADS>();
     barrier_nofence();
     read_ops(0, 0, C0{});
 
-    // Step kt (operands of kt in register buffer kt&1, stages kt+1 .. kt+NSTAGE-1 in
-    // flight): MFMAs of the first K16 half; wait until this wave's loads of kt+1 landed
-    // and its LDS reads are done; barrier (so every wave's loads of kt+1 landed and
-    // every wave is done reading stage kt); refill stage kt with kt+NSTAGE; read the
-    // operands of kt+1; MFMAs of the second half.  In the last full step (vm 0) nothing
-    // is refilled.
+    // A step consumes the operands of one 32-deep K slice from register buffer `cur`
+    // and reads the next slice's into the other buffer.  A step that ends a stage (every
+    // step for KH == 1, the second of each pair for KH == 2): MFMAs of the first K16
+    // half; wait until this wave's loads of the next stage landed and its LDS reads are
+    // done; barrier (so every wave's loads of the next stage landed and every wave is
+    // done reading this one); refill this stage's slot NS stages ahead; read the next
+    // stage's first operands; MFMAs of the second half.  A step inside a stage (KH == 2,
+    // the first of each pair) only reads the stage's second half between its MFMAs.  In
+    // the last stage-ending step (vm 0) nothing is refilled.
     // Scheduling: the MFMAs of the first half stay before the barrier, and the loads,
     // LDS reads and MFMAs of the second half are interleaved after it.  The refill
-    // index is clamped: near the end it reloads the last stage into a stage nobody
+    // index is clamped: near the end it reloads the last stage into a slot nobody
     // reads again, which keeps the step branch-free.
     constexpr int NMF = MI * NJ, NRD = MX ? 2 * MI + 3 * NJ : 2 * (MI + NJ);
-    auto step = [&](int kt, auto cur_c, auto vm_c, auto refill_c) WG_INLINE {
+    constexpr int VPM = (LOADS + NMF - 1) / NMF;   // refill loads placed per MFMA
+    auto step = [&](int kt, int st, auto cur_c, auto ends_c, auto vm_c, auto refill_c) WG_INLINE {
         using Next = std::integral_constant<int, 1 - decltype(cur_c)::value>;
-        constexpr bool refill = decltype(refill_c)::value;
+        constexpr bool ends = decltype(ends_c)::value;
+        constexpr bool refill = ends && decltype(refill_c)::value;
         mfma_sub(cur_c, C0{});
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<decltype(vm_c)::value>();
-        wait_lgkm0();
-        barrier_nofence();
-        __builtin_amdgcn_sched_barrier(0);
-        if (refill) issue(min(kt + NSTAGE, KT - 1), kt % NSTAGE);
-        read_ops(kt + 1, (kt + 1) % NSTAGE, Next{});
+        if constexpr (ends) {
+            wait_vm<decltype(vm_c)::value>();
+            wait_lgkm0();
+            barrier_nofence();
+            __builtin_amdgcn_sched_barrier(0);
+            if (refill) issue(min(st + NS, NST - 1), st % NS);
+            read_ops(kt + 1, (st + 1) % NS, Next{});
+        } else {
+            read_ops(kt + 1, st % NS, Next{});
+        }
         mfma_sub(cur_c, C1{});
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                   // one MFMA
-            if (refill && q < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);          // one VMEM read
+            if (refill && q * VPM < LOADS) __builtin_amdgcn_sched_group_barrier(0x020, VPM, 0);  // VMEM reads
             if (q < NRD) __builtin_amdgcn_sched_group_barrier(0x100, NRD / NMF > 1 ? NRD / NMF : 1, 0);  // LDS reads
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    using VL = std::integral_constant<int, (NSTAGE - 2) * LOADS>;
+    using VL = std::integral_constant<int, (NS - 2) * LOADS>;
     using V0 = std::integral_constant<int, 0>;
-    using RF = std::true_type;
-    using NR = std::false_type;
-    for (int kt = 0; kt < KT - 2; kt += 2) {
-        step(kt, C0{}, VL{}, RF{});
-        step(kt + 1, C1{}, VL{}, RF{});
+    using T = std::true_type;
+    using F = std::false_type;
+    if constexpr (KH == 1) {
+        for (int kt = 0; kt < NST - 2; kt += 2) {
+            step(kt, kt, C0{}, T{}, VL{}, T{});
+            step(kt + 1, kt + 1, C1{}, T{}, VL{}, T{});
+        }
+        step(NST - 2, NST - 2, C0{}, T{}, V0{}, F{});
+    } else {
+        for (int st = 0; st < NST - 2; ++st) {
+            step(2 * st, st, C0{}, F{}, V0{}, F{});
+            step(2 * st + 1, st, C1{}, T{}, VL{}, T{});
+        }
+        step(2 * NST - 4, NST - 2, C0{}, F{}, V0{}, F{});
+        step(2 * NST - 3, NST - 2, C1{}, T{}, V0{}, F{});
+        step(2 * NST - 2, NST - 1, C0{}, F{}, V0{}, F{});
     }
-    step(KT - 2, C0{}, V0{}, NR{});
     mfma_sub(C1{}, C0{});
     mfma_sub(C1{}, C1{});
 
@@ -368,24 +399,32 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
 
 namespace {
 
-// the configuration the launchers use: 2 x 2 waves (64 x 128 per wave, 128 x 256 per
-// work-group, 72 KB of LDS), two work-groups per CU
-#ifndef MOE_WIDE_WM
-#define MOE_WIDE_WM 2
-#endif
-#ifndef MOE_WIDE_WN
-#define MOE_WIDE_WN 2
-#endif
-constexpr int CWM = MOE_WIDE_WM, CWN = MOE_WIDE_WN, CNTH = CWM * CWN * 64;
-constexpr int CBN = CWN * WROWS;
+// the configurations the launchers use, per GEMM (the 8192-token chunk, H=2048, E=128,
+// k=8, I=768, same-box A/B):
+//  * bf16 gate/up: 4 x 2 waves (32 x 128 per wave, 128 x 256 per work-group), stages of
+//    64 K elements (whole-line rows), 3 of them (144 KB), one work-group per CU;
+//  * down (bf16 and MXFP4): 2 x 2 waves (64 x 128 per wave), stages of 32 K elements,
+//    3 of them (72 KB; MXFP4 codes of a B row are 16 bytes per step either way), two
+//    work-groups per CU.
+constexpr int CWN = 2, CBN = CWN * WROWS;
 constexpr int MX_MAX_K = 4096;   // MXFP4: the tile's scale table (CBN x K/32 bytes) stays <= 32 KB
 
 template <int MODE, bool MX>
+struct WideCfg {
+    static constexpr bool wide_stage = MODE == WG_GATEUP && !MX;
+    static constexpr int WM = wide_stage ? 4 : 2, KH = wide_stage ? 2 : 1, NS = 3, OCC = wide_stage ? 1 : 2;
+    static constexpr int NTH = WM * CWN * 64;
+};
+
+template <int MODE, bool MX>
 hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
-    constexpr size_t ring = (size_t)NSTAGE * (BM * ROWB + CBN * (MX ? BK / 2 : ROWB));
+    using C = WideCfg<MODE, MX>;
+    constexpr size_t rowb = 64 * C::KH;
+    constexpr size_t ring = (size_t)C::NS * (BM * rowb + CBN * (MX ? BK / 2 : rowb));
     constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
+    static_assert(lds_max <= 160 * 1024 - 2048, "LDS ring too large");
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, CWM, CWN, MOE_WIDE_OCC, MX>;
+    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, CWN, C::OCC, MX, C::KH, C::NS>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
@@ -396,9 +435,9 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
     if (ev0 || ev1)
-        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), lds, st, ev0, ev1, 0, prm);
+        hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(C::NTH), lds, st, ev0, ev1, 0, prm);
     else
-        hipLaunchKernelGGL(kern, dim3(nblk), dim3(CNTH), lds, st, prm);
+        hipLaunchKernelGGL(kern, dim3(nblk), dim3(C::NTH), lds, st, prm);
     return hipGetLastError();
 }
 
@@ -411,8 +450,9 @@ int mt_max_wide(const moe_shape &s) {
 
 static_assert(BM == kGroupedTileM, "m-tiles follow the grouping");
 
-// K must be a whole even number of stages, at least 4; MXFP4 also wants K a multiple of
-// 512 (whole 16-byte chunks of scales per row) and at most MX_MAX_K
+// K must be a multiple of 64 and at least 128 (an even number of 32-deep steps, at least
+// 4: two stages of 64); MXFP4 also wants K a multiple of 512 (whole 16-byte chunks of
+// scales per row) and at most MX_MAX_K
 static bool wide_k_ok(const moe_shape &s, int K) {
     if (K % (2 * BK) || K < 4 * BK) return false;
     return s.weight_dtype == MOE_BF16 || (K % 512 == 0 && K <= MX_MAX_K);

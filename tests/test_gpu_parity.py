@@ -511,10 +511,13 @@ def test_forward_grouped_ragged_zipf():
     compare_forward(li, got, label="grouped ragged zipf")
 
 
-@pytest.mark.parametrize("T,H,E,K,I,beta", [(333, 512, 16, 4, 256, 2.0), (1000, 1024, 32, 8, 512, 1.0)])
+@pytest.mark.parametrize("T,H,E,K,I,beta", [(333, 512, 16, 4, 256, 2.0), (1000, 1024, 32, 8, 512, 1.0),
+                                           (200, 512, 8, 2, 128, 1.0), (150, 768, 8, 2, 384, 1.0)])
 def test_forward_grouped_wide_tiles_ragged(T, H, E, K, I, beta):
-    """Shapes that take the large-tile kernels for both expert GEMMs (I a multiple of
-    256, H of 512): skewed groups with partial m-tiles, several n-tiles, K of 4+ stages."""
+    """Shapes that take the large-tile kernels for the expert GEMMs (gate/up: I a
+    multiple of 128; down: H a multiple of 256): skewed groups with partial m-tiles,
+    several n-tiles.  I = 128 gives the down projection the fewest 64-deep stages (two);
+    H = 768 and I = 384 give three n-tiles to each GEMM."""
     note(f"grouped wide T={T} H={H} E={E} K={K} I={I}")
     sh_ = synth.Shape(T, H, E, K, I, "bf16", "bf16", bias="zipf")
     li = synth.make_layer(sh_, beta=beta)
