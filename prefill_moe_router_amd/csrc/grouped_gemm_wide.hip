@@ -12,8 +12,9 @@
 //    (128 registers), so one 16-deep K slice moves 6 KB of operands out of LDS per 8
 //    MFMAs; 72 KB of LDS and <= 256 registers per lane let two work-groups share a
 //    CU, so one group's tile start (metadata loads, pipeline fill) and epilogue hide
-//    under the other's MFMAs.  GATEUP: 4 x 2 waves of 32 x 128 in one work-group per
-//    CU, with 64-deep stages (below).
+//    under the other's MFMAs.  GATEUP: 4 x 2 waves of 32 x 128 in one persistent
+//    work-group per CU, with 64-deep stages (below); it fetches each next tile's rows
+//    under the K loop and its first stages under the epilogue.
 //  * Each m-tile's rows come from a tile table the grouping writes ({first row, end
 //    row, expert} per tile): one load, no search over the m-tile offsets.
 //  * Operands go from global memory straight into LDS (global_load_lds_dwordx4: no
@@ -90,12 +91,17 @@ __device__ __forceinline__ int swz(int r) { return KH == 1 ? (r >> 2) & 3 : (r >
 // consecutive rows take without bank conflicts), the tile's E8M0 scales for the whole K
 // sit in an LDS table loaded once, and each B operand is decoded to bf16 as it is read
 // from LDS (v_cvt_scalef32_pk_bf16_fp4): a quarter of the LDS bytes of bf16 weights.
-template <int MODE, int WM, int WN, int OCC, bool MX, int KH, int NS>
+// PER: persistent work-groups (one per CU, with the 144 KB ring) that walk their XCD's
+// share of tiles.  Under each K loop they fetch the next tile's rows; after it, the next
+// tile's first two stages load into ring slots 0 and 1 while the epilogue transposes
+// through slot 2, so a tile's start no longer waits on the tile table and row list.
+template <int MODE, int WM, int WN, int OCC, bool MX, int KH, int NS, bool PER>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(WideParams p) {
     constexpr int NTH = WM * WN * 64;
     static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
     static_assert(KH == 1 || (KH == 2 && !MX), "two-step stages are for bf16 weights");
     static_assert(NS >= 2, "at least two stages");
+    static_assert(!PER || (NS == 3 && WM * WN * 64 >= BM), "persistent: three slots, a thread per tile row");
     constexpr int BN = WN * WROWS;                   // weight rows per n-tile
     constexpr int RW = BM / WM;                      // rows per wave
     constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
@@ -108,35 +114,51 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     constexpr int LOADS = A_LOADS + B_LOADS;
     constexpr int NCOL = MODE == WG_GATEUP ? BN / 2 : BN;   // output columns per n-tile
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
-    __shared__ int s_slot[BM];
+    __shared__ int s_slot[PER ? 2 : 1][BM];
     __shared__ float s_scale[BM];
 
     // ---- which tile: groups of GM m-tiles swept n-tile by n-tile (the last group holds
     // the remaining m-tiles), each XCD a contiguous, equal share of that order (blocks are
     // dealt to XCDs round-robin).  The share comes from the tile count the grouping wrote,
-    // so the grid's slack past it (sized for the worst case) exits at once.
+    // so the grid's slack past it (sized for the worst case) exits at once; persistent
+    // work-groups take every (grid / 8)-th tile of their XCD's share.
     const int n_mt = p.mtile_off[p.E];
     const int total = n_mt * p.nt;
     const int per_xcd = (total + NXCD - 1) / NXCD;
-    const int slot = blockIdx.x / NXCD;
-    const int L = (blockIdx.x % NXCD) * per_xcd + slot;
-    if (slot >= per_xcd || L >= total) return;
-    const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
-    const int gm = min(GM, n_mt - grp * GM);          // m-tiles in this group
-    const int n_tile = in_grp / gm, mt = grp * GM + in_grp % gm;
-    const int4 tinfo = p.tiles[mt];
-    const int m0 = tinfo.x, m_end = tinfo.y, e = tinfo.z;
+    const int xcd = blockIdx.x % NXCD;
+    const int wstride = PER ? (int)(gridDim.x / NXCD) : per_xcd;
+    // tile idx of this XCD's share: its n-tile, rows [m0, m_end) and expert
+    auto tile_at = [&](int idx, int &nt_, int &m0_, int &mend_, int &e_) WG_INLINE {
+        const int L = xcd * per_xcd + idx;
+        if (idx >= per_xcd || L >= total) return false;
+        const int grp = L / (GM * p.nt), in_grp = L % (GM * p.nt);
+        const int gm = min(GM, n_mt - grp * GM);          // m-tiles in this group
+        nt_ = in_grp / gm;
+        // through the constant address space: a scalar load, counted by lgkmcnt, so fetching
+        // the next tile under a K loop does not wait for the stage loads in flight (the table
+        // is written by an earlier launch and only read here)
+        typedef int i32x4c __attribute__((ext_vector_type(4)));
+        const i32x4c ti = ((const __attribute__((address_space(4))) i32x4c *)(uintptr_t)p.tiles)[grp * GM + in_grp % gm];
+        m0_ = ti.x;
+        mend_ = ti.y;
+        e_ = ti.z;
+        return true;
+    };
+    int idx = blockIdx.x / NXCD;
+    int n_tile, m0, m_end, e;
+    if (!tile_at(idx, n_tile, m0, m_end, e)) return;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
     const size_t krow = (size_t)p.K * 2;           // bytes of one A row
     const int NST = p.K / (BK * KH);   // stages; KH == 1: even and >= 4, KH == 2: >= 2 (wide_*_supported)
 
+    int sb = 0;   // s_slot buffer of the current tile
     for (int m = tid; m < BM; m += NTH) {
         const int pos = min(m0 + m, m_end - 1);
         const int slot = p.sorted[pos];
-        s_slot[m] = slot;
-        s_scale[m] = (MODE == WG_GATEUP && m0 + m < m_end) ? (p.wts ? p.wts[slot] : 1.f) : 0.f;
+        s_slot[0][m] = slot;
+        if (!PER) s_scale[m] = (MODE == WG_GATEUP && m0 + m < m_end) ? (p.wts ? p.wts[slot] : 1.f) : 0.f;
     }
     __syncthreads();
 
@@ -145,39 +167,44 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     // chunk slot l % LPR, which holds the row's logical chunk (l % LPR) ^ swz(row).
     constexpr int RPL = 1024 / ROWB;               // rows per wave-wide load
     const int lrow = lane / LPR;
-    const uint8_t *asrc[A_LOADS];
-#pragma unroll
-    for (int q = 0; q < A_LOADS; ++q) {
-        const int r = RPL * (wave * A_LOADS + q) + lrow;
-        const int kc = (lane % LPR) ^ swz<KH>(r);
-        const size_t row = MODE == WG_GATEUP ? (size_t)(s_slot[r] / p.topk) : (size_t)min(m0 + r, m_end - 1);
-        asrc[q] = p.a + row * krow + kc * 16;
-    }
     // B: LDS row q of the tile belongs to wave q / 128.  GATEUP: rows 0-63 of a wave's
     // range are gate columns c0 + 64 * (q / 128) + (0..63), rows 64-127 the same up
     // columns (c0 = the n-tile's first intermediate column).  DOWN: output column
     // n0 + q.
-    // global weight row of LDS B row r, and whether it belongs to the second matrix (up)
-    auto brow_of = [&](int r, bool &second) WG_INLINE {
+    // global weight row of LDS B row r of n-tile nt_ of expert e_, and whether it belongs
+    // to the second matrix (up)
+    auto brow_of = [&](int r, bool &second, int e_, int nt_) WG_INLINE {
         if (MODE == WG_GATEUP) {
             const int rl = r % WROWS;
             second = rl >= 64;
-            return (size_t)e * p.N + (size_t)n_tile * NCOL + 64 * (r / WROWS) + (rl & 63);
+            return (size_t)e_ * p.N + (size_t)nt_ * NCOL + 64 * (r / WROWS) + (rl & 63);
         }
         second = false;
-        return (size_t)e * p.N + (size_t)n_tile * BN + r;
+        return (size_t)e_ * p.N + (size_t)nt_ * BN + r;
     };
     const size_t brow_bytes = MX ? (size_t)p.K / 2 : krow;   // bytes of one global B row
+    const uint8_t *asrc[A_LOADS];
     const uint8_t *bsrc[B_LOADS];
+    // sources of a tile whose row slots are in s_slot[sbuf]
+    auto set_sources = [&](int sbuf, int e_, int nt_, int m0_, int mend_) WG_INLINE {
 #pragma unroll
-    for (int q = 0; q < B_LOADS; ++q) {
-        // bf16: RPL rows of LPR swizzled chunks per wave-wide load; MX: 64 rows of one chunk
-        const int r = MX ? 64 * (wave * B_LOADS + q) + lane : RPL * (wave * B_LOADS + q) + lrow;
-        const int kc = MX ? 0 : (lane % LPR) ^ swz<KH>(r);
-        bool second;
-        const size_t wrow = brow_of(r, second);
-        bsrc[q] = (second ? p.b1 : p.b0) + wrow * brow_bytes + kc * 16;
-    }
+        for (int q = 0; q < A_LOADS; ++q) {
+            const int r = RPL * (wave * A_LOADS + q) + lrow;
+            const int kc = (lane % LPR) ^ swz<KH>(r);
+            const size_t row = MODE == WG_GATEUP ? (size_t)(s_slot[sbuf][r] / p.topk) : (size_t)min(m0_ + r, mend_ - 1);
+            asrc[q] = p.a + row * krow + kc * 16;
+        }
+#pragma unroll
+        for (int q = 0; q < B_LOADS; ++q) {
+            // bf16: RPL rows of LPR swizzled chunks per wave-wide load; MX: 64 rows of one chunk
+            const int r = MX ? 64 * (wave * B_LOADS + q) + lane : RPL * (wave * B_LOADS + q) + lrow;
+            const int kc = MX ? 0 : (lane % LPR) ^ swz<KH>(r);
+            bool second;
+            const size_t wrow = brow_of(r, second, e_, nt_);
+            bsrc[q] = (second ? p.b1 : p.b0) + wrow * brow_bytes + kc * 16;
+        }
+    };
+    set_sources(0, e, n_tile, m0, m_end);
     auto issue = [&](int st, int stage) WG_INLINE {
         uint8_t *sa = lds + stage * STAGE;
         const size_t ko = (size_t)st * ROWB;
@@ -196,7 +223,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
         for (int c0 = wave * WAVE; c0 < BN * cpr; c0 += NTH) {
             const int c = c0 + lane, r = c / cpr, w = c - r * cpr;
             bool second;
-            const size_t wrow = brow_of(r, second);
+            const size_t wrow = brow_of(r, second, e, n_tile);
             load_lds16((second ? p.s1 : p.s0) + wrow * spr + w * 16, lds + SC_OFF + (size_t)c0 * 16);
         }
     };
@@ -249,12 +276,6 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     };
 
     f32x16_t acc[MI][NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     auto mfma_sub = [&](auto buf_c, auto s_c) WG_INLINE {
         constexpr int buf = decltype(buf_c)::value, s = decltype(s_c)::value;
@@ -320,80 +341,130 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     using V0 = std::integral_constant<int, 0>;
     using T = std::true_type;
     using F = std::false_type;
-    if constexpr (KH == 1) {
-        for (int kt = 0; kt < NST - 2; kt += 2) {
-            step(kt, kt, C0{}, T{}, VL{}, T{});
-            step(kt + 1, kt + 1, C1{}, T{}, VL{}, T{});
+    for (;;) {
+        // PER: the next tile's rows and this tile's gate weights, fetched under the K loop
+        // (kept in registers until the epilogue, so the K loop's waits are not extended)
+        int n_nt = 0, n_m0 = 0, n_mend = 0, n_e = 0, n_slot = 0;
+        float c_scale = 0.f;
+        bool have_next = false;
+        if constexpr (PER) {
+            have_next = tile_at(idx + wstride, n_nt, n_m0, n_mend, n_e);
+            if (tid < BM) {
+                if (have_next) n_slot = p.sorted[min(n_m0 + tid, n_mend - 1)];
+                if (MODE == WG_GATEUP) c_scale = m0 + tid < m_end ? (p.wts ? p.wts[s_slot[sb][tid]] : 1.f) : 0.f;
+            }
         }
-        step(NST - 2, NST - 2, C0{}, T{}, V0{}, F{});
-    } else {
-        for (int st = 0; st < NST - 2; ++st) {
-            step(2 * st, st, C0{}, F{}, V0{}, F{});
-            step(2 * st + 1, st, C1{}, T{}, VL{}, T{});
-        }
-        step(2 * NST - 4, NST - 2, C0{}, F{}, V0{}, F{});
-        step(2 * NST - 3, NST - 2, C1{}, T{}, V0{}, F{});
-        step(2 * NST - 2, NST - 1, C0{}, F{}, V0{}, F{});
-    }
-    mfma_sub(C1{}, C0{});
-    mfma_sub(C1{}, C1{});
-
-    // ---- epilogue: each wave transposes its tile through LDS (its own region) and
-    // stores whole 16-byte row pieces.  All waves are past their last LDS operand read
-    // once they pass this barrier.
-    __builtin_amdgcn_s_waitcnt(0);
-    barrier_nofence();
-    // acc[i][j][r] holds C[row][col], row = 32i + 8(r/4) + 4(lane/32) + r%4, col = 32j + lane%32
-    if (MODE == WG_GATEUP) {
-        // wave's h' tile: RW rows x 64 columns (gate blocks j = 0, 1 pair with up blocks 2, 3)
-        constexpr int PITCH = 64 + 8;   // bf16 elements per transposed row
-        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * RW * PITCH;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ml = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float sc = s_scale[wm * RW + ml];
+            for (int j = 0; j < NJ; ++j)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(sc * swiglu(acc[i][j][r], acc[i][2 + j][r]));
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+        if constexpr (KH == 1) {
+            for (int kt = 0; kt < NST - 2; kt += 2) {
+                step(kt, kt, C0{}, T{}, VL{}, T{});
+                step(kt + 1, kt + 1, C1{}, T{}, VL{}, T{});
             }
-        wait_lgkm0();
-        __builtin_amdgcn_wave_barrier();
-        const int col0 = n_tile * NCOL + 64 * wn;
-        for (int q = lane; q < RW * 8; q += 64) {
-            const int ml = q >> 3, ch = q & 7;
-            const int m = wm * RW + ml;
-            if (m0 + m >= m_end) continue;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
-            *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
+            step(NST - 2, NST - 2, C0{}, T{}, V0{}, F{});
+        } else {
+            for (int st = 0; st < NST - 2; ++st) {
+                step(2 * st, st, C0{}, F{}, V0{}, F{});
+                step(2 * st + 1, st, C1{}, T{}, VL{}, T{});
+            }
+            step(2 * NST - 4, NST - 2, C0{}, F{}, V0{}, F{});
+            step(2 * NST - 3, NST - 2, C1{}, T{}, V0{}, F{});
+            step(2 * NST - 2, NST - 1, C0{}, F{}, V0{}, F{});
         }
-    } else {
-        // wave's o' tile: RW rows x 128 columns, in passes of 32 rows
-        constexpr int PITCH = 128 + 8;
-        uint16_t *ep = reinterpret_cast<uint16_t *>(lds) + wave * 32 * PITCH;
-        const int col0 = n_tile * BN + WROWS * wn;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int ml = 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-                for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+        mfma_sub(C1{}, C0{});
+        mfma_sub(C1{}, C1{});
+
+        // ---- epilogue: each wave transposes its tile through LDS (its own region) and
+        // stores whole 16-byte row pieces.  All waves are past their last LDS operand read
+        // once they pass this barrier.
+        __builtin_amdgcn_s_waitcnt(0);
+        barrier_nofence();
+        uint8_t *epi = lds;
+        if constexpr (PER) {
+            // this tile's gate weights and the next tile's row slots into LDS, then the next
+            // tile's first two stages into slots 0 and 1; the epilogue works in slot 2
+            if (tid < BM) {
+                s_scale[tid] = c_scale;
+                if (have_next) s_slot[sb ^ 1][tid] = n_slot;
             }
+            __syncthreads();
+            if (have_next) {
+                set_sources(sb ^ 1, n_e, n_nt, n_m0, n_mend);
+                issue(0, 0);
+                issue(min(1, NST - 1), 1);
+            }
+            epi = lds + 2 * STAGE;
+        }
+        // acc[i][j][r] holds C[row][col], row = 32i + 8(r/4) + 4(lane/32) + r%4, col = 32j + lane%32
+        if (MODE == WG_GATEUP) {
+            // wave's h' tile: RW rows x 64 columns (gate blocks j = 0, 1 pair with up blocks 2, 3)
+            constexpr int PITCH = 64 + 8;   // bf16 elements per transposed row
+            uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * RW * PITCH;
+    #pragma unroll
+            for (int i = 0; i < MI; ++i)
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
+                    const float sc = s_scale[wm * RW + ml];
+    #pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(sc * swiglu(acc[i][j][r], acc[i][2 + j][r]));
+                }
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
-            for (int q = lane; q < 32 * 16; q += 64) {
-                const int ml = q >> 4, ch = q & 15;
-                const int m = wm * RW + 32 * i + ml;
+            const int col0 = n_tile * NCOL + 64 * wn;
+            for (int q = lane; q < RW * 8; q += 64) {
+                const int ml = q >> 3, ch = q & 7;
+                const int m = wm * RW + ml;
                 if (m0 + m >= m_end) continue;
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
-                *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[m] * p.N + col0 +
-                                             ch * 8) = v;
+                *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
             }
-            wait_lgkm0();
-            __builtin_amdgcn_wave_barrier();
+        } else {
+            // wave's o' tile: RW rows x 128 columns, in passes of 32 rows
+            constexpr int PITCH = 128 + 8;
+            uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * 32 * PITCH;
+            const int col0 = n_tile * BN + WROWS * wn;
+    #pragma unroll
+            for (int i = 0; i < MI; ++i) {
+    #pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int ml = 8 * (r >> 2) + 4 * hh + (r & 3);
+    #pragma unroll
+                    for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                }
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
+                for (int q = lane; q < 32 * 16; q += 64) {
+                    const int ml = q >> 4, ch = q & 15;
+                    const int m = wm * RW + 32 * i + ml;
+                    if (m0 + m >= m_end) continue;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
+                    *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[sb][m] * p.N + col0 +
+                                                 ch * 8) = v;
+                }
+                wait_lgkm0();
+                __builtin_amdgcn_wave_barrier();
+            }
         }
+        if (!PER || !have_next) break;
+        // the next tile: its stages 0 and 1 landed (vm 0 also retires the epilogue's stores),
+        // every wave is past the epilogue's use of slot 2, which now takes stage 2
+        idx += wstride;
+        n_tile = n_nt;
+        m0 = n_m0;
+        m_end = n_mend;
+        e = n_e;
+        sb ^= 1;
+        wait_vm<0>();
+        wait_lgkm0();
+        barrier_nofence();
+        issue(min(2, NST - 1), 2);
+        read_ops(0, 0, C0{});
     }
 }
 
@@ -402,7 +473,7 @@ namespace {
 // the configurations the launchers use, per GEMM (the 8192-token chunk, H=2048, E=128,
 // k=8, I=768, same-box A/B):
 //  * bf16 gate/up: 4 x 2 waves (32 x 128 per wave, 128 x 256 per work-group), stages of
-//    64 K elements (whole-line rows), 3 of them (144 KB), one work-group per CU;
+//    64 K elements (whole-line rows), 3 of them (144 KB), one persistent work-group per CU;
 //  * down (bf16 and MXFP4): 2 x 2 waves (64 x 128 per wave), stages of 32 K elements,
 //    3 of them (72 KB; MXFP4 codes of a B row are 16 bytes per step either way), two
 //    work-groups per CU.
@@ -413,6 +484,7 @@ template <int MODE, bool MX>
 struct WideCfg {
     static constexpr bool wide_stage = MODE == WG_GATEUP && !MX;
     static constexpr int WM = wide_stage ? 4 : 2, KH = wide_stage ? 2 : 1, NS = 3, OCC = wide_stage ? 1 : 2;
+    static constexpr bool PER = wide_stage;
     static constexpr int NTH = WM * CWN * 64;
 };
 
@@ -424,7 +496,7 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
     static_assert(lds_max <= 160 * 1024 - 2048, "LDS ring too large");
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, CWN, C::OCC, MX, C::KH, C::NS>;
+    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, CWN, C::OCC, MX, C::KH, C::NS, C::PER>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
@@ -434,6 +506,14 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     const size_t lds = ring + (MX ? (size_t)CBN * prm.K / 32 : 0);
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
+    if (C::PER) {
+        // one work-group per CU (the ring takes most of a CU's LDS), a multiple of the XCD count
+        int dev = 0, cus = 0;
+        hipError_t r = hipGetDevice(&dev);
+        if (r == hipSuccess) r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (r != hipSuccess) return r;
+        nblk = std::min(nblk, std::max(NXCD, cus / NXCD * NXCD));
+    }
     if (ev0 || ev1)
         hipExtLaunchKernelGGL(kern, dim3(nblk), dim3(C::NTH), lds, st, ev0, ev1, 0, prm);
     else
