@@ -527,6 +527,21 @@ def test_forward_grouped_wide_tiles_ragged(T, H, E, K, I, beta):
     compare_forward(li, got, label=f"grouped wide T={T}")
 
 
+def test_forward_grouped_wide_persistent_tiles():
+    """2048 tokens on the large-tile kernels: the gate/up grid holds one work-group per CU
+    and each walks four or five of the ~1100 tiles, so the next-tile prefetch and the hand
+    over of ring slots under the epilogue run many times.  Ids everywhere, y on a token
+    sample spanning the chunk."""
+    sh_ = synth.Shape(2048, 512, 16, 8, 1024, "bf16", "bf16", bias="zipf")
+    li = synth.make_layer(sh_, beta=1.0)
+    note("grouped wide persistent T=2048 H=512 E=16 K=8 I=1024")
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    ref = oracle.router(oracle_layer(li))
+    mism = (got["ids"] != ref["ids"]).any(1)
+    assert not (mism & ~ref["near"]).any()
+    compare_forward(li, got, tokens=_sample(2048, 96), label="grouped wide persistent")
+
+
 @pytest.mark.parametrize("T,H,E,K,I", [(300, 1024, 32, 4, 512), (160, 2048, 16, 8, 1024)])
 def test_forward_grouped_wide_tiles_mxfp4(T, H, E, K, I):
     """MXFP4 experts on the large-tile kernels (codes and scales loaded straight into LDS,
