@@ -295,7 +295,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     for (int st = 0; st < NS; ++st) issue(min(st, NST - 1), st);
     wait_vm<(NS - 1) * LOADS>();
     barrier_nofence();
-    read_ops(0, 0, C0{});
+    if (wm * RW < m_end - m0) read_ops(0, 0, C0{});
 
     // A step consumes the operands of one 32-deep K slice from register buffer `cur`
     // and reads the next slice's into the other buffer.  A step that ends a stage (every
@@ -312,11 +312,14 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     // reads again, which keeps the step branch-free.
     constexpr int NMF = MI * NJ, NRD = MX ? 2 * MI + 3 * NJ : 2 * (MI + NJ);
     constexpr int VPM = (LOADS + NMF - 1) / NMF;   // refill loads placed per MFMA
-    auto step = [&](int kt, int st, auto cur_c, auto ends_c, auto vm_c, auto refill_c) WG_INLINE {
+    // ACT: the wave has rows of the tile's expert; a wave past the expert's last row only
+    // loads its share of the stages and takes the barriers.
+    auto step = [&](int kt, int st, auto cur_c, auto ends_c, auto vm_c, auto refill_c, auto act_c) WG_INLINE {
         using Next = std::integral_constant<int, 1 - decltype(cur_c)::value>;
         constexpr bool ends = decltype(ends_c)::value;
         constexpr bool refill = ends && decltype(refill_c)::value;
-        mfma_sub(cur_c, C0{});
+        constexpr bool act = decltype(act_c)::value;
+        if constexpr (act) mfma_sub(cur_c, C0{});
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (ends) {
             wait_vm<decltype(vm_c)::value>();
@@ -324,10 +327,11 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
             barrier_nofence();
             __builtin_amdgcn_sched_barrier(0);
             if (refill) issue(min(st + NS, NST - 1), st % NS);
-            read_ops(kt + 1, (st + 1) % NS, Next{});
+            if constexpr (act) read_ops(kt + 1, (st + 1) % NS, Next{});
         } else {
-            read_ops(kt + 1, st % NS, Next{});
+            if constexpr (act) read_ops(kt + 1, st % NS, Next{});
         }
+        if constexpr (!act) return;
         mfma_sub(cur_c, C1{});
 #pragma unroll
         for (int q = 0; q < NMF; ++q) {
@@ -360,23 +364,31 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-        if constexpr (KH == 1) {
-            for (int kt = 0; kt < NST - 2; kt += 2) {
-                step(kt, kt, C0{}, T{}, VL{}, T{});
-                step(kt + 1, kt + 1, C1{}, T{}, VL{}, T{});
+        auto kloop = [&](auto a) WG_INLINE {
+            if constexpr (KH == 1) {
+                for (int kt = 0; kt < NST - 2; kt += 2) {
+                    step(kt, kt, C0{}, T{}, VL{}, T{}, a);
+                    step(kt + 1, kt + 1, C1{}, T{}, VL{}, T{}, a);
+                }
+                step(NST - 2, NST - 2, C0{}, T{}, V0{}, F{}, a);
+            } else {
+                for (int st = 0; st < NST - 2; ++st) {
+                    step(2 * st, st, C0{}, F{}, V0{}, F{}, a);
+                    step(2 * st + 1, st, C1{}, T{}, VL{}, T{}, a);
+                }
+                step(2 * NST - 4, NST - 2, C0{}, F{}, V0{}, F{}, a);
+                step(2 * NST - 3, NST - 2, C1{}, T{}, V0{}, F{}, a);
+                step(2 * NST - 2, NST - 1, C0{}, F{}, V0{}, F{}, a);
             }
-            step(NST - 2, NST - 2, C0{}, T{}, V0{}, F{});
-        } else {
-            for (int st = 0; st < NST - 2; ++st) {
-                step(2 * st, st, C0{}, F{}, V0{}, F{});
-                step(2 * st + 1, st, C1{}, T{}, VL{}, T{});
+            if constexpr (decltype(a)::value) {
+                mfma_sub(C1{}, C0{});
+                mfma_sub(C1{}, C1{});
             }
-            step(2 * NST - 4, NST - 2, C0{}, F{}, V0{}, F{});
-            step(2 * NST - 3, NST - 2, C1{}, T{}, V0{}, F{});
-            step(2 * NST - 2, NST - 1, C0{}, F{}, V0{}, F{});
-        }
-        mfma_sub(C1{}, C0{});
-        mfma_sub(C1{}, C1{});
+        };
+        if (wm * RW < m_end - m0)
+            kloop(T{});
+        else
+            kloop(F{});
 
         // ---- epilogue: each wave transposes its tile through LDS (its own region) and
         // stores whole 16-byte row pieces.  All waves are past their last LDS operand read
@@ -464,7 +476,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
         wait_lgkm0();
         barrier_nofence();
         issue(min(2, NST - 1), 2);
-        read_ops(0, 0, C0{});
+        if (wm * RW < m_end - m0) read_ops(0, 0, C0{});
     }
 }
 
