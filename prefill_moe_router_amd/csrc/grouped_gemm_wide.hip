@@ -7,14 +7,16 @@
 //
 // Design for gfx950:
 //  * A work-group owns a 128-row m-tile of one expert and 256 weight rows (GATEUP: 128
-//    intermediate columns of both gate and up; DOWN: 256 output columns).  DOWN: 2 x 2
-//    waves of 64 rows x 128 weight rows, i.e. 8 independent 32x32 MFMA accumulators
-//    (128 registers), so one 16-deep K slice moves 6 KB of operands out of LDS per 8
-//    MFMAs; 72 KB of LDS and <= 256 registers per lane let two work-groups share a
-//    CU, so one group's tile start (metadata loads, pipeline fill) and epilogue hide
-//    under the other's MFMAs.  GATEUP: 4 x 2 waves of 32 x 128 in one persistent
-//    work-group per CU, with 64-deep stages (below); it fetches each next tile's rows
-//    under the K loop and its first stages under the epilogue.
+//    intermediate columns of both gate and up; DOWN: 256 output columns).  bf16: 4 x 2
+//    waves of 32 rows x 128 weight rows (4 independent 32x32 MFMA accumulators) in one
+//    persistent work-group per CU, with 64-deep stages (below); it fetches each next
+//    tile's rows under the K loop and its first stages under the epilogue.  MXFP4 down:
+//    2 x 2 waves of 64 x 128 (8 accumulators, 128 registers), 72 KB of LDS, so two
+//    work-groups share a CU and one group's tile start and epilogue hide under the
+//    other's MFMAs.
+//  * A wave whose rows all lie past the expert's last row (the tail m-tile of an expert)
+//    skips its operand reads and MFMAs; it still issues its share of the stage loads and
+//    takes every barrier, so the wait counts hold.
 //  * Each m-tile's rows come from a tile table the grouping writes ({first row, end
 //    row, expert} per tile): one load, no search over the m-tile offsets.
 //  * Operands go from global memory straight into LDS (global_load_lds_dwordx4: no
@@ -437,32 +439,40 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
                 *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
             }
         } else {
-            // wave's o' tile: RW rows x 128 columns, in passes of 32 rows
+            // wave's o' tile: RW rows x 128 columns, in passes of PR rows (16 when the
+            // epilogue shares the ring with the next tile's loads: a third of it)
             constexpr int PITCH = 128 + 8;
-            uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * 32 * PITCH;
+            constexpr int PR = PER ? 16 : 32;
+            uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * PR * PITCH;
             const int col0 = n_tile * BN + WROWS * wn;
-    #pragma unroll
+#pragma unroll
             for (int i = 0; i < MI; ++i) {
-    #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int ml = 8 * (r >> 2) + 4 * hh + (r & 3);
-    #pragma unroll
-                    for (int j = 0; j < NJ; ++j) ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+#pragma unroll
+                for (int h = 0; h < 32 / PR; ++h) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int ml = 8 * (r >> 2) + 4 * hh + (r & 3);   // ml / PR depends on r only
+                        if ((8 * (r >> 2)) / PR != h) continue;
+#pragma unroll
+                        for (int j = 0; j < NJ; ++j)
+                            ep[(ml - h * PR) * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+                    }
+                    wait_lgkm0();
+                    __builtin_amdgcn_wave_barrier();
+                    for (int q = lane; q < PR * 16; q += 64) {
+                        const int ml = q >> 4, ch = q & 15;
+                        const int m = wm * RW + 32 * i + h * PR + ml;
+                        if (m0 + m >= m_end) continue;
+                        const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
+                        *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[sb][m] * p.N +
+                                                     col0 + ch * 8) = v;
+                    }
+                    wait_lgkm0();
+                    __builtin_amdgcn_wave_barrier();
                 }
-                wait_lgkm0();
-                __builtin_amdgcn_wave_barrier();
-                for (int q = lane; q < 32 * 16; q += 64) {
-                    const int ml = q >> 4, ch = q & 15;
-                    const int m = wm * RW + 32 * i + ml;
-                    if (m0 + m >= m_end) continue;
-                    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
-                    *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)s_slot[sb][m] * p.N + col0 +
-                                                 ch * 8) = v;
-                }
-                wait_lgkm0();
-                __builtin_amdgcn_wave_barrier();
             }
         }
+
         if (!PER || !have_next) break;
         // the next tile: its stages 0 and 1 landed (vm 0 also retires the epilogue's stores),
         // every wave is past the epilogue's use of slot 2, which now takes stage 2
@@ -482,19 +492,20 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
 
 namespace {
 
-// the configurations the launchers use, per GEMM (the 8192-token chunk, H=2048, E=128,
-// k=8, I=768, same-box A/B):
-//  * bf16 gate/up: 4 x 2 waves (32 x 128 per wave, 128 x 256 per work-group), stages of
-//    64 K elements (whole-line rows), 3 of them (144 KB), one persistent work-group per CU;
-//  * down (bf16 and MXFP4): 2 x 2 waves (64 x 128 per wave), stages of 32 K elements,
-//    3 of them (72 KB; MXFP4 codes of a B row are 16 bytes per step either way), two
+// the configurations the launchers use (the 8192-token chunk, H=2048, E=128, k=8, I=768,
+// same-box A/B):
+//  * bf16 gate/up and down: 4 x 2 waves (32 x 128 per wave, 128 x 256 per work-group),
+//    stages of 64 K elements (whole-line rows), 3 of them (144 KB), one persistent
+//    work-group per CU;
+//  * MXFP4 down: 2 x 2 waves (64 x 128 per wave), stages of 32 K elements (the codes of a
+//    B row are 16 bytes per step either way), 3 of them (72 KB with the scale table), two
 //    work-groups per CU.
 constexpr int CWN = 2, CBN = CWN * WROWS;
 constexpr int MX_MAX_K = 4096;   // MXFP4: the tile's scale table (CBN x K/32 bytes) stays <= 32 KB
 
 template <int MODE, bool MX>
 struct WideCfg {
-    static constexpr bool wide_stage = MODE == WG_GATEUP && !MX;
+    static constexpr bool wide_stage = !MX;
     static constexpr int WM = wide_stage ? 4 : 2, KH = wide_stage ? 2 : 1, NS = 3, OCC = wide_stage ? 1 : 2;
     static constexpr bool PER = wide_stage;
     static constexpr int NTH = WM * CWN * 64;
