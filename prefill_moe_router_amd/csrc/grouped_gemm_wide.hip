@@ -47,9 +47,12 @@ constexpr int NXCD = 8;
 constexpr int BM = 128;                 // rows per m-tile (the grouping's tile)
 constexpr int WROWS = 128;              // weight rows per wave
 constexpr int BK = 32;                  // K elements of one step (two 16-deep MFMA slices)
-constexpr int GM = 8;                   // m-tiles per group of the tile order
-
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
+
+// m-tiles per group of the tile order.  Measured on the 8192-token chunk (bf16, same-box
+// rounds of 4 / 8 / 16 / 32): gate/up 546-553 us at 4 against 555-559 at 8, down
+// 325.5-326.3 us at 16 against 327.3-329.2 at 8; MXFP4 down keeps 8.
+constexpr int group_m(int mode, bool mx) { return mx ? 8 : mode == WG_GATEUP ? 4 : 16; }
 
 
 struct WideParams {
@@ -119,6 +122,7 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     __shared__ int s_slot[PER ? 2 : 1][BM];
     __shared__ float s_scale[BM];
 
+    constexpr int GM = group_m(MODE, MX);
     // ---- which tile: groups of GM m-tiles swept n-tile by n-tile (the last group holds
     // the remaining m-tiles), each XCD a contiguous, equal share of that order (blocks are
     // dealt to XCDs round-robin).  The share comes from the tile count the grouping wrote,
@@ -527,6 +531,7 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
         attr_done = true;
     }
     const size_t lds = ring + (MX ? (size_t)CBN * prm.K / 32 : 0);
+    constexpr int GM = group_m(MODE, MX);
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
     if (C::PER) {
