@@ -80,12 +80,12 @@ moe_status check_path(const moe_shape *s) {
 bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 
 // AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
-// experts, four with MXFP4 / NVFP4 (whose streaming kernels read a quarter of the bytes); measured
-// crossovers on the decode shapes: bf16 T = 24..32 (k = 8, E = 128), MXFP4 above T = 64
-// (k = 8, E = 256)
+// experts, three with MXFP4 and four with NVFP4 (whose streaming kernels read a quarter of the
+// bytes); measured crossovers on the decode shapes: bf16 T = 24..32 (k = 8, E = 128), MXFP4
+// T = 64..96 (k = 8, E = 256: 661 / 701 us streaming / grouped at 64, 802 / 734 at 96)
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : 4L;
+    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : s.weight_dtype == MOE_MXFP4 ? 3L : 4L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
            (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
 }

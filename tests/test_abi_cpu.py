@@ -102,7 +102,7 @@ def test_forward_validation():
 
 def test_nvfp4_validation():
     """NVFP4 experts: scale arrays required and 2-byte aligned, finite tensor scales; AUTO
-    takes the grouped GEMMs from four pairs per expert as for MXFP4."""
+    takes the grouped GEMMs from four pairs per expert (MXFP4: three)."""
     L = pm.lib()
     shp = _shape(weight_dtype=pm.NVFP4)
     s = shp.c()
@@ -116,6 +116,10 @@ def test_nvfp4_validation():
     # E = 128, k = 8: streaming below 64 tokens, grouped from 64
     for T, grouped in ((9, False), (63, False), (64, True), (4096, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.NVFP4, num_tokens=T))
+        assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
+    # MXFP4 switches at three pairs per expert: 48 tokens at E = 128, k = 8
+    for T, grouped in ((47, False), (48, True)):
+        stages = pm.forward_stages(_shape(weight_dtype=pm.MXFP4, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     # with fp32 activations NVFP4 is not a supported pair
     assert pm.workspace_size(_shape(weight_dtype=pm.NVFP4, act_dtype=pm.F32)) == 0
