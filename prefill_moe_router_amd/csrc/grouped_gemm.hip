@@ -414,13 +414,23 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
     const int n8 = (blockIdx.y * blockDim.x + threadIdx.x) * 8;
     if (t >= T || n8 >= H) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-        const uint4 v = *reinterpret_cast<const uint4 *>(o + ((size_t)t * k + j) * H + n8);
+    auto add = [&](const uint4 v) {
         acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
         acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
         acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);
         acc[6] += bf16_lo(v.w); acc[7] += bf16_hi(v.w);
+    };
+    // the token's k rows are contiguous; up to eight loads in flight, summed in j order
+    const uint16_t *src = o + (size_t)t * k * H + n8;
+    int j = 0;
+    for (; j + 8 <= k; j += 8) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const uint4 *>(src + (size_t)(j + u) * H);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) add(v[u]);
     }
+    for (; j < k; ++j) add(*reinterpret_cast<const uint4 *>(src + (size_t)j * H));
     uint4 r;
     r.x = pack_bf16x2(acc[0], acc[1]);
     r.y = pack_bf16x2(acc[2], acc[3]);
