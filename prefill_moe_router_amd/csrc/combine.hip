@@ -17,15 +17,32 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
     const int n4 = (blockIdx.y * blockDim.x + threadIdx.x) * 4;
     if (t >= T || n4 >= H) return;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int pos = slot_pos[(size_t)t * k + j];
-        if (pos < 0) continue;
-        const float wj = w[(size_t)t * k + j];
-        const float4 v = *reinterpret_cast<const float4 *>(o + (size_t)pos * H + n4);
+    auto fma4 = [&](float wj, const float4 v) {
         acc.x = fmaf(wj, v.x, acc.x);
         acc.y = fmaf(wj, v.y, acc.y);
         acc.z = fmaf(wj, v.z, acc.z);
         acc.w = fmaf(wj, v.w, acc.w);
+    };
+    // up to eight rows in flight, summed in j order; a slot left out of the grouping
+    // (pos < 0, a bad expert id) adds nothing
+    const int32_t *sp = slot_pos + (size_t)t * k;
+    const float *wt = w + (size_t)t * k;
+    int j = 0;
+    for (; j + 8 <= k; j += 8) {
+        int pos[8];
+        float4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) pos[u] = sp[j + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)   // row 0 stands in for a left-out slot (not added)
+            v[u] = *reinterpret_cast<const float4 *>(o + (size_t)max(pos[u], 0) * H + n4);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (pos[u] >= 0) fma4(wt[j + u], v[u]);
+    }
+    for (; j < k; ++j) {
+        const int pos = sp[j];
+        if (pos >= 0) fma4(wt[j], *reinterpret_cast<const float4 *>(o + (size_t)pos * H + n4));
     }
     if (act_f32) {
         *reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + (size_t)t * H + n4) = acc;
