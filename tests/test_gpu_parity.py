@@ -248,19 +248,25 @@ def test_staged_pipeline_parity(name):
     compare_forward(li, dict(y=y, ids=gids, w=w.cpu().numpy()), label=f"staged {name}")
 
 
-def test_combine_parity_random():
-    T, H, K = 37, 512, 5
+@pytest.mark.parametrize("K", [5, 10])
+def test_combine_parity_random(K):
+    """Random rows and weights; K = 10 takes a batch of eight rows and a tail of two.  A few
+    slots are left out of the grouping (slot_pos -1, as for a bad expert id) and add
+    nothing."""
+    T, H = 37, 512
     rng = np.random.default_rng(11)
     o = rng.standard_normal((T * K, H)).astype(np.float32)
     w = rng.random((T, K)).astype(np.float32)
     perm = rng.permutation(T * K).astype(np.int32)
+    perm[[3, 2 * K + K - 1, 5 * K + 4]] = -1
     sh = pm.LayerShape(T, H, 16, K, 64, act_dtype=pm.BF16, weight_dtype=pm.BF16)
     y = torch.empty(T, H, dtype=torch.int16, device="cuda")
     pm.combine(sh, tdev(o), tdev(w), tdev(perm), y)
     ref = np.zeros((T, H))
     for t in range(T):
         for j in range(K):
-            ref[t] += np.float64(w[t, j]) * o[perm[t * K + j]]
+            if perm[t * K + j] >= 0:
+                ref[t] += np.float64(w[t, j]) * o[perm[t * K + j]]
     yg = to_f64(y, "bf16")
     assert np.all(np.abs(yg - ref) <= np.abs(ref) * 2.0 ** -8 + 1e-6)
 
@@ -525,6 +531,15 @@ def test_forward_grouped_wide_tiles_ragged(T, H, E, K, I, beta):
     counts = np.bincount(got["ids"].ravel(), minlength=E)
     note(f"  group sizes max {counts.max()} empty {(counts == 0).sum()}")
     compare_forward(li, got, label=f"grouped wide T={T}")
+
+
+def test_forward_grouped_top10():
+    """k = 10 on the grouped path: the combine of each token's rows takes a batch of eight and
+    a tail of two."""
+    sh_ = synth.Shape(100, 512, 32, 10, 256, "bf16", "bf16", bias="normal")
+    li = synth.make_layer(sh_)
+    got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
+    compare_forward(li, got, label="grouped top-10")
 
 
 def test_forward_grouped_wide_persistent_tiles():
