@@ -7,8 +7,9 @@
 //
 // Design for gfx950:
 //  * A work-group owns a 128-row m-tile of one expert and 256 weight rows (GATEUP: 128
-//    intermediate columns of both gate and up; DOWN: 256 output columns).  bf16: 4 x 2
-//    waves of 32 rows x 128 weight rows (4 independent 32x32 MFMA accumulators) in one
+//    intermediate columns of both gate and up; DOWN: 256 output columns).  bf16: 2 x 4
+//    waves of 64 rows x 64 weight rows (4 independent 32x32 MFMA accumulators; a 16-deep
+//    K slice reads 4 KB of operands from LDS per 4 MFMAs, against 5 KB for 32 x 128) in one
 //    persistent work-group per CU, with 64-deep stages (below); it fetches each next
 //    tile's rows under the K loop and its first stages under the epilogue.  MXFP4 down:
 //    2 x 2 waves of 64 x 128 (8 accumulators, 128 registers), 72 KB of LDS, so two
@@ -45,7 +46,7 @@ namespace {
 
 constexpr int NXCD = 8;
 constexpr int BM = 128;                 // rows per m-tile (the grouping's tile)
-constexpr int WROWS = 128;              // weight rows per wave
+constexpr int TBN = 256;                // weight rows per n-tile (all configurations)
 constexpr int BK = 32;                  // K elements of one step (two 16-deep MFMA slices)
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
 
@@ -107,7 +108,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     static_assert(KH == 1 || (KH == 2 && !MX), "two-step stages are for bf16 weights");
     static_assert(NS >= 2, "at least two stages");
     static_assert(!PER || (NS == 3 && WM * WN * 64 >= BM), "persistent: three slots, a thread per tile row");
-    constexpr int BN = WN * WROWS;                   // weight rows per n-tile
+    constexpr int WROWS = TBN / WN;                  // weight rows per wave
+    constexpr int BN = TBN;                          // weight rows per n-tile
     constexpr int RW = BM / WM;                      // rows per wave
     constexpr int MI = RW / 32, NJ = WROWS / 32;     // 32x32 blocks per wave
     constexpr int ROWB = 64 * KH;                    // bytes of one staged bf16 row
@@ -173,17 +175,17 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
     // chunk slot l % LPR, which holds the row's logical chunk (l % LPR) ^ swz(row).
     constexpr int RPL = 1024 / ROWB;               // rows per wave-wide load
     const int lrow = lane / LPR;
-    // B: LDS row q of the tile belongs to wave q / 128.  GATEUP: rows 0-63 of a wave's
-    // range are gate columns c0 + 64 * (q / 128) + (0..63), rows 64-127 the same up
-    // columns (c0 = the n-tile's first intermediate column).  DOWN: output column
-    // n0 + q.
+    // B: LDS row q of the tile belongs to the waves of column wn = q / WROWS.  GATEUP: the
+    // first half of a wave's range is gate columns c0 + (WROWS / 2) * wn + (0 .. WROWS/2-1),
+    // the second half the same up columns (c0 = the n-tile's first intermediate column).
+    // DOWN: output column n0 + q.
     // global weight row of LDS B row r of n-tile nt_ of expert e_, and whether it belongs
     // to the second matrix (up)
     auto brow_of = [&](int r, bool &second, int e_, int nt_) WG_INLINE {
         if (MODE == WG_GATEUP) {
             const int rl = r % WROWS;
-            second = rl >= 64;
-            return (size_t)e_ * p.N + (size_t)nt_ * NCOL + 64 * (r / WROWS) + (rl & 63);
+            second = rl >= WROWS / 2;
+            return (size_t)e_ * p.N + (size_t)nt_ * NCOL + (WROWS / 2) * (r / WROWS) + ((unsigned)rl % (WROWS / 2));
         }
         second = false;
         return (size_t)e_ * p.N + (size_t)nt_ * BN + r;
@@ -419,8 +421,10 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
         }
         // acc[i][j][r] holds C[row][col], row = 32i + 8(r/4) + 4(lane/32) + r%4, col = 32j + lane%32
         if (MODE == WG_GATEUP) {
-            // wave's h' tile: RW rows x 64 columns (gate blocks j = 0, 1 pair with up blocks 2, 3)
-            constexpr int PITCH = 64 + 8;   // bf16 elements per transposed row
+            // wave's h' tile: RW rows x HC columns (gate blocks j < NJ / 2 pair with up blocks
+            // NJ / 2 + j)
+            constexpr int HC = WROWS / 2, CPR = HC / 8;
+            constexpr int PITCH = HC + 8;   // bf16 elements per transposed row
             uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * RW * PITCH;
     #pragma unroll
             for (int i = 0; i < MI; ++i)
@@ -429,23 +433,24 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
                     const int ml = 32 * i + 8 * (r >> 2) + 4 * hh + (r & 3);
                     const float sc = s_scale[wm * RW + ml];
     #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        ep[ml * PITCH + 32 * j + lr] = (uint16_t)f32_to_bf16_rne(sc * swiglu(acc[i][j][r], acc[i][2 + j][r]));
+                    for (int j = 0; j < NJ / 2; ++j)
+                        ep[ml * PITCH + 32 * j + lr] =
+                            (uint16_t)f32_to_bf16_rne(sc * swiglu(acc[i][j][r], acc[i][NJ / 2 + j][r]));
                 }
             wait_lgkm0();
             __builtin_amdgcn_wave_barrier();
-            const int col0 = n_tile * NCOL + 64 * wn;
-            for (int q = lane; q < RW * 8; q += 64) {
-                const int ml = q >> 3, ch = q & 7;
+            const int col0 = n_tile * NCOL + HC * wn;
+            for (int q = lane; q < RW * CPR; q += 64) {
+                const int ml = (unsigned)q / CPR, ch = (unsigned)q % CPR;
                 const int m = wm * RW + ml;
                 if (m0 + m >= m_end) continue;
                 const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
                 *reinterpret_cast<u32x4_t *>(reinterpret_cast<uint16_t *>(p.out) + (size_t)(m0 + m) * p.N + col0 + ch * 8) = v;
             }
         } else {
-            // wave's o' tile: RW rows x 128 columns, in passes of PR rows (16 when the
+            // wave's o' tile: RW rows x WROWS columns, in passes of PR rows (16 when the
             // epilogue shares the ring with the next tile's loads: a third of it)
-            constexpr int PITCH = 128 + 8;
+            constexpr int PITCH = WROWS + 8, CPR = WROWS / 8;
             constexpr int PR = PER ? 16 : 32;
             uint16_t *ep = reinterpret_cast<uint16_t *>(epi) + wave * PR * PITCH;
             const int col0 = n_tile * BN + WROWS * wn;
@@ -463,8 +468,8 @@ __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(Wi
                     }
                     wait_lgkm0();
                     __builtin_amdgcn_wave_barrier();
-                    for (int q = lane; q < PR * 16; q += 64) {
-                        const int ml = q >> 4, ch = q & 15;
+                    for (int q = lane; q < PR * CPR; q += 64) {
+                        const int ml = (unsigned)q / CPR, ch = (unsigned)q % CPR;
                         const int m = wm * RW + 32 * i + h * PR + ml;
                         if (m0 + m >= m_end) continue;
                         const u32x4_t v = *reinterpret_cast<const u32x4_t *>(ep + ml * PITCH + ch * 8);
@@ -498,21 +503,22 @@ namespace {
 
 // the configurations the launchers use (the 8192-token chunk, H=2048, E=128, k=8, I=768,
 // same-box A/B):
-//  * bf16 gate/up and down: 4 x 2 waves (32 x 128 per wave, 128 x 256 per work-group),
+//  * bf16 gate/up and down: 2 x 4 waves (64 x 64 per wave, 128 x 256 per work-group),
 //    stages of 64 K elements (whole-line rows), 3 of them (144 KB), one persistent
 //    work-group per CU;
 //  * MXFP4 down: 2 x 2 waves (64 x 128 per wave), stages of 32 K elements (the codes of a
 //    B row are 16 bytes per step either way), 3 of them (72 KB with the scale table), two
 //    work-groups per CU.
-constexpr int CWN = 2, CBN = CWN * WROWS;
+constexpr int CBN = TBN;
 constexpr int MX_MAX_K = 4096;   // MXFP4: the tile's scale table (CBN x K/32 bytes) stays <= 32 KB
 
 template <int MODE, bool MX>
 struct WideCfg {
     static constexpr bool wide_stage = !MX;
-    static constexpr int WM = wide_stage ? 4 : 2, KH = wide_stage ? 2 : 1, NS = 3, OCC = wide_stage ? 1 : 2;
+    static constexpr int WM = 2, KH = wide_stage ? 2 : 1, NS = 3, OCC = wide_stage ? 1 : 2;
     static constexpr bool PER = wide_stage;
-    static constexpr int NTH = WM * CWN * 64;
+    static constexpr int WN = wide_stage ? 4 : 2;
+    static constexpr int NTH = WM * WN * 64;
 };
 
 template <int MODE, bool MX>
@@ -523,7 +529,7 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
     static_assert(lds_max <= 160 * 1024 - 2048, "LDS ring too large");
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, CWN, C::OCC, MX, C::KH, C::NS, C::PER>;
+    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, C::WN, C::OCC, MX, C::KH, C::NS, C::PER>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
