@@ -49,10 +49,10 @@ COUNTED_TRAFFIC = {
                     write_scale=1.0, sources={
                         "prefill_moe_router_amd/csrc/decode_fused.hip": "2eca5cb8dc38ff70a79a81ab942a99ce7feffdad",
                         "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
-    "prefill8192": dict(kernel="gate_up", fetch_kib=1075870.3, write_kib=98304.0, fetch_scale=2.0,
+    "prefill8192": dict(kernel="gate_up", fetch_kib=1045638.3, write_kib=98308.9, fetch_scale=2.0,
                         write_scale=1.0, sources={
                             "prefill_moe_router_amd/csrc/grouped_gemm_wide.hip":
-                                "657d8c9b4b248dba054ad2214233dc422745a385",
+                                "184620b7f66e1d476dfca39d16d3330072077942",
                             "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
 }
 
