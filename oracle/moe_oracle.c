@@ -97,6 +97,20 @@ double orc_decode_e4m3(uint8_t code)
     return s ? -v : v;
 }
 
+/* Every code's value, looked up per element instead of decoded again: entry c is
+ * exactly what the decoder above returns for code c, so the lookups change no value
+ * (they only spare the per-element ldexp calls of the 4-bit formats). */
+static double tab_e2m1[16], tab_e8m0[256], tab_e4m3[256];
+
+static void fill_code_tables(void)
+{
+    for (unsigned c = 0; c < 16; ++c) tab_e2m1[c] = orc_decode_e2m1(c);
+    for (unsigned c = 0; c < 256; ++c) {
+        tab_e8m0[c] = orc_decode_e8m0((uint8_t)c);
+        tab_e4m3[c] = orc_decode_e4m3((uint8_t)c);
+    }
+}
+
 static double act_at(const orc_layer *L, const void *base, size_t idx)
 {
     if (L->act_dtype == ORC_F32) return (double)((const float *)base)[idx];
@@ -114,9 +128,9 @@ static double wt_at(const orc_layer *L, const void *w, const uint8_t *s, double 
     uint8_t byte = ((const uint8_t *)w)[row * (cols / 2) + col / 2];
     unsigned code = (col & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
     if (L->w_dtype == ORC_NVFP4) /* one E4M3 scale per 16 elements, then the tensor scale */
-        return orc_decode_e2m1(code) * orc_decode_e4m3(s[row * (cols / 16) + col / 16]) * ts;
+        return tab_e2m1[code] * tab_e4m3[s[row * (cols / 16) + col / 16]] * ts;
     /* MXFP4: one E8M0 scale per 32 consecutive elements of a row */
-    return orc_decode_e2m1(code) * orc_decode_e8m0(s[row * (cols / 32) + col / 32]);
+    return tab_e2m1[code] * tab_e8m0[s[row * (cols / 32) + col / 32]];
 }
 
 /* ---- a1: router logits -------------------------------------------------- */
@@ -275,6 +289,7 @@ static void expert_apply(const orc_layer *L, int t, int e, double *o, double *a)
 int orc_expert_pairs(const orc_layer *L, const int32_t *tok, const int32_t *exp_id, int npairs, double *o)
 {
     int err = 0;
+    fill_code_tables();
 #pragma omp parallel for schedule(dynamic)
     for (int p = 0; p < npairs; ++p) {
         if (tok[p] < 0 || tok[p] >= L->T || exp_id[p] < 0 || exp_id[p] >= L->E) { err = -1; continue; }
@@ -299,6 +314,7 @@ int orc_forward(const orc_layer *L, const int32_t *tokens, int n, const int32_t 
 {
     int err = orc_router(L, tokens, n, NULL, ids, w, near, gap);
     if (err) return err;
+    fill_code_tables();
     const int H = L->H, E = L->E, k = L->K;
     if (forced_ids) {
         for (int r = 0; r < n; ++r)
