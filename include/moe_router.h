@@ -16,8 +16,15 @@
  * Conventions shared by every call
  *   - Pointers are device pointers unless stated otherwise; the caller owns
  *     every buffer, including the workspace.  The library allocates nothing
- *     and keeps no global state; calls on different workspaces may run
- *     concurrently.
+ *     and keeps no global state.  Calls on different workspaces may run
+ *     concurrently, with one exception: the single-launch decode path
+ *     (moe_forward_stages == "decode_fused", T <= 8) needs one work-group
+ *     resident on every compute unit at once, because its work-groups wait
+ *     for one another.  It checks at launch that one of its work-groups fits
+ *     a compute unit (and runs the staged decode kernels when it does not),
+ *     but it cannot see other kernels: a call that overlaps with other work
+ *     holding compute units may let its bounded waits expire, which sets
+ *     MOE_DEVERR_TIMEOUT (moe_check_device_error) and leaves y invalid.
  *   - Every call only enqueues work on `stream` (a hipStream_t; NULL is the
  *     default stream).  No call synchronises or reads device memory on the
  *     host, except moe_check_device_error, which says so.
@@ -28,9 +35,11 @@
  *     even element in the low nibble) with one E8M0 scale byte per 32
  *     consecutive contraction elements.
  *   - Device pointers must be 16-byte aligned.
- *   - The workspace must be zero-filled before its first use.  Every call
- *     leaves its control words zero again; only the sticky device error
- *     word (cleared by moe_check_device_error) can remain set.
+ *   - The workspace must be zero-filled before its first use.  Zero-filling
+ *     it whole again between calls is allowed; clearing parts of it is not:
+ *     the decode path keeps a call counter in its control words across calls
+ *     (it only grows), and the words it publishes carry that count.  The
+ *     sticky device error word (byte 0) is cleared by moe_check_device_error.
  */
 #ifndef MOE_ROUTER_H
 #define MOE_ROUTER_H
@@ -171,6 +180,23 @@ moe_status moe_forward_timed(const moe_shape *shape, const void *x, const void *
                              const float *bias, const moe_expert_weights *w, void *y,
                              int32_t *topk_ids_out, float *topk_w_out, void *ws, size_t ws_bytes,
                              void *stream, void *const *stage_events, int32_t n_stage_events);
+
+/*
+ * The token->expert grouping that the last moe_forward (or moe_forward_timed) on
+ * this workspace built on the device, copied into the caller's buffers on
+ * `stream`: expert_offsets [E+1], sorted_slots [T*k] and slot_pos [T*k], as
+ * moe_group_tokens defines them, for the ids that call routed.  It lets a caller
+ * check the whole-layer call's own grouping output for output against a
+ * reference ("第 9 章 prefill：最大的瓶颈" §9.9: a switch of numeric path is
+ * checked against the old path's outputs).  Shapes whose moe_forward groups on
+ * chip without storing the grouping (the single-launch decode path,
+ * moe_forward_stages == "decode_fused") give MOE_ERR_UNSUPPORTED.  `ws` must be
+ * the workspace of that call, with the same shape; nothing is checked about
+ * whether a call ran.  Enqueues three device-to-device copies.
+ */
+moe_status moe_forward_grouping(const moe_shape *shape, const void *ws, size_t ws_bytes,
+                                int32_t *expert_offsets, int32_t *sorted_slots, int32_t *slot_pos,
+                                void *stream);
 
 /* Comma-separated names of the kernel launches moe_forward makes for `shape`,
  * in order (static string; "" for an invalid shape). */

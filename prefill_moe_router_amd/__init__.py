@@ -31,8 +31,8 @@ PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 DEVERR_BAD_EXPERT_ID, DEVERR_TIMEOUT = 1, 2
 
 EXPORTS = ["moe_workspace_size", "moe_router_topk", "moe_group_tokens", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_forward_timed", "moe_forward_stages", "moe_check_device_error",
-           "moe_status_string"]
+           "moe_forward", "moe_forward_timed", "moe_forward_stages", "moe_forward_grouping",
+           "moe_check_device_error", "moe_status_string"]
 
 
 class MoeError(RuntimeError):
@@ -81,6 +81,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.argtypes = [PS, vp, vp, vp, PW, vp, vp, vp, vp, sz, vp, ctypes.POINTER(vp), i32]
         L.moe_forward_stages.restype = ctypes.c_char_p
         L.moe_forward_stages.argtypes = [PS]
+        L.moe_forward_grouping.restype = i32
+        L.moe_forward_grouping.argtypes = [PS, vp, sz, vp, vp, vp, vp]
         L.moe_check_device_error.restype = i32
         L.moe_check_device_error.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -196,6 +198,13 @@ def forward_timed(shape: LayerShape, x, w_router, bias, weights: dict, y, ws, st
 def forward_stages(shape: LayerShape) -> list:
     s = shape.c()
     return lib().moe_forward_stages(ctypes.byref(s)).decode().split(",")
+
+
+def forward_grouping(shape: LayerShape, ws, expert_offsets, sorted_slots, slot_pos, stream=None):
+    """Copies the grouping the last forward on `ws` built into the given int32 tensors."""
+    s = shape.c()
+    _check(lib().moe_forward_grouping(ctypes.byref(s), _p(ws), ws.numel(), _p(expert_offsets), _p(sorted_slots),
+                                      _p(slot_pos), _stream(stream)), "moe_forward_grouping")
 
 
 def check_device_error(ws, stream=None) -> int:

@@ -616,6 +616,62 @@ static hipError_t fused_dispatch(const moe_shape &s, const FusedParams &prm, siz
     return hipErrorInvalidConfiguration;
 }
 
+// Every work-group of the fused kernel waits on the others, so all of them must be
+// resident at once: one per compute unit.  Checked once per kernel instance at the largest
+// LDS it may ask for (a work-group that fits then fits with less).
+template <class F, class A, int CG, int CR, int CD>
+static bool fused_fits_one() {
+    static const bool ok = [] {
+        auto kern = decode_fused_kernel<F, A, CG, CR, CD>;
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)FLDS_MAX) != hipSuccess)
+            return false;
+        int n = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kern, FTHREADS, FLDS_MAX) != hipSuccess) return false;
+        return n >= 1;
+    }();
+    return ok;
+}
+
+template <class F, class A>
+static bool fused_fits(const moe_shape &s) {
+    const int cg = bucket((s.hidden / F::EPC + WAVE - 1) / WAVE);
+    const int cr = bucket((s.hidden / A::EPC + WAVE - 1) / WAVE);
+    const int nchd = s.intermediate / F::EPC;
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
+    const int cd = bucket((nchd + lpr - 1) / lpr);
+#define MOE_FF(CG, CR, CD) \
+    if (cg == CG && cr == CR && cd == CD) return fused_fits_one<F, A, CG, CR, CD>()
+    MOE_FF(4, 4, 2);
+    MOE_FF(4, 4, 1);
+    MOE_FF(4, 4, 4);
+    MOE_FF(2, 8, 1);
+    MOE_FF(2, 8, 2);
+    MOE_FF(1, 4, 1);
+    MOE_FF(1, 1, 1);
+    MOE_FF(1, 1, 2);
+    MOE_FF(2, 2, 1);
+    MOE_FF(2, 2, 2);
+    MOE_FF(8, 8, 2);
+    MOE_FF(8, 8, 4);
+#undef MOE_FF
+    return false;
+}
+
+bool decode_fused_coresident(const moe_shape &s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return true;   // no device: nothing will be launched
+    }
+    switch (s.weight_dtype) {
+        case MOE_F32: return fused_fits<FmtF32, FmtF32>(s);
+        case MOE_BF16: return fused_fits<FmtBF16, FmtBF16>(s);
+        case MOE_NVFP4: return fused_fits<FmtNV4, FmtBF16>(s);
+        default: return fused_fits<FmtMX4, FmtBF16>(s);
+    }
+}
+
 // (gate/up, router, down) chunk buckets the fused kernel is built for
 static bool fused_bucket_built(int cg, int cr, int cd) {
     static const int combos[][3] = {{4, 4, 2}, {4, 4, 1}, {4, 4, 4}, {2, 8, 1}, {2, 8, 2}, {1, 4, 1},

@@ -55,11 +55,11 @@ moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
     if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down)) return MOE_ERR_INVALID_ARG;
     const bool scaled = s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4;
     if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
+    // scale arrays: 16-byte aligned like every device pointer (the large-tile MXFP4 GEMM
+    // loads a tile's scale rows into LDS 16 bytes at a time)
+    if (scaled && (!aligned16(w->s_gate) || !aligned16(w->s_up) || !aligned16(w->s_down)))
+        return MOE_ERR_INVALID_ARG;
     if (s->weight_dtype == MOE_NVFP4) {
-        // 2-byte scale pairs are read per 16-byte chunk of codes
-        if ((reinterpret_cast<uintptr_t>(w->s_gate) | reinterpret_cast<uintptr_t>(w->s_up) |
-             reinterpret_cast<uintptr_t>(w->s_down)) & 1u)
-            return MOE_ERR_INVALID_ARG;
         if (!std::isfinite(w->ts_gate) || !std::isfinite(w->ts_up) || !std::isfinite(w->ts_down))
             return MOE_ERR_INVALID_ARG;
     }
@@ -201,8 +201,10 @@ const char *const kStagesFused = "decode_fused";
 const char *const kStagesGrouped = "router_logits,topk,group,gate_up,down,combine";
 const char *const kStagesGroupedFusedRouter = "router_topk,group,gate_up,down,combine";
 
+// The single-launch decode kernel needs a work-group on every compute unit at once; when
+// one of its work-groups does not fit a compute unit, the staged decode kernels run.
 bool use_fused(const moe_shape &s) {
-    return !use_grouped(s) && s.num_tokens <= 8 && decode_fused_supported(s);
+    return !use_grouped(s) && s.num_tokens <= 8 && decode_fused_supported(s) && decode_fused_coresident(s);
 }
 
 // Event pair (start, stop) of launch i, taken from ev[2i], ev[2i+1] when present.
@@ -223,9 +225,13 @@ hipError_t around(const StageEvents &se, int i, hipStream_t st, Fn &&fn) {
     return hipSuccess;
 }
 
-moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
-                        const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
-                        size_t ws_bytes, hipStream_t st, hipEvent_t *events, int n_events) {
+}  // namespace
+
+namespace moe {
+
+moe_status forward_check(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                         const moe_expert_weights *w, const void *y, const int32_t *topk_ids_out,
+                         const float *topk_w_out, const void *ws, size_t ws_bytes) {
     MOE_CHECK(check_shape(shape));
     MOE_CHECK(check_path(shape));
     if (shape->num_tokens == 0) return MOE_OK;
@@ -235,7 +241,14 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     if ((topk_ids_out && !aligned16(topk_ids_out)) || (topk_w_out && !aligned16(topk_w_out)))
         return MOE_ERR_INVALID_ARG;
     if (bias && (reinterpret_cast<uintptr_t>(bias) & 3u)) return MOE_ERR_INVALID_ARG;
-    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    return check_ws(shape, ws, ws_bytes);
+}
+
+moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                        const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, hipStream_t st, hipEvent_t *events, int n_events) {
+    MOE_CHECK(forward_check(shape, x, w_router, bias, w, y, topk_ids_out, topk_w_out, ws, ws_bytes));
+    if (shape->num_tokens == 0) return MOE_OK;
     const StageEvents se{events, n_events};
     if (use_fused(*shape)) {
         MOE_TRY(launch_decode_fused(*shape, x, w_router, bias, *w, y, topk_ids_out, topk_w_out, ws, st, se.start(0),
@@ -299,7 +312,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
     return MOE_OK;
 }
 
-}  // namespace
+}  // namespace moe
 
 extern "C" {
 
@@ -324,6 +337,27 @@ const char *moe_forward_stages(const moe_shape *shape) {
     if (check_shape(shape) != MOE_OK) return "";
     if (use_grouped(*shape)) return fused_router(*shape) ? kStagesGroupedFusedRouter : kStagesGrouped;
     return use_fused(*shape) ? kStagesFused : kStagesStaged;
+}
+
+moe_status moe_forward_grouping(const moe_shape *shape, const void *ws, size_t ws_bytes, int32_t *expert_offsets,
+                                int32_t *sorted_slots, int32_t *slot_pos, void *stream) {
+    MOE_CHECK(check_shape(shape));
+    MOE_CHECK(check_path(shape));
+    if (use_fused(*shape)) return MOE_ERR_UNSUPPORTED;
+    const size_t P = (size_t)shape->num_tokens * (size_t)shape->top_k;
+    if (!expert_offsets || (P && (!sorted_slots || !slot_pos))) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(expert_offsets) || !aligned16(sorted_slots) || !aligned16(slot_pos)) return MOE_ERR_INVALID_ARG;
+    MOE_CHECK(check_ws(shape, ws, ws_bytes));
+    const WsLayout L = ws_layout(*shape);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint8_t *b = static_cast<const uint8_t *>(ws);
+    const size_t E1 = (size_t)shape->num_experts + 1;
+    MOE_TRY(hipMemcpyAsync(expert_offsets, b + L.offsets, E1 * 4, hipMemcpyDeviceToDevice, st));
+    if (P) {
+        MOE_TRY(hipMemcpyAsync(sorted_slots, b + L.sorted, P * 4, hipMemcpyDeviceToDevice, st));
+        MOE_TRY(hipMemcpyAsync(slot_pos, b + L.slot_pos, P * 4, hipMemcpyDeviceToDevice, st));
+    }
+    return MOE_OK;
 }
 
 moe_status moe_check_device_error(void *ws, int32_t *err_bits, void *stream) {

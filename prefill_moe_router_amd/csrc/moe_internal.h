@@ -30,7 +30,9 @@ inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM + (P < E ? P : E); }
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
-// words: [0] the sticky device error word, the rest zero between calls.
+// words: [0] the sticky device error word; [8] the fused decode kernel's 64-bit
+// call counter, which only grows (the tag of the words that kernel publishes is
+// derived from it, so it must never be reset on its own).
 // tokens per work-group of the MFMA router (and per count row of its grouping output)
 constexpr int kRouterRows = 32;
 
@@ -108,6 +110,9 @@ hipError_t launch_combine(const moe_shape &s, const float *o, const float *w, co
 
 // whole layer for T <= 8 in one persistent launch (see decode_fused.hip)
 bool decode_fused_supported(const moe_shape &s);
+// one work-group of the fused kernel for `s` fits a compute unit of the current device
+// (true when no device can be queried: nothing is launched then)
+bool decode_fused_coresident(const moe_shape &s);
 hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr, const float *bias,
                                const moe_expert_weights &w, void *y, int32_t *ids_out, float *w_out, void *ws,
                                hipStream_t st, hipEvent_t ev_start, hipEvent_t ev_stop);
@@ -140,5 +145,15 @@ hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, con
                             hipEvent_t ev0, hipEvent_t ev1);
 // y[t] = sum_j o'[t*k+j] (bf16 rows)
 hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st);
+
+// moe_forward's host-side argument validation alone (launches nothing)
+moe_status forward_check(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                         const moe_expert_weights *w, const void *y, const int32_t *topk_ids_out,
+                         const float *topk_w_out, const void *ws, size_t ws_bytes);
+// the whole layer on a given workspace (moe_forward, moe_forward_timed and the
+// scratch-backed entry point share it): validation, then the launch sequence
+moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_router, const float *bias,
+                        const moe_expert_weights *w, void *y, int32_t *topk_ids_out, float *topk_w_out, void *ws,
+                        size_t ws_bytes, hipStream_t st, hipEvent_t *events, int n_events);
 
 }  // namespace moe

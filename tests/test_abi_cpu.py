@@ -100,8 +100,43 @@ def test_forward_validation():
                          pm.workspace_size(_shape(num_tokens=0)), None) == pm.OK
 
 
+def test_scale_pointers_must_be_16_byte_aligned():
+    """MXFP4 and NVFP4 scale arrays follow the header's 16-byte rule for device pointers."""
+    L = pm.lib()
+    for fmt in (pm.MXFP4, pm.NVFP4):
+        shp = _shape(weight_dtype=fmt)
+        s = shp.c()
+        n = pm.workspace_size(shp)
+        for bad in (FAKE + 1, FAKE + 2, FAKE + 8):
+            for pos in range(3):
+                sc = [FAKE, FAKE, FAKE]
+                sc[pos] = bad
+                w = pm.ExpertWeights(FAKE, FAKE, FAKE, *sc, 1.0, 1.0, 1.0)
+                assert L.moe_forward(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE, n,
+                                     None) == pm.ERR_INVALID_ARG, (fmt, bad, pos)
+
+
+def test_forward_grouping_validation():
+    """The grouping view: decode shapes keep their grouping on chip (unsupported); null
+    outputs, a short workspace and bad shapes are rejected before any copy."""
+    L = pm.lib()
+    def grp(shp, ws=FAKE, nbytes=None, off=FAKE, srt=FAKE, pos=FAKE):
+        s = shp.c()
+        nb = pm.workspace_size(shp) if nbytes is None else nbytes
+        return L.moe_forward_grouping(ctypes.byref(s), ws, nb, off, srt, pos, None)
+    assert pm.forward_stages(_shape(num_tokens=1)) == ["decode_fused"]
+    assert grp(_shape(num_tokens=1)) == pm.ERR_UNSUPPORTED
+    big = _shape(num_tokens=8192)
+    assert grp(big, off=None) == pm.ERR_INVALID_ARG
+    assert grp(big, srt=None) == pm.ERR_INVALID_ARG
+    assert grp(big, pos=FAKE + 4) == pm.ERR_INVALID_ARG
+    assert grp(big, ws=None) == pm.ERR_INVALID_ARG
+    assert grp(big, nbytes=pm.workspace_size(big) - 1) == pm.ERR_WORKSPACE
+    assert grp(_shape(top_k=0), nbytes=1 << 30) == pm.ERR_INVALID_ARG
+
+
 def test_nvfp4_validation():
-    """NVFP4 experts: scale arrays required and 2-byte aligned, finite tensor scales; AUTO
+    """NVFP4 experts: scale arrays required and 16-byte aligned, finite tensor scales; AUTO
     takes the grouped GEMMs from four pairs per expert (MXFP4: three)."""
     L = pm.lib()
     shp = _shape(weight_dtype=pm.NVFP4)

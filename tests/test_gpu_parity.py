@@ -7,8 +7,8 @@ import torch
 import oracle
 import prefill_moe_router_amd as pm
 import synth
-from tests.gpu_common import (DevLayer, canary_ok, compare_forward, guarded, layer, layer_of, lshape, note,
-                              run_forward, tdev, to_f64)
+from tests.gpu_common import (W_TOL, DevLayer, canary_ok, compare_forward, forward_grouping, guarded, layer, layer_of,
+                              lshape, note, run_forward, tdev, to_f64)
 from tests.helpers import grouping_violations, max_abs, oracle_layer, rel_l2
 
 pytestmark = pytest.mark.gpu
@@ -18,13 +18,6 @@ pytestmark = pytest.mark.gpu
 def _gpu():
     assert torch.cuda.is_available(), "GPU tests need a visible MI355X"
     pm.lib()  # loud failure when the library is missing
-
-
-def _sample(T, n=48):
-    """Token sample spanning the chunk: first, last, and evenly spread in between."""
-    if T <= n:
-        return np.arange(T)
-    return np.unique(np.concatenate([[0, T - 1], np.linspace(0, T - 1, n - 2).astype(int)]))
 
 
 # ---- router ------------------------------------------------------------------------------
@@ -47,7 +40,7 @@ def test_router_topk_parity(name):
     mism = (gids != ref["ids"]).any(1)
     assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
     ok = ~mism
-    assert max_abs(gw[ok], ref["w"][ok]) <= 1e-6
+    assert max_abs(gw[ok], ref["w"][ok]) <= W_TOL
     assert np.all(np.diff(gids, axis=1) > 0)          # ascending ids
     note(f"  near-ties {int(ref['near'].sum())}, id mismatches {int(mism.sum())}")
 
@@ -89,7 +82,7 @@ def test_router_topk_mfma_shapes(T, H, E, K, renorm, bias):
     mism = (gids != ref["ids"]).any(1)
     assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
     ok = ~mism
-    assert max_abs(gw[ok], ref["w"][ok]) <= 1e-6
+    assert max_abs(gw[ok], ref["w"][ok]) <= W_TOL
     assert np.all(np.diff(gids, axis=1) > 0) and gids.min() >= 0 and gids.max() < E
     note(f"  near-ties {int(ref['near'].sum())}, id mismatches {int(mism.sum())}")
 
@@ -113,7 +106,7 @@ def test_router_gemv_shapes(T, H, E, K, act):
     gids, gw = ids.cpu().numpy(), wt.cpu().numpy()
     mism = (gids != ref["ids"]).any(1)
     assert not (mism & ~ref["near"]).any(), np.nonzero(mism & ~ref["near"])[0][:10]
-    assert max_abs(gw[~mism], ref["w"][~mism]) <= 1e-6
+    assert max_abs(gw[~mism], ref["w"][~mism]) <= W_TOL
     assert np.all(np.diff(gids, axis=1) > 0)
 
 
@@ -305,19 +298,6 @@ def test_forward_parity_decode_configs(name):
     compare_forward(li, got, label=name)
 
 
-def test_forward_parity_prefill_chunk_sampled():
-    """8192-token Zipf-skewed chunk: all ids and the grouping checked everywhere, y on a
-    token sample spanning the chunk."""
-    name = "c3_prefill8192_bf16"
-    note(f"forward parity {name} (sampled)")
-    li = layer(name)
-    got = run_forward(DevLayer(li))
-    ref = oracle.router(oracle_layer(li))
-    mism = (got["ids"] != ref["ids"]).any(1)
-    assert not (mism & ~ref["near"]).any()
-    compare_forward(li, got, tokens=_sample(li.shape.T, 40), label=name)
-
-
 @pytest.mark.parametrize("name", ["c4_mxfp4_decode1", "c4_mxfp4_decode8"])
 def test_forward_parity_mxfp4_decode(name):
     note(f"forward parity {name}")
@@ -348,7 +328,7 @@ def test_forward_nvfp4_streaming(T):
     note(f"nvfp4 streaming T={T}")
     li = layer_of(synth.Shape(T, 4096, 256, 8, 1024, "bf16", "nvfp4"), batch=90 + T)
     got = run_forward(DevLayer(li))
-    compare_forward(li, got, tokens=_sample(T, 12), label=f"nvfp4 T={T}")
+    compare_forward(li, got, label=f"nvfp4 T={T}")
 
 
 @pytest.mark.parametrize("T,H,E,K,I,path", [(130, 1024, 32, 4, 256, pm.PATH_GROUPED),
@@ -362,7 +342,7 @@ def test_forward_nvfp4_grouped(T, H, E, K, I, path):
     assert "router_topk" in pm.forward_stages(sh) or "router_logits" in pm.forward_stages(sh)
     assert "gate_up" in pm.forward_stages(sh)
     got = run_forward(DevLayer(li), path=path)
-    compare_forward(li, got, tokens=_sample(T, 16), label=f"nvfp4 grouped T={T}")
+    compare_forward(li, got, label=f"nvfp4 grouped T={T}")
 
 
 @pytest.mark.parametrize("T,H,E,K,I", [(3, 1024, 64, 4, 512), (12, 512, 32, 4, 256)])
@@ -450,42 +430,14 @@ def test_forward_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
 
 
-def test_forward_mixed_prefill_and_decode_rows_in_one_graph():
-    """A prefill chunk with decode rows appended, in one captured moe_forward: the decode
-    rows ride the chunk's expert GEMMs.  Every replay equals the eager run, and the decode
-    rows (and a sample of the chunk) match the oracle."""
-    li = layer("c3_mixed8200_bf16")
-    dl = DevLayer(li)
-    sh = lshape(li)
-    T = li.shape.T
-    ws = pm.alloc_workspace(sh)
-    y = torch.empty(T, li.shape.H, dtype=torch.int16, device="cuda")
-    ids = torch.empty(T, li.shape.K, dtype=torch.int32, device="cuda")
-    w = torch.empty(T, li.shape.K, dtype=torch.float32, device="cuda")
-    pm.forward(sh, dl.x, dl.wr, dl.bias, dl.weights, y, ws, ids, w)
-    torch.cuda.synchronize()
-    eager = (y.clone(), ids.clone(), w.clone())
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        pm.forward(sh, dl.x, dl.wr, dl.bias, dl.weights, y, ws, ids, w)
-    for r in range(3):
-        y.fill_(0)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        assert torch.equal(y, eager[0]) and torch.equal(ids, eager[1]) and torch.equal(w, eager[2]), f"replay {r}"
-    got = dict(y=y, ids=ids.cpu().numpy(), w=w.cpu().numpy())
-    toks = np.unique(np.concatenate([_sample(T - 8, 24), np.arange(T - 8, T)]))
-    compare_forward(li, got, tokens=toks, label="mixed 8192 + 8")
-
-
 # ---- streaming GEMV family beyond 8 tokens (medium batches) -------------------------------------
 
 @pytest.mark.parametrize("T,w,path", [(24, "bf16", pm.PATH_AUTO), (48, "bf16", pm.PATH_DECODE),
                                       (40, "mxfp4", pm.PATH_AUTO), (20, "mxfp4", pm.PATH_DECODE)])
 def test_forward_medium_batch_streaming(T, w, path):
     """Tens of tokens on the streaming family (tokens staged in LDS, MXFP4 decoded once
-    per row, several row passes per work-group): ids exact, y sampled against the oracle."""
+    per row, several row passes per work-group): ids exact, y of every token against the
+    oracle."""
     note(f"medium batch T={T} {w}")
     if w == "bf16":
         sh_ = synth.Shape(T, 2048, 128, 8, 768, "bf16", "bf16", bias="normal")
@@ -493,7 +445,7 @@ def test_forward_medium_batch_streaming(T, w, path):
         sh_ = synth.Shape(T, 4096, 256, 8, 1024, "bf16", "mxfp4")
     li = layer_of(sh_, batch=70 + T)
     got = run_forward(DevLayer(li), path=path)
-    compare_forward(li, got, tokens=_sample(T, 16), label=f"medium T={T} {w}")
+    compare_forward(li, got, label=f"medium T={T} {w}")
 
 
 # ---- grouped MFMA family ----------------------------------------------------------------------
@@ -504,7 +456,7 @@ def test_forward_grouped_path_forced(T):
     note(f"grouped forced T={T}")
     li = layer_of(synth.Shape(T, 2048, 128, 8, 768, "bf16", "bf16", bias="normal"), batch=50 + T)
     got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
-    compare_forward(li, got, tokens=_sample(T, 64), label=f"grouped T={T}")
+    compare_forward(li, got, label=f"grouped T={T}")
 
 
 def test_forward_grouped_ragged_zipf():
@@ -545,8 +497,8 @@ def test_forward_grouped_top10():
 def test_forward_grouped_wide_persistent_tiles():
     """2048 tokens on the large-tile kernels: the gate/up grid holds one work-group per CU
     and each walks four or five of the ~1100 tiles, so the next-tile prefetch and the hand
-    over of ring slots under the epilogue run many times.  Ids everywhere, y on a token
-    sample spanning the chunk."""
+    over of ring slots under the epilogue run many times.  Ids, y and the call's own
+    grouping on every token."""
     sh_ = synth.Shape(2048, 512, 16, 8, 1024, "bf16", "bf16", bias="zipf")
     li = synth.make_layer(sh_, beta=1.0)
     note("grouped wide persistent T=2048 H=512 E=16 K=8 I=1024")
@@ -554,7 +506,13 @@ def test_forward_grouped_wide_persistent_tiles():
     ref = oracle.router(oracle_layer(li))
     mism = (got["ids"] != ref["ids"]).any(1)
     assert not (mism & ~ref["near"]).any()
-    compare_forward(li, got, tokens=_sample(2048, 96), label="grouped wide persistent")
+    compare_forward(li, got, label="grouped wide persistent")
+    sh = lshape(li, pm.PATH_GROUPED)
+    off, srt, pos = forward_grouping(sh, got["ws"])
+    roff, rsrt, rpos = oracle.group(got["ids"], li.shape.E)
+    np.testing.assert_array_equal(off, roff)
+    np.testing.assert_array_equal(srt, rsrt)
+    np.testing.assert_array_equal(pos, rpos)
 
 
 @pytest.mark.parametrize("T,H,E,K,I", [(300, 1024, 32, 4, 512), (160, 2048, 16, 8, 1024)])
@@ -565,7 +523,7 @@ def test_forward_grouped_wide_tiles_mxfp4(T, H, E, K, I):
     sh_ = synth.Shape(T, H, E, K, I, "bf16", "mxfp4", bias="zipf")
     li = synth.make_layer(sh_, beta=1.0)
     got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
-    compare_forward(li, got, tokens=_sample(T, 48), label=f"grouped wide mxfp4 T={T}")
+    compare_forward(li, got, label=f"grouped wide mxfp4 T={T}")
 
 
 def test_staged_expert_ffn_grouped_path():
@@ -592,15 +550,3 @@ def test_forward_grouped_mxfp4_small():
     li = layer_of(synth.Shape(77, 256, 16, 4, 128, "bf16", "mxfp4", bias="normal"))
     got = run_forward(DevLayer(li), path=pm.PATH_GROUPED)
     compare_forward(li, got, label="grouped mxfp4 small")
-
-
-def test_forward_parity_mxfp4_prefill_sampled():
-    """4096-token MXFP4 chunk (H=4096, E=256, top-8, I=1024): all ids checked, y sampled."""
-    name = "c4_mxfp4_prefill4096"
-    note(f"forward parity {name} (sampled)")
-    li = layer(name)
-    got = run_forward(DevLayer(li))
-    ref = oracle.router(oracle_layer(li))
-    mism = (got["ids"] != ref["ids"]).any(1)
-    assert not (mism & ~ref["near"]).any()
-    compare_forward(li, got, tokens=_sample(li.shape.T, 24), label=name)
