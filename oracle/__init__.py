@@ -27,7 +27,7 @@ import numpy as np
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liboracle.so")
 
-F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
+F32, BF16, MXFP4, NVFP4, MXINT8 = 0, 1, 2, 3, 4
 
 
 class _Layer(ctypes.Structure):
@@ -60,6 +60,8 @@ def lib():
         L.orc_decode_e2m1.argtypes = [ctypes.c_uint]
         L.orc_decode_e8m0.restype = ctypes.c_double
         L.orc_decode_e8m0.argtypes = [ctypes.c_uint8]
+        L.orc_decode_int8.restype = ctypes.c_double
+        L.orc_decode_int8.argtypes = [ctypes.c_uint8]
         L.orc_decode_e4m3.restype = ctypes.c_double
         L.orc_decode_e4m3.argtypes = [ctypes.c_uint8]
         L.orc_router.restype = ctypes.c_int
@@ -76,6 +78,8 @@ def lib():
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                   ctypes.c_void_p]
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.restype = None
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -96,6 +100,8 @@ class Layer:
     uint8 packed codes [E,I,H/2] / [E,H,I/2] with uint8 E8M0 scales sg, su
     [E,I,H/32] and sd [E,H,I/32].  fmt="nvfp4": the same codes with uint8 E4M3
     scales [E,I,H/16] / [E,H,I/16] and the tensor scales ts (gate, up, down).
+    MXINT8: int8 codes [E,I,H] / [E,H,I] (OCP MX INT8 elements, implicit scale
+    2^-6) with uint8 E8M0 scales as for MXFP4.
     bias [E] float32 or None.
     """
     x: np.ndarray
@@ -122,6 +128,8 @@ class Layer:
             return F32
         if self.wg.dtype == np.uint16:
             return BF16
+        if self.wg.dtype == np.int8:
+            return MXINT8
         return NVFP4 if self.fmt == "nvfp4" else MXFP4
 
     @property
@@ -224,9 +232,19 @@ def decode_e8m0(code: int) -> float:
     return lib().orc_decode_e8m0(code)
 
 
+def decode_int8(code: int) -> float:
+    """OCP MX INT8 element value of a code byte (before the block scale)."""
+    return lib().orc_decode_int8(code)
+
+
 def decode_e4m3(code: int) -> float:
     return lib().orc_decode_e4m3(code)
 
 
 def num_threads() -> int:
     return lib().orc_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    """Thread count of later oracle calls (OpenMP)."""
+    lib().orc_set_num_threads(int(n))

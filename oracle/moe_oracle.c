@@ -38,6 +38,7 @@
 #define ORC_BF16 1
 #define ORC_MXFP4 2
 #define ORC_NVFP4 3
+#define ORC_MXINT8 4
 
 typedef struct {
     int32_t T;          /* number of tokens */
@@ -47,11 +48,11 @@ typedef struct {
     int32_t I;          /* expert intermediate size */
     int32_t renorm;     /* 1: kept weights renormalised to sum 1 */
     int32_t act_dtype;  /* x and router weight: ORC_F32 or ORC_BF16 */
-    int32_t w_dtype;    /* expert weights: ORC_F32, ORC_BF16, ORC_MXFP4 or ORC_NVFP4 */
+    int32_t w_dtype;    /* expert weights: ORC_F32, ORC_BF16, ORC_MXFP4, ORC_NVFP4 or ORC_MXINT8 */
     const void *x;      /* [T][H] */
     const void *wr;     /* [E][H] */
     const float *bias;  /* [E] or NULL */
-    const void *wg;     /* [E][I][H]   (MXFP4: [E][I][H/2] bytes) */
+    const void *wg;     /* [E][I][H]   (MXFP4: [E][I][H/2] bytes; MXINT8: [E][I][H] bytes) */
     const void *wu;     /* [E][I][H] */
     const void *wd;     /* [E][H][I]   (MXFP4: [E][H][I/2] bytes) */
     const uint8_t *sg;  /* MXFP4 scales [E][I][H/32]; NVFP4 [E][I][H/16] */
@@ -97,10 +98,18 @@ double orc_decode_e4m3(uint8_t code)
     return s ? -v : v;
 }
 
+/* OCP MX INT8 element: an 8-bit two's complement integer with an implicit scale of
+ * 2^-6 (so codes span -2 .. 127/64); the block's E8M0 scale multiplies it. */
+double orc_decode_int8(uint8_t code)
+{
+    int v = (code & 0x80u) ? (int)code - 256 : (int)code;
+    return ldexp((double)v, -6);
+}
+
 /* Every code's value, looked up per element instead of decoded again: entry c is
  * exactly what the decoder above returns for code c, so the lookups change no value
  * (they only spare the per-element ldexp calls of the 4-bit formats). */
-static double tab_e2m1[16], tab_e8m0[256], tab_e4m3[256];
+static double tab_e2m1[16], tab_e8m0[256], tab_e4m3[256], tab_int8[256];
 
 static void fill_code_tables(void)
 {
@@ -108,6 +117,7 @@ static void fill_code_tables(void)
     for (unsigned c = 0; c < 256; ++c) {
         tab_e8m0[c] = orc_decode_e8m0((uint8_t)c);
         tab_e4m3[c] = orc_decode_e4m3((uint8_t)c);
+        tab_int8[c] = orc_decode_int8((uint8_t)c);
     }
 }
 
@@ -124,6 +134,8 @@ static double wt_at(const orc_layer *L, const void *w, const uint8_t *s, double 
 {
     if (L->w_dtype == ORC_F32) return (double)((const float *)w)[row * cols + col];
     if (L->w_dtype == ORC_BF16) return orc_decode_bf16(((const uint16_t *)w)[row * cols + col]);
+    if (L->w_dtype == ORC_MXINT8) /* one byte per element, one E8M0 scale per 32 elements */
+        return tab_int8[((const uint8_t *)w)[row * cols + col]] * tab_e8m0[s[row * (cols / 32) + col / 32]];
     /* MXFP4 and NVFP4: two codes per byte, the even element in the low nibble */
     uint8_t byte = ((const uint8_t *)w)[row * (cols / 2) + col / 2];
     unsigned code = (col & 1) ? (unsigned)(byte >> 4) : (unsigned)(byte & 15u);
@@ -266,7 +278,7 @@ int orc_group(int T, int k, int E, const int32_t *ids, int32_t *off, int32_t *so
 static void expert_apply(const orc_layer *L, int t, int e, double *o, double *a)
 {
     const int H = L->H, I = L->I;
-    const int sc = (L->w_dtype == ORC_MXFP4 || L->w_dtype == ORC_NVFP4);
+    const int sc = (L->w_dtype == ORC_MXFP4 || L->w_dtype == ORC_NVFP4 || L->w_dtype == ORC_MXINT8);
     const size_t rows_gu = (size_t)e * I, rows_d = (size_t)e * H;
     for (int i = 0; i < I; ++i) {
         double g = 0.0, u = 0.0;
@@ -352,6 +364,17 @@ int orc_forward(const orc_layer *L, const int32_t *tokens, int n, const int32_t 
         free(o); free(a);
     }
     return 0;
+}
+
+/* sets the number of OpenMP threads later calls use (no effect without OpenMP) */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    extern void omp_set_num_threads(int);
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
 }
 
 /* number of OpenMP threads the oracle will use (1 without OpenMP) */

@@ -15,6 +15,8 @@ and 8192-token prefill chunks -- the same chapter, §9.8):
   c3  prefill T=8192 bf16, Zipf(1) expert popularity through the router bias
   c4  MXFP4 experts (E2M1, 32-element blocks, E8M0 scales), bf16 activations:
       H=4096, E=256, top-8, I=1024, at T=1, T=8 and T=4096
+  c5  the same with NVFP4 experts; c6 the same with MXINT8 experts (OCP MX INT8:
+      int8 elements with an implicit 2^-6, 32-element blocks, E8M0 scales)
 
 Distributions: x ~ N(0,1); router W ~ N(0, 0.02); expert W ~ N(0, 1/sqrt(fan_in))
 with fan_in = H for gate/up and I for down (the second parameter is the
@@ -53,7 +55,7 @@ class Shape:
     K: int
     I: int
     act: str          # "f32" | "bf16"
-    w: str            # "f32" | "bf16" | "mxfp4" | "nvfp4"
+    w: str            # "f32" | "bf16" | "mxfp4" | "nvfp4" | "mxint8"
     bias: str = "none"  # "none" | "normal" | "zipf"
     renorm: bool = True
 
@@ -72,6 +74,10 @@ CONFIGS: Dict[str, Shape] = {
     "c5_nvfp4_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "nvfp4"),
     "c5_nvfp4_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "nvfp4"),
     "c5_nvfp4_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "nvfp4"),
+    # the same shapes with MXINT8 experts (OCP MX INT8: int8 codes, E8M0 scale per 32)
+    "c6_mxint8_decode1": Shape(1, 4096, 256, 8, 1024, "bf16", "mxint8"),
+    "c6_mxint8_decode8": Shape(8, 4096, 256, 8, 1024, "bf16", "mxint8"),
+    "c6_mxint8_prefill4096": Shape(4096, 4096, 256, 8, 1024, "bf16", "mxint8"),
 }
 
 
@@ -149,6 +155,37 @@ def mxfp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
     val = np.where(c & 8, -mag, mag)
     X = np.ldexp(1.0, scales.astype(np.int64) - 127)
     return val * np.repeat(X, 32, axis=1)
+
+
+def mxint8_quantize(w: np.ndarray):
+    """Quantise fp32 rows [R, C] (C % 32 == 0) to MXINT8 along C (OCP MX v1.0 INT8: an
+    element is a two's complement int8 with an implicit scale of 2^-6, i.e. code / 64).
+
+    Block scale X = 2^floor(log2 amax) (the INT8 element's largest power of two is 2^0);
+    codes = v / X * 64 rounded to nearest even and clamped to [-127, 127].  An all-zero
+    block gets scale code 0 and zero codes.  Returns (codes [R, C] int8, scales
+    [R, C/32] uint8 E8M0).
+    """
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    R, C = w.shape
+    assert C % 32 == 0
+    blk = w.reshape(R, C // 32, 32)
+    amax = np.abs(blk).max(axis=2)
+    _, ex = np.frexp(amax)                   # floor(log2 amax) = ex - 1
+    e = ex.astype(np.int64) - 1
+    nz = amax > 0
+    scale_code = np.where(nz, np.clip(e + 127, 0, 254), 0).astype(np.uint8)
+    X = np.ldexp(np.float64(1.0), scale_code.astype(np.int32) - 127)[..., None]
+    q = np.rint(blk.astype(np.float64) / X * 64.0)   # exact scaling, then ties to even
+    q = np.clip(q, -127, 127)
+    q = np.where(nz[..., None], q, 0).astype(np.int8).reshape(R, C)
+    return q, scale_code
+
+
+def mxint8_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Inverse storage map used by tests on the quantiser: fp64 [R, C]."""
+    X = np.ldexp(1.0, scales.astype(np.int64) - 127)
+    return codes.astype(np.float64) / 64.0 * np.repeat(X, 32, axis=1)
 
 
 # NVFP4 (E2M1 codes, one E4M3 scale per 16 elements, one fp32 scale per tensor).
@@ -253,6 +290,9 @@ def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigm
     if shape.w in ("mxfp4", "nvfp4"):
         codes = np.empty((E, rows, cols // 2), np.uint8)
         scales = np.empty((E, rows, cols // (32 if shape.w == "mxfp4" else 16)), np.uint8)
+    elif shape.w == "mxint8":
+        codes = np.empty((E, rows, cols), np.int8)
+        scales = np.empty((E, rows, cols // 32), np.uint8)
     else:
         out = np.empty((E, rows, cols), np.float32 if shape.w == "f32" else np.uint16)
 
@@ -262,6 +302,8 @@ def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigm
             codes[e], scales[e] = mxfp4_quantize(a32)
         elif shape.w == "nvfp4":
             codes[e], scales[e] = nvfp4_quantize(a32, ts)
+        elif shape.w == "mxint8":
+            codes[e], scales[e] = mxint8_quantize(a32)
         elif shape.w == "bf16":
             out[e] = f32_to_bf16_bits(a32)
         else:
@@ -273,7 +315,7 @@ def _expert_tensor(shape: Shape, seed: int, tag: str, rows: int, cols: int, sigm
     else:
         for e in range(E):
             one(e)
-    if shape.w in ("mxfp4", "nvfp4"):
+    if shape.w in ("mxfp4", "nvfp4", "mxint8"):
         return codes, scales
     return out, None
 

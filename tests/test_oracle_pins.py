@@ -474,3 +474,69 @@ def test_nvfp4_quantiser_round_trip():
     blk_scale = np.repeat(np.array([[oracle.decode_e4m3(int(c)) for c in row] for row in scales]) * ts, 16, axis=1)
     ok = np.abs(w) <= 6.0 * blk_scale
     assert np.all(np.abs(d - w)[ok] <= 1.0 * blk_scale[ok] + 1e-12)
+
+
+# ---- MXINT8 (OCP MX INT8 elements, E8M0 block scales per 32 elements) -------------------
+
+def test_mxint8_table():
+    """Element values of the OCP MX INT8 encoding, hand-derived from the definition."""
+    rows = _table("mxint8_table.txt")
+    assert len(rows) >= 12
+    for code, val in rows:
+        assert oracle.decode_int8(int(code, 16)) == float(val), code
+
+
+def test_mxint8_decode_exhaustive_against_twos_complement():
+    """All 256 codes against numpy's two's complement reading of the byte, over 64."""
+    ref = np.arange(256, dtype=np.int64).astype(np.uint8).view(np.int8).astype(np.float64) / 64.0
+    for code in range(256):
+        assert oracle.decode_int8(code) == ref[code], code
+
+
+def test_mxint8_hand_case():
+    """One nonzero element per matrix, worked by hand from the format definition:
+    gate 0x30 (0.75) x 2^1 (E8M0 128) = 1.5; up 0xC0 (-1.0) x 2^-2 (E8M0 125) = -0.25;
+    down 0x50 (1.25) x 2^2 (E8M0 129) = 5.0, so with x = e_9 the expert output is
+    o[5] = 5 * silu(1.5) * -0.25 and zero elsewhere."""
+    H = I = 32
+    x = np.zeros((1, H), np.uint16)
+    x[0, 9] = 0x3F80                                   # bf16 1.0
+    cg = np.zeros((1, I, H), np.int8); cg[0, 4, 9] = 0x30
+    cu = np.zeros((1, I, H), np.int8); cu[0, 4, 9] = np.int8(-64)
+    cd = np.zeros((1, H, I), np.int8); cd[0, 5, 4] = 0x50
+    sg = np.zeros((1, I, 1), np.uint8); sg[0, 4, 0] = 128
+    su = np.zeros((1, I, 1), np.uint8); su[0, 4, 0] = 125
+    sd = np.zeros((1, H, 1), np.uint8); sd[0, 5, 0] = 129
+    L = oracle.Layer(x=x, wr=np.zeros((1, H), np.uint16), wg=cg, wu=cu, wd=cd, top_k=1, sg=sg, su=su, sd=sd)
+    o = oracle.expert_pairs(L, [0], [0])[0]
+    want = np.zeros(H)
+    want[5] = 5.0 * (1.5 / (1.0 + math.exp(-1.5))) * -0.25
+    np.testing.assert_allclose(o, want, rtol=1e-15, atol=0)
+
+
+def test_forward_mxint8_matches_numpy_on_dequantised_weights():
+    """The oracle's expert outputs and whole layer on MXINT8 storage equal fp64 numpy
+    products on the weights dequantised by the generator's own (independent) inverse map,
+    and the oracle on fp32 storage of those values."""
+    li = synth.make_layer(synth.Shape(3, 64, 4, 2, 32, "bf16", "mxint8", bias="normal"))
+    L = oracle_layer(li)
+    E, T = li.shape.E, li.shape.T
+    deq = {}
+    for name, sname in (("wg", "sg"), ("wu", "su"), ("wd", "sd")):
+        c, s = getattr(li, name), getattr(li, sname)
+        deq[name] = np.stack([synth.mxint8_dequantize(c[e], s[e]) for e in range(E)])
+    x = synth.bf16_bits_to_f32(li.x).astype(np.float64)
+    tok = [t for t in range(T) for e in range(E)]
+    exp_ = [e for t in range(T) for e in range(E)]
+    got = oracle.expert_pairs(L, tok, exp_)
+    for p, (t, e) in enumerate(zip(tok, exp_)):
+        g = deq["wg"][e] @ x[t]
+        u = deq["wu"][e] @ x[t]
+        want = deq["wd"][e] @ (g / (1.0 + np.exp(-g)) * u)
+        np.testing.assert_allclose(got[p], want, rtol=1e-11, atol=1e-14)
+    f32 = {k: v.astype(np.float32) for k, v in deq.items()}
+    assert all(np.array_equal(f32[k].astype(np.float64), deq[k]) for k in deq)   # exact in fp32
+    L32 = oracle.Layer(x=li.x, wr=li.wr, wg=f32["wg"], wu=f32["wu"], wd=f32["wd"], top_k=2, bias=li.bias)
+    a, b = oracle.forward(L), oracle.forward(L32)
+    np.testing.assert_array_equal(a["ids"], b["ids"])
+    np.testing.assert_array_equal(a["y"], b["y"])

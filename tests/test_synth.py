@@ -116,3 +116,34 @@ def test_zipf_beta_matches_record():
     assert rec["beta"] == synth.ZIPF_BETA
     h = np.array(rec["histogram"])
     assert h.sum() == 8192 * 8 and (h == 0).any() and (h > 2000).any()
+
+
+def test_mxint8_quantiser():
+    """The generator's MXINT8 quantiser (OCP MX INT8): block scale 2^floor(log2 amax), codes
+    the nearest multiple of X/64 (ties to even) clamped to +-127, so every stored value is
+    within half a step of its input unless clamped; representable values round-trip; an
+    all-zero block gets scale code 0 and zero codes."""
+    rng = np.random.default_rng(9)
+    w = (rng.standard_normal((6, 96)) * 0.03).astype(np.float32)
+    w[2, 32:64] = 0.0
+    codes, scales = synth.mxint8_quantize(w)
+    assert codes.dtype == np.int8 and scales.dtype == np.uint8 and codes.shape == w.shape
+    assert scales[2, 1] == 0 and np.all(codes[2, 32:64] == 0)
+    blk = np.abs(w.reshape(6, 3, 32)).max(axis=2)
+    nz = blk > 0
+    assert np.all(np.ldexp(1.0, scales[nz].astype(int) - 127) <= blk[nz])
+    assert np.all(blk[nz] < np.ldexp(2.0, scales[nz].astype(int) - 127))
+    d = synth.mxint8_dequantize(codes, scales)
+    step = np.repeat(np.ldexp(1.0, scales.astype(int) - 127 - 6), 32, axis=1)
+    assert np.all(codes >= -127) and np.all(codes <= 127)
+    clamped = np.abs(codes) == 127
+    assert np.all(np.abs(d - w)[~clamped] <= 0.5 * step[~clamped] + 1e-12)
+    # values on the grid come back exactly; a value just under 2 X clamps to 127/64 X
+    grid = np.array([[0.5, -0.25, 1.984375, -1.0] + [1.0] * 28], np.float32)
+    c2, s2 = synth.mxint8_quantize(grid)
+    assert s2[0, 0] == 127 and np.array_equal(synth.mxint8_dequantize(c2, s2), grid.astype(np.float64))
+    c3, _ = synth.mxint8_quantize(np.array([[1.999] + [0.0] * 31], np.float32))
+    assert c3[0, 0] == 127
+    # ties to even: 0.5/64 and 1.5/64 above an exact grid value of a block with X = 1
+    c4, s4 = synth.mxint8_quantize(np.array([[1.0, 1.0 / 128, 3.0 / 128, -1.0 / 128] + [0.0] * 28], np.float32))
+    assert s4[0, 0] == 127 and list(c4[0, :4]) == [64, 0, 2, 0]
