@@ -2,24 +2,28 @@
 grouping, SwiGLU experts, weighted combine) through the C ABI.
 
 One step = one moe_forward over one batch of synthetic, seeded inputs that
-are already resident in HBM.  Default workload: decode, 1 token, bf16,
-H=2048, E=128, top-8, I=768.  Other workloads (--config) serve for
-measurement of the other shapes; the default is the headline line.
+are already resident in HBM.  Default workload (the JSON line's `value`): the
+8192-token bf16 prefill chunk with Zipf-skewed routing, H=2048, E=128, top-8,
+I=768 -- the largest single-GPU workload and the bf16-MFMA half of the metric.
+The decode workloads of the same layer shape (1 token; 8 tokens with a router
+bias) are measured in the same run and reported under `extra_workloads`, each
+with its own roofline object (`--extra` selects them; `--extra none` skips).
 
-Decode steps rotate over `--copies` copies of the layer's weights (each at its
-own addresses, 16 x 1.2 GB by default) so the 256 MB Infinity Cache cannot
-serve repeats: every step streams its experts from HBM.  The steps are
-captured once into a HIP graph (through torch.cuda.CUDAGraph) and replayed,
-so host launch cost does not hide µs-scale GPU work; replays are checked
-against eager results before timing.
+Weights rotate over `--copies` copies (each at its own addresses: 16 x 1.2 GB
+for decode, 2 for prefill) so the 256 MB Infinity Cache cannot serve repeats:
+every step streams its experts from HBM.  The steps are captured once into a
+HIP graph (through torch.cuda.CUDAGraph) and replayed, so host launch cost
+does not hide us-scale GPU work; replays are checked against eager results
+before timing.
 
-Prints ONE JSON line.  The roofline object reports the dominant kernel (the
-fused decode launch, or the expert gate/up + SwiGLU launch of the staged
-path): algorithmic bytes (decode) or flops (prefill) per launch over its
-average duration.  The durations are HIP events that moe_forward_timed ties
-to that launch's start and end (hipExtLaunchKernelGGL), over a second timed
-pass of the same steps on torch's current stream.  The cpu_baseline object times the fp64 CPU oracle
-on a bounded sample of the same workload.
+The roofline object reports the dominant kernel (the fused decode launch, or
+the expert gate/up + SwiGLU launch of the grouped path): algorithmic bytes
+(decode) or flops (prefill) per launch over its average duration.  The
+durations are HIP events that moe_forward_timed ties to that launch's start
+and end (hipExtLaunchKernelGGL), over a second timed pass of the same steps on
+torch's current stream.  The cpu_baseline object times the fp64 CPU oracle on
+a bounded sample of the headline workload; each decode extra also carries a
+one-thread oracle run.
 """
 from __future__ import annotations
 
@@ -101,49 +105,51 @@ def act_bytes(a: str) -> int:
     return 4 if a == "f32" else 2
 
 
+HEADLINE = "prefill8192"
+DEFAULT_EXTRA = "decode1,decode8"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=None)
-    ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="decode1", choices=sorted(WORKLOADS))
+    ap.add_argument("--steps", type=int, default=None, help="timed steps of the headline workload")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed warm-up steps of the headline workload")
+    ap.add_argument("--config", default=HEADLINE, choices=sorted(WORKLOADS))
+    ap.add_argument("--extra", default=None,
+                    help="comma-separated extra workloads measured after the headline one ('none': skip; "
+                         f"default {DEFAULT_EXTRA} with the default --config, none otherwise)")
     ap.add_argument("--copies", type=int, default=None, help="weight copies rotated over (defeats the MALL)")
     ap.add_argument("--path", default="auto", choices=["auto", "decode", "grouped"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--events-replays", type=int, default=10)
     return ap.parse_args()
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the layer is measured on one MI355X", file=sys.stderr)
-        sys.exit(2)
+def dev(a):
+    import torch
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
 
+
+def measure(config: str, steps, warmup, copies, path_name: str):
+    """Times exactly `steps` moe_forward calls of one workload (after `warmup` untimed ones)
+    and the dominant kernel's launches; returns (line fields, layer inputs, shape)."""
     import torch
     import prefill_moe_router_amd as pm
     import synth
 
-    name, desc = WORKLOADS[args.config]
+    name, desc = WORKLOADS[config]
     sh = synth.CONFIGS[name]
     decode = sh.T <= 8
-    copies = args.copies or (16 if decode else 2)
-    steps = args.steps or (1600 if decode else 20)
-    warmup = args.warmup if args.warmup is not None else (160 if decode else 4)
-    path = {"auto": pm.PATH_AUTO, "decode": pm.PATH_DECODE, "grouped": pm.PATH_GROUPED}[args.path]
+    copies = copies or (16 if decode else 2)
+    steps = steps or (1600 if decode else 20)
+    warmup = warmup if warmup is not None else (160 if decode else 4)
+    path = {"auto": pm.PATH_AUTO, "decode": pm.PATH_DECODE, "grouped": pm.PATH_GROUPED}[path_name]
 
-    torch.cuda.set_device(0)
     t0 = time.time()
     li = synth.make_layer(name)
-    log(f"generated {args.config} inputs in {time.time() - t0:.1f}s")
-
-    def dev(a):
-        if a is None:
-            return None
-        return torch.from_numpy(np.ascontiguousarray(a.view(np.int16) if a.dtype == np.uint16 else a)).cuda()
-
+    log(f"{config}: generated inputs in {time.time() - t0:.1f}s")
     w0 = dict(wg=dev(li.wg), wu=dev(li.wu), wd=dev(li.wd), sg=dev(li.sg), su=dev(li.su), sd=dev(li.sd), ts=li.ts)
     wcopies = [w0] + [{k: (v.clone() if isinstance(v, torch.Tensor) else v) for k, v in w0.items()}
                       for _ in range(copies - 1)]
@@ -158,7 +164,7 @@ def main():
     ids = [torch.empty(sh.T, sh.K, dtype=torch.int32, device="cuda") for _ in range(copies)]
     wts = [torch.empty(sh.T, sh.K, dtype=torch.float32, device="cuda") for _ in range(copies)]
     torch.cuda.synchronize()
-    log(f"resident: {copies} weight copies, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+    log(f"{config}: resident: {copies} weight copies, {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
     def step(b, stream=None):
         pm.forward(shape, xs[b], wr, bias, wcopies[b], ys[b], ws, ids[b], wts[b], stream=stream)
@@ -171,54 +177,62 @@ def main():
     y_eager = [y.clone() for y in ys]
     ids_eager = [i.clone() for i in ids]
 
-    # graph of one sweep over the copies
+    # graphs: one sweep over the copies, and partial sweeps of the first n copies (cached)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
         step(0, stream=s)          # a warm call on the capture stream
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for b in range(copies):
-            step(b)
-    rem = steps % copies
-    g_rem = None
-    if rem:
-        g_rem = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_rem):
-            for b in range(rem):
-                step(b)
+    graphs = {}
+
+    def graph_of(n):
+        if n not in graphs:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for b in range(n):
+                    step(b)
+            graphs[n] = g
+        return graphs[n]
+
+    def replay(n):
+        """Exactly n forward calls: whole sweeps, then the first n % copies copies."""
+        for _ in range(n // copies):
+            graph_of(copies).replay()
+        if n % copies:
+            graph_of(n % copies).replay()
+
+    graph_of(copies)
+    if steps % copies:
+        graph_of(steps % copies)
+    if warmup % copies:
+        graph_of(warmup % copies)
     for r in range(3):
         for y in ys:
             y.fill_(0)
-        g.replay()
+        graph_of(copies).replay()
         torch.cuda.synchronize()
         for b in range(copies):
             assert torch.equal(ys[b], y_eager[b]), f"graph replay {r} differs from eager (copy {b})"
             assert torch.equal(ids[b], ids_eager[b])
-    log("graph replays match eager results")
+    log(f"{config}: graph replays match eager results")
 
-    n_full, n_w = steps // copies, max(1, math.ceil(warmup / copies))
-    for _ in range(n_w):
-        g.replay()
+    replay(warmup)
     torch.cuda.synchronize()
     # ---- timed region: exactly `steps` forward calls ----
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     ev0.record()
-    for _ in range(n_full):
-        g.replay()
-    if g_rem is not None:
-        g_rem.replay()
+    replay(steps)
     ev1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     gpu_ms = ev0.elapsed_time(ev1)
     ms_per_step = wall * 1e3 / steps
     tokens_per_s = sh.T * steps / wall
-    log(f"timed {steps} steps: {wall * 1e3:.2f} ms wall ({gpu_ms:.2f} ms GPU events), {ms_per_step * 1e3:.2f} us/step")
+    log(f"{config}: timed {steps} steps: {wall * 1e3:.2f} ms wall ({gpu_ms:.2f} ms GPU events), "
+        f"{ms_per_step * 1e3:.2f} us/step")
 
     # ---- algorithmic work per step --------------------------------------------------
     bw = weight_bytes_per_elem(sh.w)
@@ -254,7 +268,7 @@ def main():
         kb = layer_bytes if fused else gateup_bytes
         achieved = float(np.mean(kb)) / kern_s / 1e9
         roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=counted_traffic(args.config, dom_name),
+                        frac=round(achieved / HBM_PEAK_GBS, 4), traffic=counted_traffic(config, dom_name),
                         kernel=("decode_fused (whole layer in one launch)" if fused
                                 else "gate_up (expert gate/up GEMV + SwiGLU)"),
                         kernel_us=round(kern_s * 1e6, 3), kernel_us_median=round(float(np.median(durs)) * 1e6, 3),
@@ -262,40 +276,69 @@ def main():
     else:
         achieved = gateup_flops / kern_s / 1e12
         roofline = dict(bound="mfma", achieved=round(achieved, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=counted_traffic(args.config, dom_name),
+                        frac=round(achieved / BF16_PEAK_TFLOPS, 4), traffic=counted_traffic(config, dom_name),
                         kernel="gate_up (grouped expert gate/up + SwiGLU)", kernel_us=round(kern_s * 1e6, 3),
                         kernel_us_median=round(float(np.median(durs)) * 1e6, 3), algorithmic_flops=gateup_flops)
-    log(f"dominant kernel {dom_name}: {kern_s * 1e6:.2f} us avg over {len(durs)} launches")
+    log(f"{config}: dominant kernel {dom_name}: {kern_s * 1e6:.2f} us avg over {len(durs)} launches")
 
     layer_s = wall / steps
-    extra = dict(layer_us=round(layer_s * 1e6, 3), unique_experts_mean=float(np.mean(U)),
-                 stages=stages)
+    layer = dict(layer_us=round(layer_s * 1e6, 3), unique_experts_mean=float(np.mean(U)), stages=stages)
     if decode:
         gbs = float(np.mean(layer_bytes)) / layer_s / 1e9
-        extra.update(layer_bytes=round(float(np.mean(layer_bytes))), layer_gbs=round(gbs, 1),
+        layer.update(layer_bytes=round(float(np.mean(layer_bytes))), layer_gbs=round(gbs, 1),
                      layer_hbm_frac=round(gbs / HBM_PEAK_GBS, 4))
     else:
         tf = layer_flops / layer_s / 1e12
-        extra.update(layer_flops=layer_flops, layer_tflops=round(tf, 2),
+        layer.update(layer_flops=layer_flops, layer_tflops=round(tf, 2),
                      layer_mfma_frac=round(tf / BF16_PEAK_TFLOPS, 4))
+    fields = dict(value=round(tokens_per_s, 1), unit="tokens/s", steps=steps, warmup=warmup,
+                  ms_per_step=round(ms_per_step, 6), dtype=sh.w if sh.w != "f32" else "f32",
+                  config={"workload": desc, "tokens_per_step": sh.T, "hidden": sh.H, "experts": sh.E,
+                          "top_k": sh.K, "intermediate": sh.I, "weight_copies": copies,
+                          "parallelism": "single GPU"},
+                  roofline=roofline, layer=layer)
+    del wcopies, w0, xs, ys, ws, graphs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return fields, li, sh
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the layer is measured on one MI355X", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    torch.cuda.set_device(0)
+
+    head, li, sh = measure(args.config, args.steps, args.warmup, args.copies, args.path)
+    extra_names = args.extra if args.extra is not None else (DEFAULT_EXTRA if args.config == HEADLINE else "none")
+    extras = {}
+    cpu_extra = {}
+    for cfg in [c for c in extra_names.split(",") if c and c != "none"]:
+        f, li_x, sh_x = measure(cfg, None, None, None, "auto")
+        extras[cfg] = f
+        if not args.no_cpu_baseline and sh_x.T <= 8:
+            cpu_extra[cfg] = (li_x, sh_x)
 
     out = {
-        "metric": METRIC, "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-        "warmup": n_w * copies, "ms_per_step": round(ms_per_step, 6), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": sh.w if sh.w != "f32" else "f32",
+        "metric": METRIC, "value": head["value"], "unit": "tokens/s", "n_gpus": 1, "steps": head["steps"],
+        "warmup": head["warmup"], "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": head["dtype"],
         "data": "synthetic (seeded N(0,1) activations, N(0,sd) random-init weights)",
-        "config": {"workload": desc, "tokens_per_step": sh.T, "hidden": sh.H, "experts": sh.E, "top_k": sh.K,
-                   "intermediate": sh.I, "weight_copies": copies, "parallelism": "single GPU"},
-        "roofline": roofline,
-        "layer": extra,
+        "config": head["config"], "roofline": head["roofline"], "layer": head["layer"],
     }
-
+    if extras:
+        out["extra_workloads"] = extras
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(li, sh, args.cpu_seconds)
+        for cfg, (li_x, sh_x) in cpu_extra.items():
+            extras[cfg]["cpu_baseline_1thread"] = cpu_baseline(li_x, sh_x, args.cpu_seconds / 3, threads=1)
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(li, sh, target_s: float) -> dict:
+def cpu_baseline(li, sh, target_s: float, threads=None) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same workload."""
     import oracle
     import synth
@@ -305,32 +348,39 @@ def cpu_baseline(li, sh, target_s: float) -> dict:
                             bias=li.bias, sg=li.sg, su=li.su, sd=li.sd,
                             fmt="nvfp4" if sh.w == "nvfp4" else None, ts=li.ts)
 
-    threads = oracle.num_threads()
-    if sh.T <= 8:
-        # independent decode steps: batches of the same shape stacked into one oracle call
-        def run(nsteps):
-            x = np.concatenate([synth.make_x(sh, seed=0, batch=100 + b) for b in range(nsteps)])
-            t = time.perf_counter()
-            oracle.forward(layer_for(x))
-            return time.perf_counter() - t, nsteps * sh.T
-        dt, n = run(max(1, threads // sh.T))
-        nsteps = max(1, int(max(1, threads // sh.T) * target_s / max(dt, 1e-3)))
-        dt, n = run(nsteps)
-        sample = f"{nsteps} independent {sh.T}-token decode steps ({n} token rows) in one oracle call"
-    else:
-        x = li.x
+    full = oracle.num_threads()
+    if threads is not None:
+        oracle.set_num_threads(threads)
+    try:
+        nthr = oracle.num_threads()
+        if sh.T <= 8:
+            # independent decode steps: batches of the same shape stacked into one oracle call
+            def run(nsteps):
+                x = np.concatenate([synth.make_x(sh, seed=0, batch=100 + b) for b in range(nsteps)])
+                t = time.perf_counter()
+                oracle.forward(layer_for(x))
+                return time.perf_counter() - t, nsteps * sh.T
+            probe = max(1, nthr // sh.T)
+            dt, n = run(probe)
+            nsteps = max(1, int(probe * target_s / max(dt, 1e-3)))
+            dt, n = run(nsteps)
+            sample = f"{nsteps} independent {sh.T}-token decode steps ({n} token rows) in one oracle call"
+        else:
+            x = li.x
 
-        def run(ntok):
-            toks = np.linspace(0, sh.T - 1, ntok).astype(np.int32)
-            t = time.perf_counter()
-            oracle.forward(layer_for(x), tokens=toks)
-            return time.perf_counter() - t, ntok
-        dt, n = run(threads)
-        ntok = max(1, int(threads * target_s / max(dt, 1e-3)))
-        dt, n = run(ntok)
-        sample = f"{ntok} tokens spread over the {sh.T}-token chunk (whole layer per token)"
-    log(f"cpu baseline: {n} tokens in {dt:.1f}s on {min(threads, n)} threads")
-    return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(min(threads, n)), kind="oracle",
+            def run(ntok):
+                toks = np.linspace(0, sh.T - 1, ntok).astype(np.int32)
+                t = time.perf_counter()
+                oracle.forward(layer_for(x), tokens=toks)
+                return time.perf_counter() - t, ntok
+            dt, n = run(nthr)
+            ntok = max(1, int(nthr * target_s / max(dt, 1e-3)))
+            dt, n = run(ntok)
+            sample = f"{ntok} tokens spread over the {sh.T}-token chunk (whole layer per token)"
+    finally:
+        oracle.set_num_threads(full)
+    log(f"cpu baseline: {n} tokens in {dt:.1f}s on {min(nthr, n)} threads")
+    return dict(value=round(n / dt, 3), unit="tokens/s", cores=int(min(nthr, n)), kind="oracle",
                 sample=sample, seconds=round(dt, 2))
 
 
