@@ -209,6 +209,35 @@ const char *moe_forward_stages(const moe_shape *shape);
  */
 moe_status moe_check_device_error(void *ws, int32_t *err_bits, void *stream);
 
+/* Bytes of device memory the library keeps per device for moe_forward_noalloc. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The workspace is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's own device memory, one per device,
+ * held until the process ends; nothing is allocated, by the library or by the
+ * HIP runtime on its behalf.  Shapes whose moe_workspace_size exceeds it get
+ * MOE_ERR_WORKSPACE before anything is enqueued: every decode batch of up to 8
+ * tokens of every supported shape fits (at most 12.2 MiB), and medium batches of
+ * up to ~200 tokens of the H=2048 / E=128 / k=8 / I=768 shape.
+ *   - All calls on one device share that device's array, which keeps the last
+ *     call's contents: calls that overlap on one device (on different streams
+ *     or threads) race and must be serialised by the caller.
+ *   - The first call on each device also clears the whole array on `stream`
+ *     before its launches; a graph that captures that call clears it at every
+ *     replay.
+ *   - device_err (optional, 16-byte aligned device int32): receives the call's
+ *     MOE_DEVERR_* bits (enqueued after the layer; the word is then cleared),
+ *     as moe_check_device_error reports them for a caller-owned workspace.
+ * Everything else (arguments, results, errors) is as for moe_forward.
+ */
+moe_status moe_forward_noalloc(const moe_shape *shape, const void *x, const void *w_router,
+                               const float *bias, const moe_expert_weights *w, void *y,
+                               int32_t *topk_ids_out, float *topk_w_out, int32_t *device_err,
+                               void *stream);
+
 /* Static text for a status code. */
 const char *moe_status_string(moe_status status);
 

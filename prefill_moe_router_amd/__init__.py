@@ -32,7 +32,7 @@ DEVERR_BAD_EXPERT_ID, DEVERR_TIMEOUT = 1, 2
 
 EXPORTS = ["moe_workspace_size", "moe_router_topk", "moe_group_tokens", "moe_expert_ffn", "moe_combine",
            "moe_forward", "moe_forward_timed", "moe_forward_stages", "moe_forward_grouping",
-           "moe_check_device_error", "moe_status_string"]
+           "moe_check_device_error", "moe_status_string", "moe_forward_noalloc"]
 
 
 class MoeError(RuntimeError):
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_stages.argtypes = [PS]
         L.moe_forward_grouping.restype = i32
         L.moe_forward_grouping.argtypes = [PS, vp, sz, vp, vp, vp, vp]
+        L.moe_forward_noalloc.restype = i32
+        L.moe_forward_noalloc.argtypes = [PS, vp, vp, vp, PW, vp, vp, vp, vp, vp]
         L.moe_check_device_error.restype = i32
         L.moe_check_device_error.argtypes = [vp, ctypes.POINTER(i32), vp]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -181,6 +183,19 @@ def forward(shape: LayerShape, x, w_router, bias, weights: dict, y, ws, topk_ids
     w = _weights(**weights)
     _check(lib().moe_forward(ctypes.byref(s), _p(x), _p(w_router), _p(bias), ctypes.byref(w), _p(y),
                              _p(topk_ids), _p(topk_w), _p(ws), ws.numel(), _stream(stream)), "moe_forward")
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def forward_noalloc(shape: LayerShape, x, w_router, bias, weights: dict, y, topk_ids=None, topk_w=None,
+                    device_err=None, stream=None):
+    """moe_forward on the library's own per-device scratch (no workspace argument)."""
+    s = shape.c()
+    w = _weights(**weights)
+    _check(lib().moe_forward_noalloc(ctypes.byref(s), _p(x), _p(w_router), _p(bias), ctypes.byref(w), _p(y),
+                                     _p(topk_ids), _p(topk_w), _p(device_err), _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def forward_timed(shape: LayerShape, x, w_router, bias, weights: dict, y, ws, stage_events, topk_ids=None,

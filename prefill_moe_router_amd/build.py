@@ -15,7 +15,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["moe_api.hip", "router.hip", "group.hip", "decode_ffn.hip", "combine.hip", "decode_fused.hip",
-           "grouped_gemm.hip", "grouped_gemm_wide.hip"]
+           "grouped_gemm.hip", "grouped_gemm_wide.hip", "noalloc.hip"]
 
 CFLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",

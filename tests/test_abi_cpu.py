@@ -135,6 +135,25 @@ def test_forward_grouping_validation():
     assert grp(_shape(top_k=0), nbytes=1 << 30) == pm.ERR_INVALID_ARG
 
 
+def test_noalloc_refuses_shapes_beyond_its_scratch_before_any_device_call():
+    """moe_forward_noalloc checks the shape's workspace need against its fixed per-device
+    scratch first: too large gives MOE_ERR_WORKSPACE, a bad shape MOE_ERR_INVALID_ARG, a
+    misaligned error word MOE_ERR_INVALID_ARG (no device needed for any of these)."""
+    L = pm.lib()
+    w = pm.ExpertWeights(FAKE, FAKE, FAKE, None, None, None)
+    def call(shp, err=None):
+        s = shp.c()
+        return L.moe_forward_noalloc(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, err, None)
+    big = _shape(num_tokens=8192)
+    assert pm.workspace_size(big) > pm.NOALLOC_SCRATCH_BYTES
+    assert call(big) == pm.ERR_WORKSPACE
+    assert call(_shape(top_k=0)) == pm.ERR_INVALID_ARG
+    assert call(_shape(num_tokens=1), err=FAKE + 4) == pm.ERR_INVALID_ARG
+    # every decode batch of the largest supported shape fits
+    assert pm.workspace_size(_shape(num_tokens=8, hidden=8192, intermediate=8192, num_experts=1024,
+                                    top_k=32)) <= pm.NOALLOC_SCRATCH_BYTES
+
+
 def test_nvfp4_validation():
     """NVFP4 experts: scale arrays required and 16-byte aligned, finite tensor scales; AUTO
     takes the grouped GEMMs from four pairs per expert (MXFP4: three)."""
