@@ -89,6 +89,11 @@ WORKLOADS = {
                           "prefill chunk, 4096 tokens, NVFP4 experts: H=4096, E=256, top-8, I=1024"),
     "mxfp4_prefill4096": ("c4_mxfp4_prefill4096",
                           "prefill chunk, 4096 tokens, MXFP4 experts: H=4096, E=256, top-8, I=1024"),
+    "mxint8_decode1": ("c6_mxint8_decode1", "decode, 1 token, MXINT8 experts (int8, E8M0 scale per 32), bf16 "
+                       "acts: H=4096, E=256, top-8, I=1024"),
+    "mxint8_decode8": ("c6_mxint8_decode8", "decode, 8 tokens, MXINT8 experts: H=4096, E=256, top-8, I=1024"),
+    "mxint8_prefill4096": ("c6_mxint8_prefill4096",
+                           "prefill chunk, 4096 tokens, MXINT8 experts: H=4096, E=256, top-8, I=1024"),
     "tiny": ("c0_tiny_f32", "tiny fp32: 4 tokens, H=256, E=8, top-2, I=128"),
 }
 
@@ -98,7 +103,8 @@ def log(msg):
 
 
 def weight_bytes_per_elem(w: str) -> float:
-    return {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0, "nvfp4": 0.5 + 1.0 / 16.0}[w]
+    return {"f32": 4.0, "bf16": 2.0, "mxfp4": 0.5 + 1.0 / 32.0, "nvfp4": 0.5 + 1.0 / 16.0,
+            "mxint8": 1.0 + 1.0 / 32.0}[w]
 
 
 def act_bytes(a: str) -> int:
@@ -157,7 +163,8 @@ def measure(config: str, steps, warmup, copies, path_name: str):
     xs = [dev(synth.make_x(sh, seed=0, batch=b)) for b in range(copies)]
     shape = pm.LayerShape(sh.T, sh.H, sh.E, sh.K, sh.I, sh.renorm,
                           pm.F32 if sh.act == "f32" else pm.BF16,
-                          {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4}[sh.w], path)
+                          {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4,
+                           "mxint8": pm.MXINT8}[sh.w], path)
     ws = pm.alloc_workspace(shape)
     ydt = torch.float32 if sh.act == "f32" else torch.int16
     ys = [torch.empty(sh.T, sh.H, dtype=ydt, device="cuda") for _ in range(copies)]

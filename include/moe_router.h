@@ -64,12 +64,16 @@ enum {
 /* element formats.  MOE_NVFP4: two E2M1 codes per byte as for MXFP4, one OCP FP8 E4M3
    scale byte (bias 7, the NaN codes 0x7F / 0xFF not allowed) per 16 consecutive
    contraction elements, and one fp32 scale per weight tensor: an element is
-   e2m1(code) * e4m3(block scale) * tensor scale. */
-enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_NVFP4 = 3 };
+   e2m1(code) * e4m3(block scale) * tensor scale.  MOE_MXINT8 (OCP MX INT8): one int8
+   two's complement code per byte with an implicit scale of 2^-6, and one E8M0 scale
+   byte per 32 consecutive contraction elements: an element is code * 2^(scale - 133)
+   (block-int8 experts, the format of the fused int8 MoE path of "第 9 章 prefill：
+   最大的瓶颈" §9.9; the kernels stay exact for scale codes 8..254). */
+enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_NVFP4 = 3, MOE_MXINT8 = 4 };
 
 /* expert-FFN kernel family; AUTO picks DECODE for T <= 8 and while T * top_k < 2 * E (bf16
-   experts), < 3 * E (MXFP4) or < 4 * E (NVFP4), GROUPED above (bf16, MXFP4 and NVFP4
-   experts with bf16 activations) */
+   experts), < 3 * E (MXFP4, MXINT8) or < 4 * E (NVFP4), GROUPED above (bf16, MXFP4, NVFP4
+   and MXINT8 experts with bf16 activations) */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
 /* device error bits reported by moe_check_device_error */
@@ -77,22 +81,23 @@ enum { MOE_DEVERR_BAD_EXPERT_ID = 1, MOE_DEVERR_TIMEOUT = 2 };
 
 typedef struct moe_shape {
     int32_t num_tokens;    /* T >= 0; T == 0 is a no-op                       */
-    int32_t hidden;        /* H, multiple of 8 (of 32 for MXFP4 / NVFP4), <= 8192 */
+    int32_t hidden;        /* H, multiple of 8 (of 32 for MXFP4 / NVFP4 / MXINT8), <= 8192 */
     int32_t num_experts;   /* E, 1..1024                                       */
     int32_t top_k;         /* k, 1..min(E, 32)                                 */
-    int32_t intermediate;  /* I, multiple of 8 (of 32 for MXFP4 / NVFP4), <= 8192 */
+    int32_t intermediate;  /* I, multiple of 8 (of 32 for MXFP4 / NVFP4 / MXINT8), <= 8192 */
     int32_t renormalize;   /* nonzero: kept gate weights rescaled to sum 1     */
     int32_t act_dtype;     /* x, router weight, y: MOE_F32 or MOE_BF16         */
     int32_t weight_dtype;  /* experts: MOE_F32 (with F32 acts), MOE_BF16,
-                              MOE_MXFP4 or MOE_NVFP4 (with BF16 acts)          */
+                              MOE_MXFP4, MOE_NVFP4 or MOE_MXINT8 (BF16 acts)   */
     int32_t path;          /* MOE_PATH_*                                        */
 } moe_shape;
 
 typedef struct moe_expert_weights {
-    const void *w_gate;    /* [E][I][H]   (MXFP4 / NVFP4: [E][I][H/2] bytes)   */
+    const void *w_gate;    /* [E][I][H]   (MXFP4 / NVFP4: [E][I][H/2] bytes;
+                              MXINT8: [E][I][H] int8 codes)                    */
     const void *w_up;      /* [E][I][H]                                        */
     const void *w_down;    /* [E][H][I]   (MXFP4 / NVFP4: [E][H][I/2] bytes)   */
-    const uint8_t *s_gate; /* MXFP4: E8M0 scales [E][I][H/32];
+    const uint8_t *s_gate; /* MXFP4, MXINT8: E8M0 scales [E][I][H/32];
                               NVFP4: E4M3 scales [E][I][H/16]; else unused    */
     const uint8_t *s_up;   /* [E][I][H/32] or [E][I][H/16]                     */
     const uint8_t *s_down; /* [E][H][I/32] or [E][H][I/16]                     */

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(HERE, "libmoe_router.so")
 # status codes
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_DEVICE = 0, -1, -2, -3, -4, -5
 # element formats
-F32, BF16, MXFP4, NVFP4 = 0, 1, 2, 3
+F32, BF16, MXFP4, NVFP4, MXINT8 = 0, 1, 2, 3, 4
 # expert FFN kernel family
 PATH_AUTO, PATH_DECODE, PATH_GROUPED = 0, 1, 2
 # device error bits

@@ -29,9 +29,10 @@ constexpr int SNT = 256;                    // threads per work-group
 constexpr int SWAVES = SNT / WAVE;
 constexpr size_t STAGE_BYTES = 64 * 1024;   // LDS for staged activation rows
 
-// 16-byte words per weight chunk once decoded: 4 for MXFP4 (32 bf16), else 1
+// 16-byte words per weight chunk once decoded: 4 for MXFP4 / NVFP4 (32 bf16), 2 for
+// MXINT8 (16 bf16), else 1
 template <class F>
-constexpr int dec_words() { return F::EPC == 32 ? 4 : 1; }
+constexpr int dec_words() { return F::EPC == 32 ? 4 : F::EPC == 16 ? 2 : 1; }
 
 // sum over groups of LPR consecutive lanes; the total lands in the group's last lane
 template <int LPR>
@@ -68,6 +69,16 @@ __device__ __forceinline__ void load_chunk(const uint8_t *row, const uint8_t *sr
             w[u][1] = bf16x2_mul_exact(fp4x2_to_bf16x2<1>(q[u], s), f);
             w[u][2] = bf16x2_mul_exact(fp4x2_to_bf16x2<2>(q[u], s), f);
             w[u][3] = bf16x2_mul_exact(fp4x2_to_bf16x2<3>(q[u], s), f);
+        }
+    } else if constexpr (W == 2) {
+        // MXINT8: codes times the block's power of two (exact in bf16)
+        const float s = mxint8_scale(load_scale<F>(srow, ch));
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            w[u][0] = i8x2_to_bf16x2<0>(q[2 * u], s);
+            w[u][1] = i8x2_to_bf16x2<1>(q[2 * u], s);
+            w[u][2] = i8x2_to_bf16x2<0>(q[2 * u + 1], s);
+            w[u][3] = i8x2_to_bf16x2<1>(q[2 * u + 1], s);
         }
     } else if constexpr (W == 4) {
         const float s = e8m0_to_f32(srow[ch]);
@@ -157,7 +168,7 @@ __global__ __launch_bounds__(SNT) void stream_ffn_kernel(StreamParams p) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int grp = lane / LPR, li = lane % LPR;
     const int nch = p.K / F::EPC;
-    const size_t wrow = (size_t)nch * 16, srow = (size_t)nch * (F::SCALED ? F::SB : 1);
+    const size_t wrow = (size_t)nch * 16, srow = scale_row_bytes<F>(nch);
     const int ab = p.act_f32 ? 4 : 2;
     const size_t xrow = (size_t)p.K * ab;                 // bytes of one activation row
 
@@ -316,7 +327,7 @@ static hipError_t stream_launch(StreamParams prm, const moe_shape &s, hipStream_
 
 bool stream_ffn_supported(const moe_shape &s) {
     const size_t ab = act_bytes(s.act_dtype);
-    const int epc = s.weight_dtype == MOE_BF16 ? 8 : s.weight_dtype == MOE_F32 ? 4 : 32;
+    const int epc = weight_chunk_elems(s.weight_dtype);
     // one activation row must fit the staging area; rows of at most 16 chunks per lane
     return (size_t)s.hidden * ab <= STAGE_BYTES && (size_t)s.intermediate * ab <= STAGE_BYTES &&
            s.hidden / epc <= 64 * 16 && s.intermediate / epc <= 64 * 16;
@@ -346,6 +357,7 @@ hipError_t launch_decode_gateup(const moe_shape &s, const void *x, const moe_exp
         case MOE_F32: return stream_launch<FmtF32, true>(prm, s, st);
         case MOE_BF16: return stream_launch<FmtBF16, true>(prm, s, st);
         case MOE_NVFP4: return stream_launch<FmtNV4, true>(prm, s, st);
+        case MOE_MXINT8: return stream_launch<FmtI8, true>(prm, s, st);
         default: return stream_launch<FmtMX4, true>(prm, s, st);
     }
 }
@@ -369,6 +381,7 @@ hipError_t launch_decode_down(const moe_shape &s, const moe_expert_weights &w, c
         case MOE_F32: return stream_launch<FmtF32, false>(prm, s, st);
         case MOE_BF16: return stream_launch<FmtBF16, false>(prm, s, st);
         case MOE_NVFP4: return stream_launch<FmtNV4, false>(prm, s, st);
+        case MOE_MXINT8: return stream_launch<FmtI8, false>(prm, s, st);
         default: return stream_launch<FmtMX4, false>(prm, s, st);
     }
 }

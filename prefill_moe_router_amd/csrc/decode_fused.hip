@@ -390,10 +390,10 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         auto fetch = [&](int q, uint4 (&g)[CG], uint32_t (&gsc)[CG], uint4 (&u)[CG], uint32_t (&usc)[CG]) {
             const int uu = q / I, i = q - uu * I;
             const size_t rsel = (size_t)s_act_e[uu] * I + i;
-            load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * nch * F::SB : nullptr, nch, lane, WAVE,
-                               g, gsc);
-            load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * nch * F::SB : nullptr, nch, lane, WAVE,
-                               u, usc);
+            load_chunks<F, CG>(p.wg + rsel * nch * 16, F::SCALED ? p.sg + rsel * scale_row_bytes<F>(nch) : nullptr, nch,
+                               lane, WAVE, g, gsc);
+            load_chunks<F, CG>(p.wu + rsel * nch * 16, F::SCALED ? p.su + rsel * scale_row_bytes<F>(nch) : nullptr, nch,
+                               lane, WAVE, u, usc);
         };
         auto consume = [&](int q, const uint4 (&g)[CG], const uint32_t (&gsc)[CG], const uint4 (&u)[CG],
                            const uint32_t (&usc)[CG]) {
@@ -556,7 +556,7 @@ bool decode_fused_supported(const moe_shape &s) {
     const size_t ab = act_bytes(s.act_dtype);
     const size_t P = (size_t)s.num_tokens * s.top_k;
     if (s.num_tokens < 1 || s.num_tokens > FMAX_T || P > FMAX_P) return false;
-    const int epc = s.weight_dtype == MOE_F32 ? 4 : s.weight_dtype == MOE_BF16 ? 8 : 32;
+    const int epc = weight_chunk_elems(s.weight_dtype);
     const int aepc = s.act_dtype == MOE_F32 ? 4 : 8;
     if ((s.hidden / epc + WAVE - 1) / WAVE > FMAX_C) return false;          // gate/up rows
     if ((s.hidden / aepc + WAVE - 1) / WAVE > FMAX_C) return false;         // router rows
@@ -612,6 +612,8 @@ static hipError_t fused_dispatch(const moe_shape &s, const FusedParams &prm, siz
     MOE_FL(2, 2, 2);
     MOE_FL(8, 8, 2);   // H 4096 bf16
     MOE_FL(8, 8, 4);
+    MOE_FL(2, 4, 2);   // H 2048 MXINT8, I 768
+    MOE_FL(4, 8, 1);   // H 4096 MXINT8, I 1024
 #undef MOE_FL
     return hipErrorInvalidConfiguration;
 }
@@ -654,6 +656,8 @@ static bool fused_fits(const moe_shape &s) {
     MOE_FF(2, 2, 2);
     MOE_FF(8, 8, 2);
     MOE_FF(8, 8, 4);
+    MOE_FF(2, 4, 2);
+    MOE_FF(4, 8, 1);
 #undef MOE_FF
     return false;
 }
@@ -668,6 +672,7 @@ bool decode_fused_coresident(const moe_shape &s) {
         case MOE_F32: return fused_fits<FmtF32, FmtF32>(s);
         case MOE_BF16: return fused_fits<FmtBF16, FmtBF16>(s);
         case MOE_NVFP4: return fused_fits<FmtNV4, FmtBF16>(s);
+        case MOE_MXINT8: return fused_fits<FmtI8, FmtBF16>(s);
         default: return fused_fits<FmtMX4, FmtBF16>(s);
     }
 }
@@ -675,7 +680,8 @@ bool decode_fused_coresident(const moe_shape &s) {
 // (gate/up, router, down) chunk buckets the fused kernel is built for
 static bool fused_bucket_built(int cg, int cr, int cd) {
     static const int combos[][3] = {{4, 4, 2}, {4, 4, 1}, {4, 4, 4}, {2, 8, 1}, {2, 8, 2}, {1, 4, 1},
-                                    {1, 1, 1}, {1, 1, 2}, {2, 2, 1}, {2, 2, 2}, {8, 8, 2}, {8, 8, 4}};
+                                    {1, 1, 1}, {1, 1, 2}, {2, 2, 1}, {2, 2, 2}, {8, 8, 2}, {8, 8, 4},
+                                    {2, 4, 2}, {4, 8, 1}};
     for (const auto &c : combos)
         if (c[0] == cg && c[1] == cr && c[2] == cd) return true;
     return false;
@@ -725,6 +731,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
         case MOE_F32: return fused_dispatch<FmtF32, FmtF32>(s, prm, lds, st, ev0, ev1);
         case MOE_BF16: return fused_dispatch<FmtBF16, FmtBF16>(s, prm, lds, st, ev0, ev1);
         case MOE_NVFP4: return fused_dispatch<FmtNV4, FmtBF16>(s, prm, lds, st, ev0, ev1);
+        case MOE_MXINT8: return fused_dispatch<FmtI8, FmtBF16>(s, prm, lds, st, ev0, ev1);
         default: return fused_dispatch<FmtMX4, FmtBF16>(s, prm, lds, st, ev0, ev1);
     }
 }

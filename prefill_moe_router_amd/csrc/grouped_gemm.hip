@@ -62,7 +62,7 @@ __device__ __forceinline__ int find_expert(const int32_t *mtile_off, int E, int 
 // BM x BN output tile per matrix (NB = 2 matrices, gate and up, for GATEUP), K steps
 // of BK, WM x WN waves, each wave MI x NJ blocks of 32x32 per matrix.  LDS rows are
 // padded by 16 bytes so 16 consecutive rows read at one k offset hit distinct banks.
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX, bool NV = false>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX, bool NV = false, bool I8 = false>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p) {
     constexpr int NTH = WM * WN * 64;
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
@@ -130,11 +130,14 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
 #pragma unroll
         for (int i = 0; i < BR; ++i) brow[b][i] = MX ? nullptr : base + (size_t)(sr + RPP * i) * krow + sc * 16;
     }
-    // MXFP4 weights: a 16-byte chunk of E2M1 codes (32 K elements, one scale block) per
-    // (weight row, chunk); dequantised to bf16 while it is written to LDS
-    constexpr int CQ = BK / 32;                                   // code chunks per row and K step
+    // MXFP4 / NVFP4 weights: a 16-byte chunk of E2M1 codes (32 K elements) per (weight row,
+    // chunk); MXINT8 (I8): a 16-byte chunk of int8 codes (16 K elements, half a scale
+    // block).  Dequantised to bf16 while it is written to LDS.
+    static_assert(!I8 || (MX && !NV), "MXINT8 takes the coded-weight path");
+    constexpr int QE = I8 ? 16 : 32;                              // K elements per code chunk
+    constexpr int CQ = BK / QE;                                   // code chunks per row and K step
     constexpr int BQ = MX ? NB * BN * CQ / NTH : 1;               // code chunks staged per thread
-    static_assert(!MX || BQ * NTH == NB * BN * CQ, "MXFP4 staging must tile the block");
+    static_assert(!MX || BQ * NTH == NB * BN * CQ, "coded-weight staging must tile the block");
     const uint8_t *bqrow[BQ], *bqsc[BQ];
     int bqlds[BQ];
 #pragma unroll
@@ -142,9 +145,10 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         const int idx = tid + NTH * i, r = idx / CQ, c = idx % CQ;   // r: row over both matrices
         const int b = r / BN, rr = r % BN;
         const size_t grow = (size_t)e * p.N + n0 + rr;
-        bqrow[i] = MX ? (b == 0 ? p.b0 : p.b1) + grow * (size_t)(p.K / 2) + c * 16 : nullptr;
-        bqsc[i] = MX ? (b == 0 ? p.s0 : p.s1) + grow * (size_t)(p.K / (NV ? 16 : 32)) + c * (NV ? 2 : 1) : nullptr;
-        bqlds[i] = (BM + r) * GROW + c * 64;
+        bqrow[i] = MX ? (b == 0 ? p.b0 : p.b1) + grow * (size_t)(I8 ? p.K : p.K / 2) + c * 16 : nullptr;
+        bqsc[i] = MX ? (b == 0 ? p.s0 : p.s1) + grow * (size_t)(p.K / (NV ? 16 : 32)) + (I8 ? c / 2 : c * (NV ? 2 : 1))
+                     : nullptr;
+        bqlds[i] = (BM + r) * GROW + c * QE * 2;
     }
 
     // two register sets: a K slice is loaded one whole step before it is written to LDS
@@ -158,9 +162,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         _Pragma("unroll") for (int i = 0; i < AR; ++i) RA[i] = *reinterpret_cast<const u32x4_t *>(arow[i] + ko_); \
         if constexpr (MX) {                                                                               \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
-                RQ[i] = *reinterpret_cast<const u32x4_t *>(bqrow[i] + (size_t)(kt) * (BK / 2));           \
+                RQ[i] = *reinterpret_cast<const u32x4_t *>(bqrow[i] + (size_t)(kt) * (I8 ? BK : BK / 2)); \
                 RS[i] = NV ? (uint32_t) * reinterpret_cast<const uint16_t *>(bqsc[i] + (kt) * CQ * 2)      \
-                           : (uint32_t)bqsc[i][(kt) * CQ];                                                 \
+                           : (uint32_t)bqsc[i][(kt) * (BK / 32)];                                          \
             }                                                                                             \
         } else {                                                                                          \
             _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
@@ -188,6 +192,19 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
                     o_[1] = bf16x2_mul_exact(fp4x2_to_bf16x2<1>(cw, s_), f2_);                            \
                     o_[2] = bf16x2_mul_exact(fp4x2_to_bf16x2<2>(cw, s_), f2_);                            \
                     o_[3] = bf16x2_mul_exact(fp4x2_to_bf16x2<3>(cw, s_), f2_);                            \
+                    *reinterpret_cast<u32x4_t *>(base_ + bqlds[i] + w * 16) = o_;                         \
+                }                                                                                         \
+            }                                                                                             \
+        } else if constexpr (I8) {                                                                        \
+            /* MXINT8: each code times the block's power of two (exact in bf16) */                        \
+            _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
+                const float s_ = mxint8_scale(RS[i]);                                                     \
+                _Pragma("unroll") for (int w = 0; w < 2; ++w) {                                           \
+                    u32x4_t o_;                                                                           \
+                    o_[0] = i8x2_to_bf16x2<0>(RQ[i][2 * w], s_);                                          \
+                    o_[1] = i8x2_to_bf16x2<1>(RQ[i][2 * w], s_);                                          \
+                    o_[2] = i8x2_to_bf16x2<0>(RQ[i][2 * w + 1], s_);                                      \
+                    o_[3] = i8x2_to_bf16x2<1>(RQ[i][2 * w + 1], s_);                                      \
                     *reinterpret_cast<u32x4_t *>(base_ + bqlds[i] + w * 16) = o_;                         \
                 }                                                                                         \
             }                                                                                             \
@@ -441,7 +458,8 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const uint16_t *__res
 
 bool grouped_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 &&
-           (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4 || s.weight_dtype == MOE_NVFP4) &&
+           (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4 || s.weight_dtype == MOE_NVFP4 ||
+            s.weight_dtype == MOE_MXINT8) &&
            s.hidden % CfgDN::BN == 0 && s.hidden % CfgGU::BK == 0 && s.intermediate % CfgGU::BN == 0 &&
            s.intermediate % CfgDN::BK == 0;
 }
@@ -450,7 +468,7 @@ bool router_mfma_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 && s.num_experts % CfgR::BN == 0 && s.hidden % CfgR::BK == 0;
 }
 
-template <int MODE, class C, bool MX = false, bool NV = false>
+template <int MODE, class C, bool MX = false, bool NV = false, bool I8 = false>
 static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
     constexpr size_t stage_bytes = C::NS * (size_t)(C::BM + NB * C::BN) * (C::BK * 2 + 16);
@@ -458,7 +476,7 @@ static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
     static_assert(lds <= 158 * 1024, "LDS budget");
     static bool attr_done = false;
-    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX, NV>;
+    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX, NV, I8>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -530,6 +548,7 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.nt = s.intermediate / CfgGU::BN;
     if (s.weight_dtype == MOE_MXFP4) return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
     if (s.weight_dtype == MOE_NVFP4) return gemm_launch<GM_GATEUP, CfgGU, true, true>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXINT8) return gemm_launch<GM_GATEUP, CfgGU, true, false, true>(prm, st, ev0, ev1);
     return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
 }
 
@@ -553,11 +572,13 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
     prm.E = s.num_experts;
     prm.mt_max = mt_max_of(s);
     prm.nt = s.hidden / CfgDN::BN;
-    const bool mx = s.weight_dtype == MOE_MXFP4, nv = s.weight_dtype == MOE_NVFP4;
+    const bool mx = s.weight_dtype == MOE_MXFP4, nv = s.weight_dtype == MOE_NVFP4, i8 = s.weight_dtype == MOE_MXINT8;
     if (f32_sorted) return nv ? gemm_launch<GM_DOWN_F32, CfgDN, true, true>(prm, st, ev0, ev1)
+                         : i8 ? gemm_launch<GM_DOWN_F32, CfgDN, true, false, true>(prm, st, ev0, ev1)
                          : mx ? gemm_launch<GM_DOWN_F32, CfgDN, true>(prm, st, ev0, ev1)
                               : gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
     if (nv) return gemm_launch<GM_DOWN, CfgDN, true, true>(prm, st, ev0, ev1);
+    if (i8) return gemm_launch<GM_DOWN, CfgDN, true, false, true>(prm, st, ev0, ev1);
     return mx ? gemm_launch<GM_DOWN, CfgDN, true>(prm, st, ev0, ev1) : gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
 }
 

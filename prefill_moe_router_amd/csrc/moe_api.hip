@@ -17,6 +17,8 @@ constexpr int MAX_DIM = 8192;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// H and I must be multiples of this: a 16-byte chunk (fp32, bf16) or a 32-element scale
+// block (MXFP4, NVFP4 in pairs of 16-element blocks, MXINT8)
 int weight_epc(int wdt) { return wdt == MOE_F32 ? 4 : wdt == MOE_BF16 ? 8 : 32; }
 
 // shape checks shared by all calls
@@ -26,7 +28,7 @@ moe_status check_shape(const moe_shape *s) {
     if (s->top_k < 1 || s->top_k > s->num_experts) return MOE_ERR_INVALID_ARG;
     if (s->act_dtype != MOE_F32 && s->act_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
     if (s->weight_dtype != MOE_F32 && s->weight_dtype != MOE_BF16 && s->weight_dtype != MOE_MXFP4 &&
-        s->weight_dtype != MOE_NVFP4)
+        s->weight_dtype != MOE_NVFP4 && s->weight_dtype != MOE_MXINT8)
         return MOE_ERR_INVALID_ARG;
     if (s->path < MOE_PATH_AUTO || s->path > MOE_PATH_GROUPED) return MOE_ERR_INVALID_ARG;
     const int epc = weight_epc(s->weight_dtype);
@@ -53,7 +55,7 @@ moe_status check_ws(const moe_shape *s, const void *ws, size_t ws_bytes) {
 moe_status check_weights(const moe_shape *s, const moe_expert_weights *w) {
     if (!w || !w->w_gate || !w->w_up || !w->w_down) return MOE_ERR_INVALID_ARG;
     if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down)) return MOE_ERR_INVALID_ARG;
-    const bool scaled = s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4;
+    const bool scaled = s->weight_dtype == MOE_MXFP4 || s->weight_dtype == MOE_NVFP4 || s->weight_dtype == MOE_MXINT8;
     if (scaled && (!w->s_gate || !w->s_up || !w->s_down)) return MOE_ERR_INVALID_ARG;
     // scale arrays: 16-byte aligned like every device pointer (the large-tile MXFP4 GEMM
     // loads a tile's scale rows into LDS 16 bytes at a time)
@@ -80,12 +82,13 @@ moe_status check_path(const moe_shape *s) {
 bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 
 // AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
-// experts, three with MXFP4 and four with NVFP4 (whose streaming kernels read a quarter of the
-// bytes); measured crossovers on the decode shapes: bf16 T = 24..32 (k = 8, E = 128), MXFP4
-// T = 64..96 (k = 8, E = 256: 661 / 701 us streaming / grouped at 64, 802 / 734 at 96)
+// experts, three with MXFP4 and MXINT8 and four with NVFP4 (whose streaming kernels read a
+// quarter of the bytes); measured crossovers on the decode shapes: bf16 T = 24..32 (k = 8,
+// E = 128), MXFP4 T = 64..96 (k = 8, E = 256: 661 / 701 us streaming / grouped at 64, 802 /
+// 734 at 96)
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : s.weight_dtype == MOE_MXFP4 ? 3L : 4L;
+    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : s.weight_dtype == MOE_NVFP4 ? 4L : 3L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
            (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
 }

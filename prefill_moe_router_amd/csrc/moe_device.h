@@ -262,13 +262,41 @@ struct FmtNV4 {  // NVFP4 weights (E2M1 codes, one E4M3 scale per 16 elements) w
     static constexpr bool SCALED = true;
     static constexpr int SB = 2;           // two E4M3 scales per chunk (elements 0-15, 16-31)
 };
+struct FmtI8 {  // MXINT8 weights (OCP MX INT8 codes, one E8M0 scale per 32 elements), bf16 activations
+    static constexpr int EPC = 16;
+    static constexpr int XB = 32;
+    static constexpr bool SCALED = true;
+    static constexpr int SB = 1;           // one E8M0 scale per two chunks
+};
 
-// the scale code of chunk idx of a scale row: one byte (MXFP4) or two (NVFP4, low byte
-// for the chunk's first 16 elements)
+// bytes of scales of a row of nch 16-byte chunks
+template <class F>
+__host__ __device__ constexpr size_t scale_row_bytes(size_t nch) {
+    return !F::SCALED ? 0 : F::EPC == 16 ? nch / 2 : nch * F::SB;
+}
+
+// the scale code of chunk idx of a scale row: one byte (MXFP4), two (NVFP4, low byte
+// for the chunk's first 16 elements), or the byte chunks 2j and 2j+1 share (MXINT8)
 template <class F>
 __device__ __forceinline__ uint32_t load_scale(const uint8_t *s, size_t idx) {
     if constexpr (F::SB == 2) return reinterpret_cast<const uint16_t *>(s)[idx];
+    if constexpr (F::EPC == 16) return s[idx >> 1];
     return s[idx];
+}
+
+// OCP MX INT8: an element is its int8 code times 2^-6, times the block's E8M0 scale
+// 2^(code - 127): one power of two 2^(code - 133) for the block
+__device__ __forceinline__ float mxint8_scale(uint32_t scale_code) {
+    return __builtin_ldexpf(1.0f, (int)scale_code - 133);
+}
+
+// the signed bytes 2 SEL and 2 SEL + 1 of w times s, as a bf16 pair: exact while s is a
+// power of two that keeps the products normal (an int8 needs 8 significant bits)
+template <int SEL>
+__device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, float s) {
+    const float lo = (float)(int8_t)(uint8_t)(w >> (16 * SEL)) * s;
+    const float hi = (float)(int8_t)(uint8_t)(w >> (16 * SEL + 8)) * s;
+    return pack_bf16x2(lo, hi);
 }
 
 // OCP FP8 E4M3 (bias 7, no infinities): normal codes (1 + m/8) * 2^(e-7), exponent field 0
@@ -337,6 +365,23 @@ __device__ __forceinline__ float chunk_dot<FmtMX4>(const uint4 &w, uint32_t scal
     acc = mx4_word_dot(w.z, s, x4[2], acc);
     acc = mx4_word_dot(w.w, s, x4[3], acc);
     return acc;
+}
+
+// MXINT8: the 16 codes as bf16 (exact), dotted with 32 bytes of activations; the block's
+// power of two multiplies the chunk's partial sum
+template <>
+__device__ __forceinline__ float chunk_dot<FmtI8>(const uint4 &w, uint32_t scale_code, const uint8_t *xp, float acc) {
+    const uint4 *x4 = reinterpret_cast<const uint4 *>(xp);
+    const uint4 xa = x4[0], xb = x4[1];
+    float a = dot2_bf16(i8x2_to_bf16x2<0>(w.x, 1.0f), xa.x, 0.f);
+    a = dot2_bf16(i8x2_to_bf16x2<1>(w.x, 1.0f), xa.y, a);
+    a = dot2_bf16(i8x2_to_bf16x2<0>(w.y, 1.0f), xa.z, a);
+    a = dot2_bf16(i8x2_to_bf16x2<1>(w.y, 1.0f), xa.w, a);
+    a = dot2_bf16(i8x2_to_bf16x2<0>(w.z, 1.0f), xb.x, a);
+    a = dot2_bf16(i8x2_to_bf16x2<1>(w.z, 1.0f), xb.y, a);
+    a = dot2_bf16(i8x2_to_bf16x2<0>(w.w, 1.0f), xb.z, a);
+    a = dot2_bf16(i8x2_to_bf16x2<1>(w.w, 1.0f), xb.w, a);
+    return fmaf(mxint8_scale(scale_code), a, acc);
 }
 
 // NVFP4: each 16-element block is dotted with its codes' E2M1 values (decoded with a unit

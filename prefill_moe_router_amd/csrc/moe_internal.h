@@ -25,6 +25,11 @@ constexpr int kFusedMaxTokens = 8;
 
 inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
+// expert-weight elements per 16-byte chunk of a row (fp32 4, bf16 8, MXINT8 16, 4-bit 32)
+inline int weight_chunk_elems(int dt) {
+    return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : dt == MOE_MXINT8 ? 16 : 32;
+}
+
 // upper bound of the number of m-tiles of P pairs over E experts:
 // sum over experts of ceil(count / tile) <= P / tile + (number of nonempty experts)
 inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM + (P < E ? P : E); }

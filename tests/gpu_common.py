@@ -15,7 +15,7 @@ from tests.helpers import max_abs, oracle_layer, rel_l2
 
 # tolerances of the layer output against the fp64 oracle
 TOL = {"bf16": dict(rel_l2=1e-2, max_abs=3e-2), "mxfp4": dict(rel_l2=2e-2, max_abs=None),
-       "nvfp4": dict(rel_l2=2e-2, max_abs=None),
+       "nvfp4": dict(rel_l2=2e-2, max_abs=None), "mxint8": dict(rel_l2=2e-2, max_abs=None),
        "f32": dict(rel_l2=1e-5, max_abs=1e-4)}
 # Gate weights, max-abs: a diagnostic (ids and y carry the acceptance bounds).  They are
 # fp32 softmaxes of fp32 logits whose sum over H bf16 products differs from the oracle's
@@ -52,7 +52,7 @@ def act_code(s: synth.Shape) -> int:
 
 
 def w_code(s: synth.Shape) -> int:
-    return {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4}[s.w]
+    return {"f32": pm.F32, "bf16": pm.BF16, "mxfp4": pm.MXFP4, "nvfp4": pm.NVFP4, "mxint8": pm.MXINT8}[s.w]
 
 
 def lshape(li: synth.LayerInputs, path=pm.PATH_AUTO, T=None, K=None, renorm=None) -> pm.LayerShape:
@@ -153,7 +153,7 @@ def compare_forward(li: synth.LayerInputs, got: dict, tokens=None, K=None, renor
         wref[mism] = forced["w"]
     werr = max_abs(gw, wref)
     assert werr <= W_TOL, f"{label}: gate weights max-abs {werr:.3e}"
-    fmt = li.shape.w if li.shape.w in ("mxfp4", "nvfp4") else li.shape.act
+    fmt = li.shape.w if li.shape.w in ("mxfp4", "nvfp4", "mxint8") else li.shape.act
     y = to_f64(got["y"], li.shape.act)[toks]
     r, m = rel_l2(y, yref), max_abs(y, yref)
     tol = TOL[fmt]

@@ -103,7 +103,7 @@ def test_forward_validation():
 def test_scale_pointers_must_be_16_byte_aligned():
     """MXFP4 and NVFP4 scale arrays follow the header's 16-byte rule for device pointers."""
     L = pm.lib()
-    for fmt in (pm.MXFP4, pm.NVFP4):
+    for fmt in (pm.MXFP4, pm.NVFP4, pm.MXINT8):
         shp = _shape(weight_dtype=fmt)
         s = shp.c()
         n = pm.workspace_size(shp)
@@ -177,6 +177,26 @@ def test_nvfp4_validation():
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     # with fp32 activations NVFP4 is not a supported pair
     assert pm.workspace_size(_shape(weight_dtype=pm.NVFP4, act_dtype=pm.F32)) == 0
+
+
+def test_mxint8_validation():
+    """MXINT8 experts: bf16 activations only, H and I multiples of the 32-element scale
+    block, scale arrays required; AUTO takes the grouped GEMMs from three pairs per expert."""
+    assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8)) > 0
+    assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8, hidden=2048 + 16)) == 0
+    assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8, intermediate=768 + 8)) == 0
+    assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8, act_dtype=pm.F32)) == 0
+    L = pm.lib()
+    shp = _shape(weight_dtype=pm.MXINT8)
+    s = shp.c()
+    w = pm.ExpertWeights(FAKE, FAKE, FAKE, None, FAKE, FAKE)
+    assert L.moe_forward(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE,
+                         pm.workspace_size(shp), None) == pm.ERR_INVALID_ARG
+    for T, grouped in ((47, False), (48, True)):
+        stages = pm.forward_stages(_shape(weight_dtype=pm.MXINT8, num_tokens=T))
+        assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
+    assert pm.forward_stages(_shape(weight_dtype=pm.MXINT8, num_tokens=8, hidden=4096, num_experts=256,
+                                    intermediate=1024)) == ["decode_fused"]
 
 
 def test_status_strings():

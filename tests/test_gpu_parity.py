@@ -353,6 +353,52 @@ def test_forward_nvfp4_small_shapes(T, H, E, K, I):
     compare_forward(li, got, label=f"nvfp4 T={T} H={H} E={E}")
 
 
+# ---- MXINT8 experts (OCP MX INT8 codes, E8M0 scale per 32 elements) --------------------------
+
+@pytest.mark.parametrize("name", ["c6_mxint8_decode1", "c6_mxint8_decode8"])
+def test_forward_parity_mxint8_decode(name):
+    """MXINT8 experts on the fused decode launch (H = 4096, E = 256): ids exact away from
+    near-ties, y of every token against the oracle."""
+    note(f"forward parity {name}")
+    li = layer(name)
+    assert pm.forward_stages(lshape(li)) == ["decode_fused"]
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=name)
+
+
+@pytest.mark.parametrize("T", [1, 5, 8])
+def test_forward_mxint8_decode_bf16_layer_shape(T):
+    """MXINT8 experts on the H = 2048, E = 128, I = 768 layer shape with a router bias."""
+    li = layer_of(synth.Shape(T, 2048, 128, 8, 768, "bf16", "mxint8", bias="normal"), batch=80 + T)
+    got = run_forward(DevLayer(li))
+    compare_forward(li, got, label=f"mxint8 T={T} H=2048")
+
+
+@pytest.mark.parametrize("T,path", [(20, pm.PATH_AUTO), (40, pm.PATH_DECODE), (90, pm.PATH_AUTO)])
+def test_forward_mxint8_streaming(T, path):
+    """MXINT8 beyond 8 tokens on the streaming family (codes decoded once per weight row)."""
+    note(f"mxint8 streaming T={T}")
+    li = layer_of(synth.Shape(T, 4096, 256, 8, 1024, "bf16", "mxint8"), batch=60 + T)
+    sh = lshape(li, path)
+    assert "router_logits" in pm.forward_stages(sh)
+    got = run_forward(DevLayer(li), path=path)
+    compare_forward(li, got, label=f"mxint8 streaming T={T}")
+
+
+@pytest.mark.parametrize("T,H,E,K,I,path", [(130, 1024, 32, 4, 256, pm.PATH_GROUPED),
+                                            (333, 512, 16, 6, 512, pm.PATH_GROUPED),
+                                            (512, 4096, 256, 8, 1024, pm.PATH_AUTO)])
+def test_forward_mxint8_grouped(T, H, E, K, I, path):
+    """MXINT8 on the grouped MFMA GEMMs (codes dequantised into LDS with the block's power
+    of two): ragged m-tiles, skewed groups, and AUTO's choice at 512 tokens."""
+    note(f"mxint8 grouped T={T} H={H} E={E}")
+    li = layer_of(synth.Shape(T, H, E, K, I, "bf16", "mxint8", bias="zipf" if T == 333 else "normal"), seed=11)
+    sh = lshape(li, path)
+    assert "gate_up" in pm.forward_stages(sh) and "topk" not in pm.forward_stages(sh)[:1]
+    got = run_forward(DevLayer(li), path=path)
+    compare_forward(li, got, label=f"mxint8 grouped T={T}")
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5, 8, 9, 13])
 def test_forward_token_sweep(T):
     note(f"token sweep T={T}")

@@ -4,8 +4,8 @@ against the oracle's grouping of those ids, and y of every token against the
 oracle within the format's tolerance.  Needs an MI355X; run with -m gpu.
 
 The chunks are the 8192-token bf16 chunk with its Zipf-skewed routing, the
-4096-token MXFP4 and NVFP4 chunks, and the 8192-token chunk with 8 decode rows
-appended in one call.  Each chunk runs once per module; the y comparison is
+4096-token MXFP4, NVFP4 and MXINT8 chunks, and the 8192-token chunk with 8
+decode rows appended in one call.  Each chunk runs once per module; the y comparison is
 split in four token ranges so that no single test holds the oracle for long.
 """
 import numpy as np
@@ -19,7 +19,8 @@ from tests.helpers import grouping_violations, oracle_layer
 
 pytestmark = pytest.mark.gpu
 
-CHUNKS = ["c3_prefill8192_bf16", "c4_mxfp4_prefill4096", "c5_nvfp4_prefill4096", "c3_mixed8200_bf16"]
+CHUNKS = ["c3_prefill8192_bf16", "c4_mxfp4_prefill4096", "c5_nvfp4_prefill4096", "c6_mxint8_prefill4096",
+          "c3_mixed8200_bf16"]
 PARTS = 4
 
 _RUNS = {}
