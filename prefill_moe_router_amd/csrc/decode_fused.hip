@@ -46,6 +46,7 @@ constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
 constexpr int FMAX_RT = 8;              // rows of a down-projection tile
+constexpr int FMAX_WR = 32;             // output rows of one work-group (its tiles' rows)
 constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
 constexpr uint64_t SPIN_TICKS = 20000000ull;  // 0.2 s of the 100 MHz real-time clock
 
@@ -103,16 +104,24 @@ __device__ __forceinline__ void bar_wait(uint64_t *bar, uint64_t target, int32_t
 
 // ---- small helpers -------------------------------------------------------------------
 
-// C chunks of 16 bytes per lane: chunk lane0 + stride*c of the row (c < C), zero past nch
+// C chunks of 16 bytes per lane: chunk lane0 + stride*c of the row (c < C), zero past nch.
+// Loaded through buffer resources over the row and its scales: chunks past the row end
+// read zero without a memory access and without a branch, so every call issues the same
+// loads.  (A load under a branch leaves the compiler unsure how many loads are in flight,
+// and it then waits for all of them, the next item's prefetch too, before the first use.)
 template <class F, int C>
 __device__ __forceinline__ void load_chunks(const uint8_t *row, const uint8_t *srow, int nch, int lane0, int stride,
                                             uint4 (&q)[C], uint32_t (&s)[C]) {
+    const rsrc_t rw = make_rsrc(row, (uint32_t)nch * 16);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-        const int ch = lane0 + stride * c;
-        const bool ok = ch < nch;
-        q[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-        s[c] = (F::SCALED && ok) ? load_scale<F>(srow, ch) : 0u;
+    for (int c = 0; c < C; ++c) q[c] = ld_rsrc16(rw, (uint32_t)(lane0 + stride * c) * 16);
+    if constexpr (F::SCALED) {
+        const rsrc_t rs = make_rsrc(srow, (uint32_t)scale_row_bytes<F>(nch));
+#pragma unroll
+        for (int c = 0; c < C; ++c) s[c] = load_scale_r<F>(rs, (uint32_t)(lane0 + stride * c));
+    } else {
+#pragma unroll
+        for (int c = 0; c < C; ++c) s[c] = 0u;
     }
 }
 
@@ -212,7 +221,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     __shared__ __attribute__((aligned(16))) int s_first[FMAX_P + 4];
     __shared__ int s_act_e[FMAX_P], s_act_start[FMAX_P], s_act_cnt[FMAX_P];
     __shared__ int s_nact;
-    __shared__ float s_part[FWPB * FMAX_T * FMAX_RT];   // down partials [wave][token][tile row]
+    __shared__ float s_part[FWPB * FMAX_T * FMAX_WR];   // down partials [wave][token][work-group row]
     __shared__ uint64_t s_base;
     __shared__ uint32_t s_tag;
 
@@ -231,7 +240,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         s_tag = (uint32_t)(s_base / (uint64_t)G) + 1u;
         s_nact = 0;
     }
-    for (int i = tid; i < FWPB * FMAX_T * FMAX_RT; i += FTHREADS) s_part[i] = 0.f;
+    for (int i = tid; i < FWPB * FMAX_T * FMAX_WR; i += FTHREADS) s_part[i] = 0.f;
     // pad the id tables to a multiple of 4 with a sentinel no id equals or exceeds
     if (tid < 4) {
         s_ids[P + tid] = 0x7fffffff;
@@ -262,17 +271,23 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         for (int ee = e; ee < E; ee += NRW) {
             if (ee != e) load_chunks<A, CR>(p.wr + (size_t)ee * nch * 16, nullptr, nch, lane, WAVE, q, sc);
             const float b = p.bias ? p.bias[ee] : 0.f;
-            // every row t < FMAX_T is rewritten each call (rows past T with the tag only), so
-            // a word this call reads was last written by this call or by the one before it
+            // every token's logit first (lane t keeps token t's), then one store of all of them:
+            // a store between the tokens would make the next token wait for it.  Every row
+            // t < FMAX_T is rewritten each call (rows past T with the tag only), so a word this
+            // call reads was last written by this call or by the one before it.
+            float mine = 0.f;
 #pragma unroll
             for (int t = 0; t < FMAX_T; ++t) {
-                const float v = t < T ? dpp_sum64(row_dot<A, CR>(q, sc, smem + t * xrow, nch, lane, WAVE)) + b
-                                      : 0.f;
-                if (lane == 63)
-                    __hip_atomic_store(p.logits + (size_t)t * E + ee,
-                                       (uint64_t)__float_as_uint(v) | ((uint64_t)s_tag << 32), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
+                if (t < T) {
+                    const float v = dpp_sum64(row_dot<A, CR>(q, sc, smem + t * xrow, nch, lane, WAVE));
+                    const float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+                    mine = lane == t ? r + b : mine;
+                }
             }
+            if (lane < FMAX_T)
+                __hip_atomic_store(p.logits + (size_t)lane * E + ee,
+                                   (uint64_t)__float_as_uint(mine) | ((uint64_t)s_tag << 32), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
         }
     }
     // ---- phase 1: logits to LDS (wave 0 waits for them), top-k + softmax per token (wave t),
@@ -381,6 +396,10 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const int U = s_nact;
 
     // ---- phase 2: gate/up + SwiGLU -> h' (next item's rows in flight while computing) -----
+    // A wave's items are gw, gw + NW, ...  Each item's rows are fetched one item ahead.  The
+    // loads are branch-free and the loop leaves before a fetch, never around one, so the
+    // compiler's wait before an item's first use leaves the next item's loads in flight (a
+    // load under a branch would make it wait for every load).
     {
         const int nch = H / F::EPC;
         const size_t xrow = (size_t)H * ab;
@@ -411,16 +430,25 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             }
         };
         int q = gw;
-        if (q < nitems) fetch(q, gq, gs, uq, us);
-        while (q < nitems) {
-            const int q2 = q + NW;
-            if (q2 < nitems) fetch(q2, gq2, gs2, uq2, us2);
-            consume(q, gq, gs, uq, us);
-            if (q2 >= nitems) break;
-            const int q3 = q2 + NW;
-            if (q3 < nitems) fetch(q3, gq, gs, uq, us);
-            consume(q2, gq2, gs2, uq2, us2);
-            q = q3;
+        if (q < nitems) {
+            fetch(q, gq, gs, uq, us);
+            for (;;) {
+                const int q2 = q + NW;
+                if (q2 >= nitems) {
+                    consume(q, gq, gs, uq, us);
+                    break;
+                }
+                fetch(q2, gq2, gs2, uq2, us2);
+                consume(q, gq, gs, uq, us);
+                const int q3 = q2 + NW;
+                if (q3 >= nitems) {
+                    consume(q2, gq2, gs2, uq2, us2);
+                    break;
+                }
+                fetch(q3, gq, gs, uq, us);
+                consume(q2, gq2, gs2, uq2, us2);
+                q = q3;
+            }
         }
     }
 
@@ -444,22 +472,41 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const int total = ntw * nexp;
     uint4 dqa[NC], dqb[NC];
     uint32_t dsa[NC], dsb[NC];
+    // Item sq of the wave is (tile j = sq / nexp, its k-th expert).  Loads are branch-free
+    // (an item past the last reloads the last one; a wave with no items loads a row of the
+    // first active expert), so the compiler's waits before an item leave the next one's
+    // loads in flight.
+    // the item's DR rows of Wd[e] are contiguous; one resource covers the rows below H
+    // (lane group rr takes row rr, chunks past a row's end read as out of range)
     auto load_item = [&](int sq, uint4 (&dq)[NC], uint32_t (&ds)[NC]) {
-        const int j = sq / nexp, k = sq - j * nexp;
-        const int n = ((int)blockIdx.x + G * j) * DR + rr;
-        const bool okr = n < H;
-        const size_t rsel = (size_t)s_act_e[wave + FWPB * k] * H + (okr ? n : 0);
-        const uint8_t *row = p.wd + rsel * nchd * 16;
+        const bool any = total > 0;
+        const int sqc = any ? min(sq, total - 1) : 0;
+        const int j = any ? sqc / nexp : 0, k = any ? sqc - j * nexp : 0;
+        const int n0 = ((int)blockIdx.x + G * j) * DR;
+        const int rows = any ? min(DR, H - n0) : 0;
+        const size_t rsel0 = (size_t)s_act_e[any ? wave + FWPB * k : 0] * H + (any ? n0 : 0);
+        const rsrc_t rw = make_rsrc(p.wd + rsel0 * nchd * 16, (uint32_t)(rows * nchd * 16));
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int ch = li + LR * c;
-            const bool ok = okr && ch < nchd;
-            dq[c] = ok ? ld_stream16(row + (size_t)ch * 16) : make_uint4(0, 0, 0, 0);
-            ds[c] = (F::SCALED && ok) ? load_scale<F>(p.sd, rsel * nchd + ch) : 0u;
+            dq[c] = ld_rsrc16(rw, ch < nchd ? (uint32_t)(rr * nchd + ch) * 16 : kOutOfRange);
+        }
+        if constexpr (F::SCALED) {
+            const uint32_t srb = (uint32_t)scale_row_bytes<F>(nchd);
+            const rsrc_t rs = make_rsrc(p.sd + rsel0 * srb, (uint32_t)rows * srb);
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int ch = li + LR * c;
+                // chunk index rr * nchd + ch of the resource: its scale sits at row rr's scales
+                ds[c] = load_scale_r<F>(rs, ch < nchd ? (uint32_t)(rr * nchd + ch) : kOutOfRange / 4);
+            }
+        } else {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) ds[c] = 0u;
         }
     };
     bar_arrive(p.bar);
-    if (total > 0) load_item(0, dqa, dsa);
+    load_item(0, dqa, dsa);
     if (total > 1) load_item(1, dqb, dsb);
     bar_wait(p.bar, s_base + (uint64_t)G, p.err);
 
@@ -477,6 +524,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                 const int i = i0 + b * nst;
                 v[b] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
             }
+            __builtin_amdgcn_sched_barrier(0);   // all eight loads before the first store
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
                 const int i = i0 + b * nst;
@@ -487,11 +535,14 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     __syncthreads();
 
     // ---- phase 3: down projection + weighted combine, by output row tile -------------------
+    // Each wave adds its experts' contributions to its own partial sums of all the
+    // work-group's rows (s_part[wave][token][row]); the work-group then adds the FWPB
+    // partials in wave order and stores y once, after every item.
     {
         const size_t hrow = (size_t)I * ab;
-        float *part = s_part + (size_t)wave * FMAX_T * FMAX_RT;
+        float *part = s_part + (size_t)wave * FMAX_T * FMAX_WR;
         auto consume = [&](int sq, const uint4 (&dq)[NC], const uint32_t (&ds)[NC]) {
-            const int k = sq % nexp;
+            const int j = sq / nexp, k = sq - j * nexp;
             const int u = wave + FWPB * k;
             const int start = s_act_start[u], cnt = s_act_cnt[u];
             for (int c = 0; c < cnt; ++c) {
@@ -500,52 +551,75 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                 const uint8_t *ha = smem + (size_t)q * hrow;
                 float d = row_dot<F, NC>(dq, ds, ha, nchd, li, LR);
                 d = lane_group_sum<LR>(d) * p.tsd;
-                if (li == LR - 1) atomicAdd(part + t * FMAX_RT + rr, d);
+                if (li == LR - 1) atomicAdd(part + t * FMAX_WR + j * DR + rr, d);
             }
-        };
-        // the tile's sum over the work-group's waves, in wave order (cleared for a next tile)
-        auto finish_tile = [&](int j, bool more) {
-            __syncthreads();
-            const int n0 = ((int)blockIdx.x + G * j) * DR;
-            for (int i = tid; i < T * DR; i += FTHREADS) {
-                const int t = i / DR, r = i - t * DR;
-                float v = 0.f;
-#pragma unroll
-                for (int w = 0; w < FWPB; ++w) {
-                    float *pp = s_part + ((size_t)w * FMAX_T + t) * FMAX_RT + r;
-                    v += *pp;
-                    if (more) *pp = 0.f;
-                }
-                const int n = n0 + r;
-                if (n < H) {
-                    if (f32)
-                        reinterpret_cast<float *>(p.y)[(size_t)t * H + n] = v;
-                    else
-                        reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
-                }
-            }
-            if (more) __syncthreads();
         };
         int sq = 0;
-        for (int j = 0; j < ntw; ++j) {
-            for (int k = 0; k < nexp; ++k, ++sq) {
-                if (sq & 1) {
-                    consume(sq, dqb, dsb);
-                    if (sq + 2 < total) load_item(sq + 2, dqb, dsb);
-                } else {
-                    consume(sq, dqa, dsa);
-                    if (sq + 2 < total) load_item(sq + 2, dqa, dsa);
-                }
+        for (; sq + 2 < total; sq += 2) {
+            consume(sq, dqa, dsa);
+            load_item(sq + 2, dqa, dsa);
+            consume(sq + 1, dqb, dsb);
+            load_item(sq + 3, dqb, dsb);
+        }
+        if (sq < total) consume(sq, dqa, dsa);
+        if (sq + 1 < total) consume(sq + 1, dqb, dsb);
+        __syncthreads();
+        for (int i = tid; i < T * ntw * DR; i += FTHREADS) {
+            const int t = i / (ntw * DR), jr = i - t * (ntw * DR);
+            const int j = jr / DR, r = jr - j * DR;
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < FWPB; ++w) v += s_part[((size_t)w * FMAX_T + t) * FMAX_WR + jr];
+            const int n = ((int)blockIdx.x + G * j) * DR + r;
+            if (n < H) {
+                if (f32)
+                    reinterpret_cast<float *>(p.y)[(size_t)t * H + n] = v;
+                else
+                    reinterpret_cast<uint16_t *>(p.y)[(size_t)t * H + n] = (uint16_t)f32_to_bf16_rne(v);
             }
-            finish_tile(j, j + 1 < ntw);
         }
     }
 }
 
-// LDS bytes of the staged x plus the logits that follow it
-static size_t fused_lds_front(const moe_shape &s) {
+// dynamic LDS of the fused kernel: the staged x and the logits after it (phases 0-2), or
+// the staged h' (phase 3)
+static size_t fused_lds_bytes(const moe_shape &s) {
     const size_t xb = (size_t)s.num_tokens * s.hidden * act_bytes(s.act_dtype);
-    return ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4;
+    const size_t front = ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4;
+    return std::max(front, (size_t)s.num_tokens * s.top_k * s.intermediate * act_bytes(s.act_dtype));
+}
+
+// rows of the down projection's tiles that one work-group owns (at most FMAX_WR)
+template <class F>
+static int fused_wg_rows(const moe_shape &s, int G) {
+    const int nchd = s.intermediate / F::EPC;
+    const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
+    const int cd = (nchd + lpr - 1) / lpr;
+    const int cdb = cd <= 1 ? 1 : cd <= 2 ? 2 : cd <= 4 ? 4 : 8;
+    const int cg = (s.hidden / F::EPC + WAVE - 1) / WAVE;
+    const int dr_reg = ((cg > 4 || F::SCALED) ? 8 : 16) / (cdb >= 4 ? 4 : cdb);
+    const int dr = dr_reg > 8 ? 8 : dr_reg;
+    const int ntile = (s.hidden + dr - 1) / dr;
+    return (ntile + G - 1) / G * dr;
+}
+
+// the number of work-groups the fused kernel runs on (one per compute unit), or 0
+static int fused_grid() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                  hipSuccess)
+        return 0;
+    return cus;
+}
+
+static int fused_rows_for(const moe_shape &s, int G) {
+    switch (s.weight_dtype) {
+        case MOE_F32: return fused_wg_rows<FmtF32>(s, G);
+        case MOE_BF16: return fused_wg_rows<FmtBF16>(s, G);
+        case MOE_NVFP4: return fused_wg_rows<FmtNV4>(s, G);
+        case MOE_MXINT8: return fused_wg_rows<FmtI8>(s, G);
+        default: return fused_wg_rows<FmtMX4>(s, G);
+    }
 }
 
 // true when the fused kernel covers this shape (otherwise the staged kernels run)
@@ -563,7 +637,9 @@ bool decode_fused_supported(const moe_shape &s) {
     const int nchd = s.intermediate / epc;
     const int lpr = nchd >= WAVE ? WAVE : (nchd >= 32 ? 32 : 16);
     if (nchd < 16 || (nchd + lpr - 1) / lpr > FMAX_C / 2) return false;    // down rows
-    if (fused_lds_front(s) > FLDS_MAX || P * s.intermediate * ab > FLDS_MAX) return false;
+    // the gfx950 parts have 256 compute units; the launch re-checks with the device's count
+    if (fused_lds_bytes(s) > FLDS_MAX) return false;
+    if (fused_rows_for(s, 256) > FMAX_WR) return false;
     if (s.num_experts > 1024) return false;
     return fused_bucket_built(bucket((s.hidden / epc + WAVE - 1) / WAVE), bucket((s.hidden / aepc + WAVE - 1) / WAVE),
                               bucket((nchd + lpr - 1) / lpr));
@@ -663,11 +739,13 @@ static bool fused_fits(const moe_shape &s) {
 }
 
 bool decode_fused_coresident(const moe_shape &s) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) {
+    const int G = fused_grid();
+    if (G <= 0) {
         (void)hipGetLastError();
         return true;   // no device: nothing will be launched
     }
+    // the output-row budget on this device's grid
+    if (fused_rows_for(s, G) > FMAX_WR) return false;
     switch (s.weight_dtype) {
         case MOE_F32: return fused_fits<FmtF32, FmtF32>(s);
         case MOE_BF16: return fused_fits<FmtBF16, FmtBF16>(s);
@@ -691,11 +769,9 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
                                const moe_expert_weights &w, void *y, int32_t *ids_out, float *w_out, void *ws,
                                hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     const WsLayout L = ws_layout(s);
-    int dev = 0, cus = 0;
-    hipError_t r = hipGetDevice(&dev);
-    if (r != hipSuccess) return r;
-    r = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (r != hipSuccess) return r;
+    const int cus = fused_grid();
+    if (cus <= 0) return hipErrorNoDevice;
+    if (fused_rows_for(s, cus) > FMAX_WR) return hipErrorInvalidConfiguration;
     FusedParams prm{};
     prm.x = static_cast<const uint8_t *>(x);
     prm.wr = static_cast<const uint8_t *>(wr);
@@ -725,8 +801,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     prm.I = s.intermediate;
     prm.renorm = s.renormalize ? 1 : 0;
     prm.nblocks = cus;
-    const size_t ab = act_bytes(s.act_dtype);
-    const size_t lds = std::max(fused_lds_front(s), (size_t)s.num_tokens * s.top_k * s.intermediate * ab);
+    const size_t lds = fused_lds_bytes(s);
     switch (s.weight_dtype) {
         case MOE_F32: return fused_dispatch<FmtF32, FmtF32>(s, prm, lds, st, ev0, ev1);
         case MOE_BF16: return fused_dispatch<FmtBF16, FmtBF16>(s, prm, lds, st, ev0, ev1);

@@ -60,6 +60,34 @@ __device__ __forceinline__ uint4 ld_stream16(const void *p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// ---- bounded loads through a buffer resource --------------------------------------------
+// A raw buffer resource over [base, base + bytes): a load at an offset past the end
+// returns zero without touching memory.  Loads of a fixed count through it need no branch
+// for the part of a row that does not exist, so the compiler's waits can count exactly
+// the loads issued after the one a use depends on.  The base must be the same in every
+// lane (it is taken from the first active one).
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOutOfRange = 0x80000000u;   // an offset past the end of every resource
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a), hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    void *u = reinterpret_cast<void *>(((uint64_t)hi << 32) | lo);
+    // word 3 (0x00020000): the gfx9 raw-buffer data format
+    return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+// 16 bytes at byte offset off, non-temporal (weights are read once per call)
+__device__ __forceinline__ uint4 ld_rsrc16(rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint32_t ld_rsrc_u8(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
+}
+__device__ __forceinline__ uint32_t ld_rsrc_u16(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
 // ---- waits, barriers and direct-to-LDS loads ----------------------------------------
 
 typedef __attribute__((address_space(3))) void lds_ptr_t;
@@ -282,6 +310,14 @@ __device__ __forceinline__ uint32_t load_scale(const uint8_t *s, size_t idx) {
     if constexpr (F::SB == 2) return reinterpret_cast<const uint16_t *>(s)[idx];
     if constexpr (F::EPC == 16) return s[idx >> 1];
     return s[idx];
+}
+
+// the scale code of chunk ch through a resource over one scale row (zero past its end)
+template <class F>
+__device__ __forceinline__ uint32_t load_scale_r(rsrc_t r, uint32_t ch) {
+    if constexpr (F::SB == 2) return ld_rsrc_u16(r, ch < 0x40000000u ? ch * 2 : kOutOfRange);
+    if constexpr (F::EPC == 16) return ld_rsrc_u8(r, ch >> 1);
+    return ld_rsrc_u8(r, ch);
 }
 
 // OCP MX INT8: an element is its int8 code times 2^-6, times the block's E8M0 scale
