@@ -44,6 +44,7 @@ constexpr int FWPB = 8;                 // waves per work-group
 constexpr int FTHREADS = FWPB * WAVE;
 constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
+constexpr int FROUNDS_MAX_K = 12;       // top-k by arg-max rounds up to this k, radix walk above
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
 constexpr int FMAX_RT = 8;              // rows of a down-projection tile
 constexpr int FMAX_WR = 32;             // output rows of one work-group (its tiles' rows)
@@ -214,11 +215,10 @@ __device__ __forceinline__ bool poll_words(const uint64_t *words, int n, uint32_
 template <class F, class A, int CG, int CR, int CD>
 __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];   // staged x, later staged h'
-    __shared__ __attribute__((aligned(16))) int s_ids[FMAX_P + 4];
+    __shared__ int s_ids[FMAX_P];
     __shared__ float s_w[FMAX_P];
     __shared__ int s_tok[FMAX_P];     // token of each slot, in expert-sorted order
     __shared__ float s_wq[FMAX_P];    // routing weight of each slot, in expert-sorted order
-    __shared__ __attribute__((aligned(16))) int s_first[FMAX_P + 4];
     __shared__ int s_act_e[FMAX_P], s_act_start[FMAX_P], s_act_cnt[FMAX_P];
     __shared__ int s_nact;
     __shared__ float s_part[FWPB * FMAX_T * FMAX_WR];   // down partials [wave][token][work-group row]
@@ -233,6 +233,10 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const bool f32 = A::EPC == 4;
     const int ab = f32 ? 4 : 2;
     const size_t lg_off = ((size_t)T * H * ab + 15) & ~(size_t)15;   // LDS logits after the staged x
+    // after the logits: the per-expert token masks of the top-k, then 64 words per wave
+    // that lanes with nothing to store write to
+    uint32_t *s_sel = reinterpret_cast<uint32_t *>(smem + lg_off + (size_t)T * E * 4);
+    uint32_t *s_trash = s_sel + ((E + 3) & ~3);
 
     if (tid == 0) {
         s_base = bar_base(p.bar, G);
@@ -241,11 +245,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         s_nact = 0;
     }
     for (int i = tid; i < FWPB * FMAX_T * FMAX_WR; i += FTHREADS) s_part[i] = 0.f;
-    // pad the id tables to a multiple of 4 with a sentinel no id equals or exceeds
-    if (tid < 4) {
-        s_ids[P + tid] = 0x7fffffff;
-        s_first[P + tid] = 0x7fffffff;
-    }
+    for (int i = tid; i < E; i += FTHREADS) s_sel[i] = 0u;
 
     // ---- phase 0: router logits (row loads first, then x staged into LDS) ----------------
     {
@@ -298,99 +298,78 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
     }
     __syncthreads();
+    // top-k of token t in wave t: K rounds of a wave arg-max for small K, otherwise a radix
+    // walk over the logit keys (exact either way, ties to the lower id); bit t of s_sel[e] marks that token t
+    // kept expert e, and its gate weight replaces the logit at s_lg[t][e]
     if (wave < T) {
-        const bool out = blockIdx.x == 0;
         const float *lg = s_lg + (size_t)wave * E;
         int *ii = s_ids + wave * K;
         float *ww = s_w + wave * K;
-        int32_t *ig = out && p.ids_out ? p.ids_out + wave * K : nullptr;
-        float *wg = out && p.w_out ? p.w_out + wave * K : nullptr;
-        if (E <= 64) wave_topk<1>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 128) wave_topk<2>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 256) wave_topk<4>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else if (E <= 512) wave_topk<8>(lg, E, K, p.renorm, ii, ww, ig, wg);
-        else wave_topk<16>(lg, E, K, p.renorm, ii, ww, ig, wg);
+        uint32_t *tr = s_trash + wave * WAVE;
+        if (K <= FROUNDS_MAX_K) {
+            if (E <= 64) wave_topk_multi<1, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 128) wave_topk_multi<2, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 256) wave_topk_multi<4, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 512) wave_topk_multi<8, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else wave_topk_multi<16, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+        } else {
+            if (E <= 64) wave_topk_multi<1, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 128) wave_topk_multi<2, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 256) wave_topk_multi<4, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else if (E <= 512) wave_topk_multi<8, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            else wave_topk_multi<16, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+        }
+        // read back as the 32-bit words the top-k stored (other lanes of this wave wrote
+        // them; a wave's LDS accesses complete in order)
+        for (int j = lane; j < K; j += WAVE) {
+            const int e = (int)reinterpret_cast<const uint32_t *>(ii)[j];
+            const float wt = __uint_as_float(reinterpret_cast<const uint32_t *>(ww)[j]);
+            s_lg[(size_t)wave * E + e] = wt;
+            if (blockIdx.x == 0) {
+                if (p.ids_out) p.ids_out[wave * K + j] = e;
+                if (p.w_out) p.w_out[wave * K + j] = wt;
+            }
+        }
     }
     __syncthreads();
-    if (P <= WAVE) {
-        // One wave holds every slot (lane = slot).  Ballots over the expert-id bits give
-        // each slot the lanes with its id (count, and its rank among them in slot order)
-        // and, from the top bit down, the number of slots and of first slots with a
-        // smaller id: the position of the slot and of its expert in the sorted order.
-        if (wave == 0) {
-            const bool valid = lane < P;
-            const int my_e = valid ? s_ids[lane] : 0;
-            int nbits = 1;
-            while ((1 << nbits) < E) ++nbits;
-            const uint64_t all = __ballot(valid);
-            uint64_t match = all;
-            for (int b = 0; b < nbits; ++b) {
-                const uint64_t B = __ballot(valid && ((my_e >> b) & 1));
-                match &= ((my_e >> b) & 1) ? B : ~B;
+    // Grouping (wave 0) from the token masks: the active experts are those with a nonzero
+    // mask, in ascending id; an expert's slots are its tokens in ascending order (slot
+    // t*k+j ascends with t), so its count is the mask's popcount and its start the
+    // exclusive prefix of the counts.
+    if (wave == 0) {
+        const uint64_t lt = lanemask_lt();
+        int nact = 0, tot = 0;
+        for (int e0 = 0; e0 < E; e0 += WAVE) {
+            const int e = e0 + lane;
+            const uint32_t m = e < E ? s_sel[e] : 0u;
+            const int cnt = __popc(m);
+            const uint64_t bal = __ballot(m != 0u);
+            // inclusive prefix of the counts over the 64 lanes (shifts within rows of 16,
+            // then the row totals through the row broadcasts)
+            int inc = cnt;
+#pragma unroll
+            for (int sh = 1; sh < WAVE; sh <<= 1) {
+                const int v = __shfl_up(inc, sh, WAVE);
+                inc += lane >= sh ? v : 0;
             }
-            const uint64_t lt = lanemask_lt();
-            const int my_cnt = __popcll(match), before = __popcll(match & lt);
-            const uint64_t firsts = __ballot(valid && before == 0);
-            uint64_t eqa = all, eqf = firsts;
-            int my_less = 0, dl = 0;
-            for (int b = nbits - 1; b >= 0; --b) {
-                const uint64_t B = __ballot(valid && ((my_e >> b) & 1));
-                if ((my_e >> b) & 1) {
-                    my_less += __popcll(eqa & ~B);
-                    dl += __popcll(eqf & ~B);
-                    eqa &= B;
-                    eqf &= B;
-                } else {
-                    eqa &= ~B;
-                    eqf &= ~B;
+            if (m != 0u) {
+                const int dl = nact + __popcll(bal & lt);
+                const int start = tot + inc - cnt;
+                s_act_e[dl] = e;
+                s_act_start[dl] = start;
+                s_act_cnt[dl] = cnt;
+                uint32_t mm = m;
+                for (int c = 0; mm; ++c) {
+                    const int t = __builtin_ctz(mm);
+                    mm &= mm - 1;
+                    s_tok[start + c] = t;
+                    s_wq[start + c] = s_lg[(size_t)t * E + e];
                 }
             }
-            if (valid) {
-                s_tok[my_less + before] = lane / K;
-                s_wq[my_less + before] = s_w[lane];
-                if (before == 0) {
-                    s_act_e[dl] = my_e;
-                    s_act_start[dl] = my_less;
-                    s_act_cnt[dl] = my_cnt;
-                }
-            }
-            if (lane == 0) s_nact = __popcll(firsts);
+            nact += __popcll(bal);
+            tot += __shfl(inc, WAVE - 1, WAVE);
         }
-    } else {
-        const int P4 = (P + 3) >> 2;
-        int my_e = 0, my_less = 0, my_cnt = 0;
-        if (tid < P) {
-            my_e = s_ids[tid];
-            int before = 0;
-            const int4 *ids4 = reinterpret_cast<const int4 *>(s_ids);
-    #pragma unroll 4
-            for (int q4 = 0; q4 < P4; ++q4) {
-                const int4 v = ids4[q4];
-                const int q = q4 * 4;
-                my_less += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
-                my_cnt += (v.x == my_e) + (v.y == my_e) + (v.z == my_e) + (v.w == my_e);
-                before += (v.x == my_e && q < tid) + (v.y == my_e && q + 1 < tid) + (v.z == my_e && q + 2 < tid) +
-                          (v.w == my_e && q + 3 < tid);
-            }
-            s_tok[my_less + before] = tid / K;
-            s_wq[my_less + before] = s_w[tid];
-            s_first[tid] = before == 0 ? my_e : 0x7fffffff;   // first slot of its expert carries the id
-            const uint64_t firsts = __ballot(before == 0);      // distinct experts: one first slot each
-            if (lane == 0) atomicAdd(&s_nact, (int)__popcll(firsts));
-        }
-        __syncthreads();
-        if (tid < P && s_first[tid] == my_e) {
-            int dl = 0;
-            const int4 *f4 = reinterpret_cast<const int4 *>(s_first);
-    #pragma unroll 4
-            for (int q4 = 0; q4 < P4; ++q4) {
-                const int4 v = f4[q4];
-                dl += (v.x < my_e) + (v.y < my_e) + (v.z < my_e) + (v.w < my_e);
-            }
-            s_act_e[dl] = my_e;
-            s_act_start[dl] = my_less;
-            s_act_cnt[dl] = my_cnt;
-        }
+        if (lane == 0) s_nact = nact;
     }
     __syncthreads();
     const int U = s_nact;
@@ -581,11 +560,12 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     }
 }
 
-// dynamic LDS of the fused kernel: the staged x and the logits after it (phases 0-2), or
-// the staged h' (phase 3)
+// dynamic LDS of the fused kernel: the staged x, the logits, the expert token masks and
+// the per-wave discard words after it (phases 0-2), or the staged h' (phase 3)
 static size_t fused_lds_bytes(const moe_shape &s) {
     const size_t xb = (size_t)s.num_tokens * s.hidden * act_bytes(s.act_dtype);
-    const size_t front = ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4;
+    const size_t front = ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4 +
+                         (size_t)((s.num_experts + 3) & ~3) * 4 + (size_t)FWPB * WAVE * 4;
     return std::max(front, (size_t)s.num_tokens * s.top_k * s.intermediate * act_bytes(s.act_dtype));
 }
 

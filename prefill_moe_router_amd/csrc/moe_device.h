@@ -261,6 +261,185 @@ __device__ __forceinline__ void wave_topk(const float *lg, int E, int K, int ren
     }
 }
 
+// DPP reductions of N independent values per lane at once, written step by step across
+// the N values so that their chains interleave; each result is read from lane 63 and is
+// wave-uniform.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t fill) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int N>
+__device__ __forceinline__ void wave_umax_n(uint32_t (&v)[N]) {
+#define MOE_UMAX_STEP(CTRL, RM)                                                     \
+    _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] = max(v[i], dpp_u<CTRL, RM>(v[i], 0u));
+    MOE_UMAX_STEP(0x111, 0xf)   // row_shr:1
+    MOE_UMAX_STEP(0x112, 0xf)   // row_shr:2
+    MOE_UMAX_STEP(0x114, 0xf)   // row_shr:4
+    MOE_UMAX_STEP(0x118, 0xf)   // row_shr:8
+    MOE_UMAX_STEP(0x142, 0xa)   // row_bcast:15 into rows 1 and 3
+    MOE_UMAX_STEP(0x143, 0xc)   // row_bcast:31 into rows 2 and 3
+#undef MOE_UMAX_STEP
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = (uint32_t)__builtin_amdgcn_readlane((int)v[i], 63);
+}
+template <int N>
+__device__ __forceinline__ void wave_fsum_n(float (&v)[N]) {
+#define MOE_FSUM_STEP(CTRL, RM) _Pragma("unroll") for (int i = 0; i < N; ++i) v[i] += dpp_f<CTRL, RM>(v[i], 0.f);
+    MOE_FSUM_STEP(0x111, 0xf)
+    MOE_FSUM_STEP(0x112, 0xf)
+    MOE_FSUM_STEP(0x114, 0xf)
+    MOE_FSUM_STEP(0x118, 0xf)
+    MOE_FSUM_STEP(0x142, 0xa)
+    MOE_FSUM_STEP(0x143, 0xc)
+#undef MOE_FSUM_STEP
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
+}
+
+// inverse of f32_order_key
+__device__ __forceinline__ float f32_from_order_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+// Top-k of NTOK tokens at once in one wave (lg: the tokens' logits rows, E apart; E <=
+// 64*NJ), with the selection and weights of wave_topk: the K largest logits, ties to the
+// lower expert id, ids ascending, softmax weights (renormalised over the kept set when
+// asked).  Logits are compared as order-preserving keys (-0 and +0 equal).  Two ways to
+// select, both exact:
+//  - ROUNDS (small K): K rounds of a wave arg-max over the keys not yet kept (DPP max,
+//    then the lowest id holding it);
+//  - otherwise the radix walk of wave_topk without its early exit: the K-th largest key
+//    tau is built bit by bit (keep a bit when at least K keys are >= the candidate), keys
+//    above tau are kept, keys equal to tau in ascending id.
+// The tokens' chains run in lockstep with no branch, so they overlap.  Token tk's ids and
+// weights go to s_ids / s_w + tk*K (LDS; the caller copies them out), and bit (bit0 + tk)
+// is ORed into sel_mask[e] (LDS) for each kept expert of the tokens below nvalid.  s_trash:
+// 64 words of LDS that lanes with nothing to write write to instead.
+template <int NJ, int NTOK, bool ROUNDS>
+__device__ __forceinline__ void wave_topk_multi(const float *lg, int E, int K, int renorm, int nvalid, int *s_ids,
+                                                float *s_w, uint32_t *sel_mask, int bit0, uint32_t *s_trash) {
+    const int lane = threadIdx.x & 63;
+    float v[NTOK][NJ];
+    uint32_t key[NTOK][NJ];
+    bool sel[NTOK][NJ];
+#pragma unroll
+    for (int tk = 0; tk < NTOK; ++tk)
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int e = lane + 64 * j;
+            v[tk][j] = e < E ? lg[tk * E + e] : 0.f;
+            key[tk][j] = e < E ? f32_order_key(v[tk][j]) : 0u;   // 0: no expert (below every key)
+            sel[tk][j] = false;
+        }
+    uint32_t mkey[NTOK];
+    if constexpr (ROUNDS) {
+        uint32_t kt[NTOK][NJ];
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk)
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) kt[tk][j] = key[tk][j];
+        for (int round = 0; round < K; ++round) {
+            uint32_t M[NTOK];
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                M[tk] = kt[tk][0];
+#pragma unroll
+                for (int j = 1; j < NJ; ++j) M[tk] = max(M[tk], kt[tk][j]);
+            }
+            wave_umax_n(M);
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                mkey[tk] = round == 0 ? M[tk] : mkey[tk];
+                // lowest id holding M (ids lane + 64j: the first j with a hit, then its
+                // lowest lane), by selects only
+                uint64_t hit = __ballot(kt[tk][NJ - 1] == M[tk]);
+                int wj = NJ - 1;
+#pragma unroll
+                for (int j = NJ - 2; j >= 0; --j) {
+                    const uint64_t hj = __ballot(kt[tk][j] == M[tk]);
+                    wj = hj ? j : wj;
+                    hit = hj ? hj : hit;
+                }
+                const int wl = __builtin_ctzll(hit | (1ull << 63));
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    const bool win = lane == wl && j == wj;
+                    kt[tk][j] = win ? 0u : kt[tk][j];
+                    sel[tk][j] = sel[tk][j] || win;
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk) {
+            mkey[tk] = key[tk][0];
+#pragma unroll
+            for (int j = 1; j < NJ; ++j) mkey[tk] = max(mkey[tk], key[tk][j]);
+        }
+        wave_umax_n(mkey);
+        uint32_t tau[NTOK];
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk) tau[tk] = 0u;
+        for (int b = 31; b >= 0; --b) {
+#pragma unroll
+            for (int tk = 0; tk < NTOK; ++tk) {
+                const uint32_t cand = tau[tk] | (1u << b);
+                int cnt = 0;
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(key[tk][j] >= cand));
+                tau[tk] = cnt >= K ? cand : tau[tk];
+            }
+        }
+        const uint64_t lt = lanemask_lt();
+#pragma unroll
+        for (int tk = 0; tk < NTOK; ++tk) {
+            int n_gt = 0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) n_gt += __popcll(__ballot(key[tk][j] > tau[tk]));
+            const int need = K - n_gt;
+            int eq_before = 0;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const bool eq = key[tk][j] != 0u && key[tk][j] == tau[tk];
+                const uint64_t eqm = __ballot(eq);
+                const int eq_rank = eq_before + __popcll(eqm & lt);
+                eq_before += __popcll(eqm);
+                sel[tk][j] = key[tk][j] != 0u && (key[tk][j] > tau[tk] || (eq && eq_rank < need));
+            }
+        }
+    }
+    const uint64_t lt = lanemask_lt();
+    float pe[NTOK][NJ];
+    float z[NTOK];
+#pragma unroll
+    for (int tk = 0; tk < NTOK; ++tk) {
+        const float m = f32_from_order_key(mkey[tk]);
+        z[tk] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            pe[tk][j] = key[tk][j] != 0u ? __expf(v[tk][j] - m) : 0.f;
+            z[tk] += (!renorm || sel[tk][j]) ? pe[tk][j] : 0.f;
+        }
+    }
+    wave_fsum_n(z);
+#pragma unroll
+    for (int tk = 0; tk < NTOK; ++tk) {
+        int sel_before = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const uint64_t sm = __ballot(sel[tk][j]);
+            const int pos = sel_before + __popcll(sm & lt);
+            sel_before += __popcll(sm);
+            const int e = lane + 64 * j;
+            const bool s = sel[tk][j];
+            *(s ? reinterpret_cast<uint32_t *>(s_ids + tk * K + pos) : s_trash + lane) = (uint32_t)e;
+            *(s ? reinterpret_cast<uint32_t *>(s_w + tk * K + pos) : s_trash + lane) =
+                __float_as_uint(pe[tk][j] / z[tk]);
+            atomicOr(sel_mask + (e < E ? e : 0), s && tk < nvalid ? 1u << (bit0 + tk) : 0u);
+        }
+    }
+}
+
 // ---- element formats -------------------------------------------------------------
 // A "chunk" is 16 bytes of a weight row: 4 fp32, 8 bf16 or 32 MXFP4 codes (one
 // scale block).  Dot products are taken chunk by chunk against the matching
