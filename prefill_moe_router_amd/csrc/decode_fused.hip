@@ -10,9 +10,12 @@
 // computed whatever the batch (no 8-entry group limit, §9.5).
 //
 // One work-group per CU, all co-resident; gate/up and down are separated by a
-// grid barrier: a 64-bit arrival counter in the workspace that only grows (the
-// barrier completes when it reaches the next multiple of the grid size), with
-// relaxed atomics only.  Data that crosses work-groups (logits, h') is written
+// grid barrier on per-work-group flag words: each work-group stores this call's
+// tag into its own word (a plain store: no read-modify-write contended by the
+// whole grid) and waits until every word carries it.  The tag comes from a
+// 64-bit call counter in the workspace that only grows (work-group 0 adds one
+// after the barrier, when every work-group has read it), with relaxed atomics
+// only.  Data that crosses work-groups (logits, h') is written
 // with write-through agent-scope stores and read with agent-scope loads, so
 // no cache writeback or invalidation is needed at the barrier.  Every wait is
 // bounded and sets MOE_DEVERR_TIMEOUT instead of hanging.
@@ -44,6 +47,7 @@ constexpr int FWPB = 8;                 // waves per work-group
 constexpr int FTHREADS = FWPB * WAVE;
 constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
+constexpr int FMAX_G = kFusedMaxGroups; // work-groups (one per CU)
 constexpr int FROUNDS_MAX_K = 12;       // top-k by arg-max rounds up to this k, radix walk above
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
 constexpr int FMAX_RT = 8;              // rows of a down-projection tile
@@ -60,7 +64,8 @@ struct FusedParams {
     float *w_out;
     uint64_t *logits; // workspace [FMAX_T][E] words: logit bits | (call tag << 32)
     uint8_t *hbuf;    // workspace [P][I] (activation dtype)
-    uint64_t *bar;    // workspace control word: grid-barrier arrivals (only grows)
+    uint64_t *bar;    // workspace control word: completed calls (only grows)
+    uint64_t *flags;  // workspace [nblocks] words: the barrier tag each work-group stored last
     int32_t *err;
     float tsg, tsu, tsd;   // tensor scales of the gate, up and down weights (1 unless NVFP4)
     int T, H, E, K, I, renorm, nblocks;
@@ -68,35 +73,47 @@ struct FusedParams {
 
 // ---- grid barrier --------------------------------------------------------------------
 
-// The counter only grows and is a multiple of the grid size between calls.
-// Read at kernel start it lies in [base, base + G) -- no work-group can pass
-// the first barrier before every work-group has read it -- so rounding down
-// gives the call's base; barrier i completes at base + i*G.
-__device__ __forceinline__ uint64_t bar_base(uint64_t *bar, int nblocks) {
-    const uint64_t c = __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return c - c % (uint64_t)nblocks;
+// The call counter: read by every work-group at kernel start; work-group 0 adds one after
+// the barrier, which no work-group passes before all have read it.  So every work-group
+// reads the same count, and this call's tag (count + 1) differs from every earlier call's.
+__device__ __forceinline__ uint64_t call_count(const uint64_t *bar) {
+    return __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Arrival: every wave's cross-group stores are acknowledged first, then one
-// relaxed increment per work-group whose result is not waited for.
-__device__ __forceinline__ void bar_arrive(uint64_t *bar) {
+// Arrival: every wave's cross-group stores are acknowledged first, then the work-group's
+// flag word takes this call's tag.
+__device__ __forceinline__ void bar_arrive(uint64_t *flags, uint32_t tag) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) __hip_atomic_fetch_add(bar, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0)
+        __hip_atomic_store(flags + blockIdx.x, (uint64_t)tag << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wave 0 polls the G flag words (NJ per lane, G <= 64 * NJ) until all carry the tag.
 // ACQ: end with an agent-scope acquire (invalidates this CU's stale cache lines) so that
 // plain loads may read what other work-groups wrote before the barrier.
-template <bool ACQ = false>
-__device__ __forceinline__ void bar_wait(uint64_t *bar, uint64_t target, int32_t *err) {
-    if (threadIdx.x == 0) {
+template <int NJ, bool ACQ = false>
+__device__ __forceinline__ void bar_wait(const uint64_t *flags, int G, uint32_t tag, int32_t *err) {
+    if (threadIdx.x < WAVE) {
+        const int lane = threadIdx.x;
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        while (__hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            __builtin_amdgcn_s_sleep(1);
+        for (;;) {
+            uint64_t wd[NJ];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) {
+                const int i = lane + WAVE * j;
+                wd[j] = i < G ? __hip_atomic_load(flags + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                              : ((uint64_t)tag << 32);
+            }
+            bool ready = true;
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) ready = ready && (uint32_t)(wd[j] >> 32) == tag;
+            if (__ballot(!ready) == 0ull) break;
             if (__builtin_amdgcn_s_memrealtime() - t0 > SPIN_TICKS) {
-                atomicOr(err, MOE_DEVERR_TIMEOUT);
+                if (lane == 0) atomicOr(err, MOE_DEVERR_TIMEOUT);
                 break;
             }
+            __builtin_amdgcn_s_sleep(1);
         }
         if (ACQ) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
@@ -222,7 +239,6 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     __shared__ int s_act_e[FMAX_P], s_act_start[FMAX_P], s_act_cnt[FMAX_P];
     __shared__ int s_nact;
     __shared__ float s_part[FWPB * FMAX_T * FMAX_WR];   // down partials [wave][token][work-group row]
-    __shared__ uint64_t s_base;
     __shared__ uint32_t s_tag;
 
     const int T = p.T, H = p.H, E = p.E, K = p.K, I = p.I, P = T * K;
@@ -239,9 +255,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     uint32_t *s_trash = s_sel + ((E + 3) & ~3);
 
     if (tid == 0) {
-        s_base = bar_base(p.bar, G);
-        // one grid barrier per call, so base/G counts the completed calls on this workspace
-        s_tag = (uint32_t)(s_base / (uint64_t)G) + 1u;
+        s_tag = (uint32_t)call_count(p.bar) + 1u;
         s_nact = 0;
     }
     for (int i = tid; i < FWPB * FMAX_T * FMAX_WR; i += FTHREADS) s_part[i] = 0.f;
@@ -484,30 +498,31 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             for (int c = 0; c < NC; ++c) ds[c] = 0u;
         }
     };
-    bar_arrive(p.bar);
+    bar_arrive(p.flags, s_tag);
     load_item(0, dqa, dsa);
     if (total > 1) load_item(1, dqb, dsb);
-    bar_wait(p.bar, s_base + (uint64_t)G, p.err);
+    if (G <= 4 * WAVE)
+        bar_wait<4>(p.flags, G, s_tag, p.err);
+    else
+        bar_wait<FMAX_G / WAVE>(p.flags, G, s_tag, p.err);
+    if (blockIdx.x == 0 && tid == 0) __hip_atomic_fetch_add(p.bar, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
-    // stage h' (all P slots, sorted order) into LDS with agent-scope loads, eight words
-    // in flight per thread
+    // stage h' (all P slots, sorted order; P*I*ab is a multiple of 16) into LDS with
+    // 16-byte loads past the non-coherent caches, eight in flight per thread
     {
-        const int n8 = P * I * ab / 8;
-        const int nst = FTHREADS;
-        const uint64_t *src = reinterpret_cast<const uint64_t *>(p.hbuf);
-        uint64_t *dst = reinterpret_cast<uint64_t *>(smem);
-        for (int i0 = tid; i0 < n8; i0 += 8 * nst) {
-            uint64_t v[8];
+        const uint32_t nb = (uint32_t)(P * I * ab);
+        const int n16 = (int)(nb / 16);
+        const rsrc_t hr = make_rsrc(p.hbuf, nb);
+        uint4 *dst = reinterpret_cast<uint4 *>(smem);
+        for (int i0 = tid; i0 < n16; i0 += 8 * FTHREADS) {
+            uint4 v[8];
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int i = i0 + b * nst;
-                v[b] = i < n8 ? __hip_atomic_load(src + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
-            }
+            for (int b = 0; b < 8; ++b) v[b] = ld_rsrc16_agent(hr, (uint32_t)(i0 + b * FTHREADS) * 16);
             __builtin_amdgcn_sched_barrier(0);   // all eight loads before the first store
 #pragma unroll
             for (int b = 0; b < 8; ++b) {
-                const int i = i0 + b * nst;
-                if (i < n8) dst[i] = v[b];
+                const int i = i0 + b * FTHREADS;
+                if (i < n16) dst[i] = v[b];
             }
         }
     }
@@ -724,8 +739,8 @@ bool decode_fused_coresident(const moe_shape &s) {
         (void)hipGetLastError();
         return true;   // no device: nothing will be launched
     }
-    // the output-row budget on this device's grid
-    if (fused_rows_for(s, G) > FMAX_WR) return false;
+    // the barrier's flag words and the output-row budget on this device's grid
+    if (G > FMAX_G || fused_rows_for(s, G) > FMAX_WR) return false;
     switch (s.weight_dtype) {
         case MOE_F32: return fused_fits<FmtF32, FmtF32>(s);
         case MOE_BF16: return fused_fits<FmtBF16, FmtBF16>(s);
@@ -751,7 +766,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     const WsLayout L = ws_layout(s);
     const int cus = fused_grid();
     if (cus <= 0) return hipErrorNoDevice;
-    if (fused_rows_for(s, cus) > FMAX_WR) return hipErrorInvalidConfiguration;
+    if (cus > FMAX_G || fused_rows_for(s, cus) > FMAX_WR) return hipErrorInvalidConfiguration;
     FusedParams prm{};
     prm.x = static_cast<const uint8_t *>(x);
     prm.wr = static_cast<const uint8_t *>(wr);
@@ -773,6 +788,7 @@ hipError_t launch_decode_fused(const moe_shape &s, const void *x, const void *wr
     prm.logits = reinterpret_cast<uint64_t *>(wsb + L.tagged);
     prm.hbuf = wsb + L.h;
     prm.bar = reinterpret_cast<uint64_t *>(wsb + L.ctrl + 8);
+    prm.flags = reinterpret_cast<uint64_t *>(wsb + L.flags);
     prm.err = reinterpret_cast<int32_t *>(wsb + L.ctrl);
     prm.T = s.num_tokens;
     prm.H = s.hidden;

@@ -81,6 +81,12 @@ __device__ __forceinline__ uint4 ld_rsrc16(rsrc_t r, uint32_t off) {
     const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// 16 bytes at byte offset off past the non-coherent caches (sc1: the load an agent-scope
+// atomic load is), for data other work-groups wrote with agent-scope stores
+__device__ __forceinline__ uint4 ld_rsrc16_agent(rsrc_t r, uint32_t off) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 16);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ uint32_t ld_rsrc_u8(rsrc_t r, uint32_t off) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0);
 }

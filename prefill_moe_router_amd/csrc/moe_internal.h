@@ -22,6 +22,8 @@ constexpr int kGroupedTileM = MOE_TILE_M;
 
 // largest token count the fused single-kernel decode path takes
 constexpr int kFusedMaxTokens = 8;
+// largest grid of the fused decode kernel (one work-group per CU)
+constexpr int kFusedMaxGroups = 1024;
 
 inline size_t act_bytes(int dt) { return dt == MOE_F32 ? 4 : 2; }
 
@@ -36,13 +38,14 @@ inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM 
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word; [8] the fused decode kernel's 64-bit
-// call counter, which only grows (the tag of the words that kernel publishes is
-// derived from it, so it must never be reset on its own).
+// call counter, which only grows (the tag of the words that kernel publishes --
+// logits and barrier flags -- is derived from it, so it must never be reset on
+// its own).
 // tokens per work-group of the MFMA router (and per count row of its grouping output)
 constexpr int kRouterRows = 32;
 
 struct WsLayout {
-    size_t ctrl, tagged, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, tiles, gcounts, h, o, total;
+    size_t ctrl, tagged, flags, logits, ids, wts, offsets, sorted, slot_pos, active, mtile, tiles, gcounts, h, o, total;
 };
 
 inline WsLayout ws_layout(const moe_shape &s) {
@@ -57,6 +60,7 @@ inline WsLayout ws_layout(const moe_shape &s) {
     };
     L.ctrl = take(256);
     L.tagged = take((size_t)kFusedMaxTokens * E * 8);   // fused decode: logit | call tag words
+    L.flags = take((size_t)kFusedMaxGroups * 8);        // fused decode: per-work-group barrier tags
     L.logits = take(T * E * 4);
     L.ids = take(P * 4);
     L.wts = take(P * 4);
@@ -127,9 +131,9 @@ bool grouped_supported(const moe_shape &s);
 bool router_mfma_supported(const moe_shape &s);
 hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-// m-tile offsets and the tile table from existing expert offsets
+// m-tile offsets and the tile table (tiles of `rows` rows) from existing expert offsets
 hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
-                                hipStream_t st);
+                                int rows, hipStream_t st);
 // h'[p][i] = (wts ? wts[slot] : 1) * silu(g) * u, bf16, sorted order
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
                               const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const float *wts,
@@ -142,6 +146,10 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
 // launchers above route to them when the shape allows
 bool wide_gateup_supported(const moe_shape &s);
 bool wide_down_supported(const moe_shape &s);
+// m-tile height the grouping must use for the grouped GEMMs of moe_forward on `s` (128 or,
+// for the bf16 large-tile configuration, its own height); the register-staged kernels
+// (other formats, the fp32 sorted down projection of moe_expert_ffn) take 128
+int grouped_tile_rows(const moe_shape &s);
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
                               const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
