@@ -50,7 +50,6 @@ constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_G = kFusedMaxGroups; // work-groups (one per CU)
 constexpr int FROUNDS_MAX_K = 12;       // top-k by arg-max rounds up to this k, radix walk above
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
-constexpr int FMAX_RT = 8;              // rows of a down-projection tile
 constexpr int FMAX_WR = 32;             // output rows of one work-group (its tiles' rows)
 constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
 constexpr uint64_t SPIN_TICKS = 20000000ull;  // 0.2 s of the 100 MHz real-time clock
@@ -622,7 +621,6 @@ static bool fused_bucket_built(int cg, int cr, int cd);
 static int bucket(int chunks_per_lane);
 
 bool decode_fused_supported(const moe_shape &s) {
-    const size_t ab = act_bytes(s.act_dtype);
     const size_t P = (size_t)s.num_tokens * s.top_k;
     if (s.num_tokens < 1 || s.num_tokens > FMAX_T || P > FMAX_P) return false;
     const int epc = weight_chunk_elems(s.weight_dtype);

@@ -131,9 +131,9 @@ bool grouped_supported(const moe_shape &s);
 bool router_mfma_supported(const moe_shape &s);
 hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-// m-tile offsets and the tile table (tiles of `rows` rows) from existing expert offsets
+// m-tile offsets and the tile table from existing expert offsets
 hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
-                                int rows, hipStream_t st);
+                                hipStream_t st);
 // h'[p][i] = (wts ? wts[slot] : 1) * silu(g) * u, bf16, sorted order
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
                               const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const float *wts,
@@ -146,10 +146,6 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
 // launchers above route to them when the shape allows
 bool wide_gateup_supported(const moe_shape &s);
 bool wide_down_supported(const moe_shape &s);
-// m-tile height the grouping must use for the grouped GEMMs of moe_forward on `s` (128 or,
-// for the bf16 large-tile configuration, its own height); the register-staged kernels
-// (other formats, the fp32 sorted down projection of moe_expert_ffn) take 128
-int grouped_tile_rows(const moe_shape &s);
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
                               const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
