@@ -48,16 +48,27 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 # WRITE_SIZE, KiB per dispatch), scaled by what the same counters read for a device copy
 # of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
 # the counters were taken on (sha1 of the listed files); otherwise traffic is null.
+_SRC_DEVICE = ("prefill_moe_router_amd/csrc/moe_device.h", "ca7c0c51793891245d22c2b10376c20f0cb12215")
+_SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "97ad174ffcd54e6bc86a1c92241f2a49c2fb621e"),
+                   _SRC_DEVICE])
+_SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "184620b7f66e1d476dfca39d16d3330072077942"),
+                  _SRC_DEVICE])
+_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "e8c74707890d4d53d20e69570381ea18c8a1184c"),
+                     _SRC_DEVICE])
+
+
+def _traffic(kernel, fetch_kib, write_kib, sources):
+    return dict(kernel=kernel, fetch_kib=fetch_kib, write_kib=write_kib, fetch_scale=2.0, write_scale=1.0,
+                sources=sources)
+
+
 COUNTED_TRAFFIC = {
-    "decode1": dict(kernel="decode_fused", fetch_kib=37450.7, write_kib=240.1, fetch_scale=2.0,
-                    write_scale=1.0, sources={
-                        "prefill_moe_router_amd/csrc/decode_fused.hip": "2eca5cb8dc38ff70a79a81ab942a99ce7feffdad",
-                        "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
-    "prefill8192": dict(kernel="gate_up", fetch_kib=1045638.3, write_kib=98308.9, fetch_scale=2.0,
-                        write_scale=1.0, sources={
-                            "prefill_moe_router_amd/csrc/grouped_gemm_wide.hip":
-                                "184620b7f66e1d476dfca39d16d3330072077942",
-                            "prefill_moe_router_amd/csrc/moe_device.h": "e823e149880173a9c517ccb2e4c56b6dd035a292"}),
+    "decode1": _traffic("decode_fused", 37518.4, 240.1, _SRC_FUSED),
+    "decode8": _traffic("decode_fused", 197213.8, 1640.5, _SRC_FUSED),
+    "mxfp4_decode1": _traffic("decode_fused", 27694.9, 344.1, _SRC_FUSED),
+    "mxfp4_decode8": _traffic("decode_fused", 188509.7, 2248.5, _SRC_FUSED),
+    "prefill8192": _traffic("gate_up", 1067694.4, 98308.6, _SRC_WIDE),
+    "mxfp4_prefill4096": _traffic("gate_up", 1087604.6, 65536.0, _SRC_GROUPED),
 }
 
 
