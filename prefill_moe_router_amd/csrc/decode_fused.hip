@@ -357,14 +357,8 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
             const uint32_t m = e < E ? s_sel[e] : 0u;
             const int cnt = __popc(m);
             const uint64_t bal = __ballot(m != 0u);
-            // inclusive prefix of the counts over the 64 lanes (shifts within rows of 16,
-            // then the row totals through the row broadcasts)
-            int inc = cnt;
-#pragma unroll
-            for (int sh = 1; sh < WAVE; sh <<= 1) {
-                const int v = __shfl_up(inc, sh, WAVE);
-                inc += lane >= sh ? v : 0;
-            }
+            // inclusive prefix of the counts over the 64 lanes
+            const int inc = (int)wave_incl_sum_u((uint32_t)cnt);
             if (m != 0u) {
                 const int dl = nact + __popcll(bal & lt);
                 const int start = tot + inc - cnt;
@@ -380,7 +374,7 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
                 }
             }
             nact += __popcll(bal);
-            tot += __shfl(inc, WAVE - 1, WAVE);
+            tot += __builtin_amdgcn_readlane(inc, WAVE - 1);
         }
         if (lane == 0) s_nact = nact;
     }

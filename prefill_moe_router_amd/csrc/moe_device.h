@@ -274,6 +274,17 @@ template <int CTRL, int ROW_MASK = 0xf>
 __device__ __forceinline__ uint32_t dpp_u(uint32_t v, uint32_t fill) {
     return (uint32_t)__builtin_amdgcn_update_dpp((int)fill, (int)v, CTRL, ROW_MASK, 0xf, false);
 }
+// inclusive prefix sum over the 64 lanes: shifts within rows of 16 lanes, then the row
+// totals through the row broadcasts (lane 63 ends with the total)
+__device__ __forceinline__ uint32_t wave_incl_sum_u(uint32_t v) {
+    v += dpp_u<0x111, 0xf>(v, 0u);   // row_shr:1
+    v += dpp_u<0x112, 0xf>(v, 0u);   // row_shr:2
+    v += dpp_u<0x114, 0xf>(v, 0u);   // row_shr:4
+    v += dpp_u<0x118, 0xf>(v, 0u);   // row_shr:8
+    v += dpp_u<0x142, 0xa>(v, 0u);   // row_bcast:15 into rows 1 and 3
+    v += dpp_u<0x143, 0xc>(v, 0u);   // row_bcast:31 into rows 2 and 3
+    return v;
+}
 template <int N>
 __device__ __forceinline__ void wave_umax_n(uint32_t (&v)[N]) {
 #define MOE_UMAX_STEP(CTRL, RM)                                                     \
