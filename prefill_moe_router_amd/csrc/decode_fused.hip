@@ -49,6 +49,8 @@ constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_G = kFusedMaxGroups; // work-groups (one per CU)
 constexpr int FROUNDS_MAX_K = 12;       // top-k by arg-max rounds up to this k, radix walk above
+constexpr int FRANK_MAX_E = 128;        // one token: top-k by counted ranks up to this E (measured:
+                                        // 0.7 us faster at E = 128, 0.5 us slower at E = 256)
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
 constexpr int FMAX_WR = 32;             // output rows of one work-group (its tiles' rows)
 constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
@@ -250,8 +252,11 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     const size_t lg_off = ((size_t)T * H * ab + 15) & ~(size_t)15;   // LDS logits after the staged x
     // after the logits: the per-expert token masks of the top-k, then 64 words per wave
     // that lanes with nothing to store write to
-    uint32_t *s_sel = reinterpret_cast<uint32_t *>(smem + lg_off + (size_t)T * E * 4);
+    const size_t sel_off = (lg_off + (size_t)T * E * 4 + 15) & ~(size_t)15;
+    uint32_t *s_sel = reinterpret_cast<uint32_t *>(smem + sel_off);
     uint32_t *s_trash = s_sel + ((E + 3) & ~3);
+    // then (one token) the experts' packed selection keys (16-byte aligned)
+    uint64_t *s_pk = reinterpret_cast<uint64_t *>(s_trash + FWPB * WAVE);
 
     if (tid == 0) {
         s_tag = (uint32_t)call_count(p.bar) + 1u;
@@ -311,72 +316,136 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
     }
     __syncthreads();
-    // top-k of token t in wave t: K rounds of a wave arg-max for small K, otherwise a radix
-    // walk over the logit keys (exact either way, ties to the lower id); bit t of s_sel[e] marks that token t
-    // kept expert e, and its gate weight replaces the logit at s_lg[t][e]
-    if (wave < T) {
-        const float *lg = s_lg + (size_t)wave * E;
-        int *ii = s_ids + wave * K;
-        float *ww = s_w + wave * K;
-        uint32_t *tr = s_trash + wave * WAVE;
-        if (K <= FROUNDS_MAX_K) {
-            if (E <= 64) wave_topk_multi<1, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 128) wave_topk_multi<2, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 256) wave_topk_multi<4, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 512) wave_topk_multi<8, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else wave_topk_multi<16, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-        } else {
-            if (E <= 64) wave_topk_multi<1, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 128) wave_topk_multi<2, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 256) wave_topk_multi<4, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else if (E <= 512) wave_topk_multi<8, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
-            else wave_topk_multi<16, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+    if (T == 1 && E <= FRANK_MAX_E) {
+        // One token: every expert's rank is the number of experts that beat it (a larger
+        // logit key, or the same key and a lower id), counted with the comparison range
+        // split over all the work-group's waves; ranks 0..K-1 are the kept experts.  The
+        // same selection as the per-wave top-k below, in a few dependent steps instead of K
+        // rounds in one wave (the counting is E*E comparisons, so only for small E).  One
+        // slot per kept expert, in ascending id, is the grouping.
+        uint32_t *s_rank = s_sel;   // zeroed at kernel start
+        for (int e = tid; e < E; e += FTHREADS)
+            s_pk[e] = ((uint64_t)f32_order_key(s_lg[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+        __syncthreads();
+        const int epad = (E + WAVE - 1) / WAVE * WAVE;
+        const int nparts = epad >= FTHREADS ? 1 : FTHREADS / epad;
+        const int span = (E + nparts - 1) / nparts;
+        for (int i = tid; i < epad * nparts; i += FTHREADS) {
+            const int e = i % epad, part = i / epad;   // part is the same in the whole wave
+            const int j0 = part * span, j1 = min(E, j0 + span);
+            const uint64_t mine = e < E ? s_pk[e] : ~0ull;
+            uint32_t r = 0;
+#pragma unroll 8
+            for (int j = j0; j < j1; ++j) r += s_pk[j] > mine ? 1u : 0u;
+            if (e < E) atomicAdd(s_rank + e, r);
         }
-        // read back as the 32-bit words the top-k stored (other lanes of this wave wrote
-        // them; a wave's LDS accesses complete in order)
-        for (int j = lane; j < K; j += WAVE) {
-            const int e = (int)reinterpret_cast<const uint32_t *>(ii)[j];
-            const float wt = __uint_as_float(reinterpret_cast<const uint32_t *>(ww)[j]);
-            s_lg[(size_t)wave * E + e] = wt;
-            if (blockIdx.x == 0) {
-                if (p.ids_out) p.ids_out[wave * K + j] = e;
-                if (p.w_out) p.w_out[wave * K + j] = wt;
+        __syncthreads();
+        for (int e = tid; e < E; e += FTHREADS) {
+            const uint32_t r = s_rank[e];
+            if (r < (uint32_t)K) s_ids[r] = e;   // s_ids by rank
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // lane j < K: the expert of rank j, its place in ascending id, its weight
+            const bool on = lane < K;
+            const int ej = on ? s_ids[lane] : 0;
+            const float m = f32_from_order_key((uint32_t)(s_pk[s_ids[0]] >> 32));   // the largest logit
+            int pos = 0;
+            for (int l = 0; l < K; ++l) pos += s_ids[l] < ej ? 1 : 0;
+            const float pe = on ? __expf(s_lg[ej] - m) : 0.f;
+            float z;
+            if (p.renorm) {
+                z = wave_sum_u(pe);
+            } else {
+                float zs = 0.f;
+                for (int e0 = 0; e0 < E; e0 += WAVE) {
+                    const int e = e0 + lane;
+                    zs += e < E ? __expf(s_lg[e] - m) : 0.f;
+                }
+                z = wave_sum_u(zs);
             }
-        }
-    }
-    __syncthreads();
-    // Grouping (wave 0) from the token masks: the active experts are those with a nonzero
-    // mask, in ascending id; an expert's slots are its tokens in ascending order (slot
-    // t*k+j ascends with t), so its count is the mask's popcount and its start the
-    // exclusive prefix of the counts.
-    if (wave == 0) {
-        const uint64_t lt = lanemask_lt();
-        int nact = 0, tot = 0;
-        for (int e0 = 0; e0 < E; e0 += WAVE) {
-            const int e = e0 + lane;
-            const uint32_t m = e < E ? s_sel[e] : 0u;
-            const int cnt = __popc(m);
-            const uint64_t bal = __ballot(m != 0u);
-            // inclusive prefix of the counts over the 64 lanes
-            const int inc = (int)wave_incl_sum_u((uint32_t)cnt);
-            if (m != 0u) {
-                const int dl = nact + __popcll(bal & lt);
-                const int start = tot + inc - cnt;
-                s_act_e[dl] = e;
-                s_act_start[dl] = start;
-                s_act_cnt[dl] = cnt;
-                uint32_t mm = m;
-                for (int c = 0; mm; ++c) {
-                    const int t = __builtin_ctz(mm);
-                    mm &= mm - 1;
-                    s_tok[start + c] = t;
-                    s_wq[start + c] = s_lg[(size_t)t * E + e];
+            const float wj = pe / z;
+            if (on) {
+                s_act_e[pos] = ej;
+                s_act_start[pos] = pos;
+                s_act_cnt[pos] = 1;
+                s_tok[pos] = 0;
+                s_wq[pos] = wj;
+                if (blockIdx.x == 0) {
+                    if (p.ids_out) p.ids_out[pos] = ej;
+                    if (p.w_out) p.w_out[pos] = wj;
                 }
             }
-            nact += __popcll(bal);
-            tot += __builtin_amdgcn_readlane(inc, WAVE - 1);
+            if (lane == 0) s_nact = K;
         }
-        if (lane == 0) s_nact = nact;
+    } else {
+        // top-k of token t in wave t: K rounds of a wave arg-max for small K, otherwise a radix
+        // walk over the logit keys (exact either way, ties to the lower id); bit t of s_sel[e] marks that token t
+        // kept expert e, and its gate weight replaces the logit at s_lg[t][e]
+        if (wave < T) {
+            const float *lg = s_lg + (size_t)wave * E;
+            int *ii = s_ids + wave * K;
+            float *ww = s_w + wave * K;
+            uint32_t *tr = s_trash + wave * WAVE;
+            if (K <= FROUNDS_MAX_K) {
+                if (E <= 64) wave_topk_multi<1, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 128) wave_topk_multi<2, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 256) wave_topk_multi<4, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 512) wave_topk_multi<8, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else wave_topk_multi<16, 1, true>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            } else {
+                if (E <= 64) wave_topk_multi<1, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 128) wave_topk_multi<2, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 256) wave_topk_multi<4, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else if (E <= 512) wave_topk_multi<8, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+                else wave_topk_multi<16, 1, false>(lg, E, K, p.renorm, 1, ii, ww, s_sel, wave, tr);
+            }
+            // read back as the 32-bit words the top-k stored (other lanes of this wave wrote
+            // them; a wave's LDS accesses complete in order)
+            for (int j = lane; j < K; j += WAVE) {
+                const int e = (int)reinterpret_cast<const uint32_t *>(ii)[j];
+                const float wt = __uint_as_float(reinterpret_cast<const uint32_t *>(ww)[j]);
+                s_lg[(size_t)wave * E + e] = wt;
+                if (blockIdx.x == 0) {
+                    if (p.ids_out) p.ids_out[wave * K + j] = e;
+                    if (p.w_out) p.w_out[wave * K + j] = wt;
+                }
+            }
+        }
+        __syncthreads();
+        // Grouping (wave 0) from the token masks: the active experts are those with a nonzero
+        // mask, in ascending id; an expert's slots are its tokens in ascending order (slot
+        // t*k+j ascends with t), so its count is the mask's popcount and its start the
+        // exclusive prefix of the counts.
+        if (wave == 0) {
+            const uint64_t lt = lanemask_lt();
+            int nact = 0, tot = 0;
+            for (int e0 = 0; e0 < E; e0 += WAVE) {
+                const int e = e0 + lane;
+                const uint32_t m = e < E ? s_sel[e] : 0u;
+                const int cnt = __popc(m);
+                const uint64_t bal = __ballot(m != 0u);
+                // inclusive prefix of the counts over the 64 lanes
+                const int inc = (int)wave_incl_sum_u((uint32_t)cnt);
+                if (m != 0u) {
+                    const int dl = nact + __popcll(bal & lt);
+                    const int start = tot + inc - cnt;
+                    s_act_e[dl] = e;
+                    s_act_start[dl] = start;
+                    s_act_cnt[dl] = cnt;
+                    uint32_t mm = m;
+                    for (int c = 0; mm; ++c) {
+                        const int t = __builtin_ctz(mm);
+                        mm &= mm - 1;
+                        s_tok[start + c] = t;
+                        s_wq[start + c] = s_lg[(size_t)t * E + e];
+                    }
+                }
+                nact += __popcll(bal);
+                tot += __builtin_amdgcn_readlane(inc, WAVE - 1);
+            }
+            if (lane == 0) s_nact = nact;
+        }
     }
     __syncthreads();
     const int U = s_nact;
@@ -568,12 +637,14 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
     }
 }
 
-// dynamic LDS of the fused kernel: the staged x, the logits, the expert token masks and
-// the per-wave discard words after it (phases 0-2), or the staged h' (phase 3)
+// dynamic LDS of the fused kernel: the staged x, the logits, the expert token masks, the
+// per-wave discard words and the packed selection keys after it (phases 0-2), or the
+// staged h' (phase 3)
 static size_t fused_lds_bytes(const moe_shape &s) {
     const size_t xb = (size_t)s.num_tokens * s.hidden * act_bytes(s.act_dtype);
-    const size_t front = ((xb + 15) & ~(size_t)15) + (size_t)s.num_tokens * s.num_experts * 4 +
-                         (size_t)((s.num_experts + 3) & ~3) * 4 + (size_t)FWPB * WAVE * 4;
+    const size_t front = ((xb + 15) & ~(size_t)15) + (((size_t)s.num_tokens * s.num_experts * 4 + 15) & ~(size_t)15) +
+                         (size_t)((s.num_experts + 3) & ~3) * 4 + (size_t)FWPB * WAVE * 4 +
+                         (size_t)s.num_experts * 8;
     return std::max(front, (size_t)s.num_tokens * s.top_k * s.intermediate * act_bytes(s.act_dtype));
 }
 

@@ -414,6 +414,36 @@ def test_forward_k_and_renorm_edges(K, renorm, E):
     compare_forward(li, got, label=f"K={K} renorm={renorm} E={E}")
 
 
+@pytest.mark.parametrize("K,renorm,E", [(1, True, 8), (8, True, 8), (3, False, 16), (32, True, 64), (8, False, 128),
+                                         (8, True, 128), (8, False, 256)])
+def test_forward_single_token_k_and_renorm(K, renorm, E):
+    """One decode token: the fused kernel's one-token selection (ranks counted over the work-group,
+    E <= 128) and its per-wave top-k (E = 256), with k = 1, k = E, renorm on and off."""
+    note(f"single token K={K} renorm={renorm} E={E}")
+    li = layer_of(synth.Shape(1, 256, E, K, 128, "bf16", "bf16", bias="normal", renorm=renorm), batch=3)
+    got = run_forward(DevLayer(li))
+    assert pm.forward_stages(lshape(li)) == ["decode_fused"]
+    compare_forward(li, got, label=f"T=1 K={K} renorm={renorm} E={E}")
+
+
+@pytest.mark.parametrize("E", [12, 200])
+def test_forward_single_token_exact_ties(E):
+    """One token whose best logits tie exactly (identical router rows): the lower ids win, in the
+    fused kernel's one-token selection (E = 12) and its per-wave top-k (E = 200)."""
+    li = layer_of(synth.Shape(1, 256, E, 3, 128, "bf16", "bf16"))
+    assert pm.forward_stages(lshape(li)) == ["decode_fused"]
+    row = synth.bf16_bits_to_f32(li.wr[2])
+    s = float(synth.bf16_bits_to_f32(li.x[0]).astype(np.float64) @ row.astype(np.float64))
+    popular = synth.f32_to_bf16_bits(row * (64.0 if s > 0 else -64.0))   # exact: a power of two
+    for e in (2, 5, 9, 11):   # four equal, largest logits for three places
+        li.wr[e] = popular
+    got = run_forward(DevLayer(li))
+    ref = oracle.router(oracle_layer(li))
+    assert ref["ids"][0].tolist() == [2, 5, 9]
+    np.testing.assert_array_equal(got["ids"], ref["ids"])
+    np.testing.assert_allclose(got["w"], ref["w"], rtol=0, atol=W_TOL)
+
+
 def test_forward_zero_tokens_is_noop():
     li = layer("c0_tiny_f32")
     dl = DevLayer(li)
