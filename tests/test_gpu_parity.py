@@ -407,11 +407,14 @@ def test_forward_token_sweep(T):
     compare_forward(li, got, label=f"sweep T={T}")
 
 
+@pytest.mark.parametrize("I", [64, 128])
 @pytest.mark.parametrize("K,renorm,E", [(1, True, 8), (8, True, 8), (3, False, 16), (32, True, 64)])
-def test_forward_k_and_renorm_edges(K, renorm, E):
-    li = layer_of(synth.Shape(6, 256, E, K, 64, "bf16", "bf16", bias="normal", renorm=renorm))
+def test_forward_k_and_renorm_edges(K, renorm, E, I):
+    """Six tokens: I = 64 runs the staged decode kernels, I = 128 the fused kernel's per-wave top-k."""
+    li = layer_of(synth.Shape(6, 256, E, K, I, "bf16", "bf16", bias="normal", renorm=renorm))
+    assert pm.forward_stages(lshape(li))[0] == ("decode_fused" if I == 128 else "router_logits")
     got = run_forward(DevLayer(li))
-    compare_forward(li, got, label=f"K={K} renorm={renorm} E={E}")
+    compare_forward(li, got, label=f"K={K} renorm={renorm} E={E} I={I}")
 
 
 @pytest.mark.parametrize("K,renorm,E", [(1, True, 8), (8, True, 8), (3, False, 16), (32, True, 64), (8, False, 128),
