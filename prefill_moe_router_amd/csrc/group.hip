@@ -14,7 +14,7 @@ namespace moe {
 
 // Block-wide exclusive scan of n (<= a few thousand) LDS ints in place; returns the
 // total.  Each thread sums a run of consecutive entries, the runs are scanned inside
-// each wave with shuffles and across the (<= 16) waves by the first wave, and each
+// each wave with DPP row shifts and across the (<= 16) waves by the first wave, and each
 // thread then rewrites its run: two work-group barriers in all.  tmp holds blockDim.x
 // ints (only the first 32 are used).
 __device__ int block_exclusive_scan(int *data, int n, int *tmp) {
@@ -24,22 +24,12 @@ __device__ int block_exclusive_scan(int *data, int n, int *tmp) {
     const int b = min(n, tid * per), e = min(n, b + per);
     int local = 0;
     for (int i = b; i < e; ++i) local += data[i];
-    int incl = local;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-    }
+    const int incl = (int)wave_incl_sum_u((uint32_t)local);
     if (lane == 63) tmp[wave] = incl;
     __syncthreads();
     if (wave == 0) {
         const int wt = lane < nw ? tmp[lane] : 0;
-        int wi = wt;
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            const int v = __shfl_up(wi, off, 64);
-            if (lane >= off) wi += v;
-        }
+        const int wi = (int)wave_incl_sum_u((uint32_t)wt);
         if (lane < nw) tmp[16 + lane] = wi - wt;   // exclusive wave offsets
         if (lane == nw - 1) tmp[32] = wi;          // total
     }

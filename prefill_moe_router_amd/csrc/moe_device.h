@@ -120,12 +120,6 @@ __device__ __forceinline__ void barrier_nofence() { asm volatile("s_barrier" :::
 
 // ---- wave64 reductions -----------------------------------------------------------
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
-    return v;
-}
-
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (WAVE - 1); }
 
 // DPP move of v (fp32 bits); lanes with no source read `fill`
