@@ -48,7 +48,7 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 # WRITE_SIZE, KiB per dispatch), scaled by what the same counters read for a device copy
 # of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
 # the counters were taken on (sha1 of the listed files); otherwise traffic is null.
-_SRC_DEVICE = ("prefill_moe_router_amd/csrc/moe_device.h", "ef662ae7d99253ced4b10dab1b05fac3a3b60802")
+_SRC_DEVICE = ("prefill_moe_router_amd/csrc/moe_device.h", "83f51350610eff16eae366237d12db13d9a245a5")
 _SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "3ddbb79b7822226fd27b12ed468ee6c1c60046d4"),
                    _SRC_DEVICE])
 _SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "184620b7f66e1d476dfca39d16d3330072077942"),
@@ -63,12 +63,12 @@ def _traffic(kernel, fetch_kib, write_kib, sources):
 
 
 COUNTED_TRAFFIC = {
-    "decode1": _traffic("decode_fused", 37504.7, 240.1, _SRC_FUSED),
-    "decode8": _traffic("decode_fused", 197351.1, 1640.5, _SRC_FUSED),
-    "mxfp4_decode1": _traffic("decode_fused", 27675.0, 344.1, _SRC_FUSED),
-    "mxfp4_decode8": _traffic("decode_fused", 188487.9, 2248.5, _SRC_FUSED),
-    "prefill8192": _traffic("gate_up", 1054708.1, 98306.8, _SRC_WIDE),
-    "mxfp4_prefill4096": _traffic("gate_up", 1098805.1, 65536.0, _SRC_GROUPED),
+    "decode1": _traffic("decode_fused", 37512.3, 240.1, _SRC_FUSED),
+    "decode8": _traffic("decode_fused", 197338.3, 1640.5, _SRC_FUSED),
+    "mxfp4_decode1": _traffic("decode_fused", 27674.9, 344.1, _SRC_FUSED),
+    "mxfp4_decode8": _traffic("decode_fused", 188488.0, 2248.5, _SRC_FUSED),
+    "prefill8192": _traffic("gate_up", 1054363.6, 98308.6, _SRC_WIDE),
+    "mxfp4_prefill4096": _traffic("gate_up", 1095457.2, 65536.0, _SRC_GROUPED),
 }
 
 
