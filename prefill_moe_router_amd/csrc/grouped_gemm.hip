@@ -400,13 +400,14 @@ using CfgDN = TileCfg<MOE_DN_CFG>;
 using CfgR = TileCfg<MOE_R_CFG>;
 static_assert(CfgGU::BM == kGroupedTileM && CfgDN::BM == kGroupedTileM, "m-tiles follow the grouping");
 
-// m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / kGroupedTileM),
+// m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / rows),
 // and the tile table: tiles[t] = {first row, end row of the expert, expert, 0}
 __global__ __launch_bounds__(1024) void mtile_offsets_kernel(const int32_t *__restrict__ offsets, int E,
-                                                             int32_t *__restrict__ mtile_off, int4 *__restrict__ tiles) {
+                                                             int32_t *__restrict__ mtile_off, int4 *__restrict__ tiles,
+                                                             int rows) {
     __shared__ int s[1025];
     const int tid = threadIdx.x;
-    for (int e = tid; e < E; e += blockDim.x) s[e] = (offsets[e + 1] - offsets[e] + kGroupedTileM - 1) / kGroupedTileM;
+    for (int e = tid; e < E; e += blockDim.x) s[e] = (offsets[e + 1] - offsets[e] + rows - 1) / rows;
     __syncthreads();
     if (tid == 0) {
         int run = 0;
@@ -421,7 +422,7 @@ __global__ __launch_bounds__(1024) void mtile_offsets_kernel(const int32_t *__re
     for (int e = tid; e <= E; e += blockDim.x) mtile_off[e] = s[e];
     for (int e = tid; e < E; e += blockDim.x)
         for (int t = s[e]; t < s[e + 1]; ++t)
-            tiles[t] = make_int4(offsets[e] + (t - s[e]) * kGroupedTileM, offsets[e + 1], e, 0);
+            tiles[t] = make_int4(offsets[e] + (t - s[e]) * rows, offsets[e + 1], e, 0);
 }
 
 // y[t][n] = sum_j o'[t*k + j][n]  (bf16 rows of one token, fp32 sum, one rounding)
@@ -510,9 +511,9 @@ hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr,
 }
 
 hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
-                                hipStream_t st) {
+                                int rows, hipStream_t st) {
     hipLaunchKernelGGL(mtile_offsets_kernel, dim3(1), dim3(1024), 0, st, offsets, s.num_experts, mtile_off,
-                       reinterpret_cast<int4 *>(tiles));
+                       reinterpret_cast<int4 *>(tiles), rows);
     return hipGetLastError();
 }
 

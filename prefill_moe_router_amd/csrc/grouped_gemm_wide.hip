@@ -6,7 +6,8 @@
 //   DOWN   : o'[slot][n] = h'[p] . Wd[e][n]             (bf16, rows scattered to slot order)
 //
 // Design for gfx950:
-//  * A work-group owns a 128-row m-tile of one expert and 256 weight rows (GATEUP: 128
+//  * A work-group owns a 128-row m-tile of one expert (bf16 medium batches: 64 rows, which
+//    the grouping then emits) and 256 weight rows (GATEUP: 128
 //    intermediate columns of both gate and up; DOWN: 256 output columns).  bf16: 2 x 4
 //    waves of 64 rows x 64 weight rows (4 independent 32x32 MFMA accumulators; a 16-deep
 //    K slice reads 4 KB of operands from LDS per 4 MFMAs, against 5 KB for 32 x 128) in one
@@ -45,7 +46,6 @@ namespace moe {
 namespace {
 
 constexpr int NXCD = 8;
-constexpr int BM = 128;                 // rows per m-tile (the grouping's tile)
 constexpr int TBN = 256;                // weight rows per n-tile (all configurations)
 constexpr int BK = 32;                  // K elements of one step (two 16-deep MFMA slices)
 enum { WG_GATEUP = 0, WG_DOWN = 1 };
@@ -101,7 +101,7 @@ __device__ __forceinline__ int swz(int r) { return KH == 1 ? (r >> 2) & 3 : (r >
 // share of tiles.  Under each K loop they fetch the next tile's rows; after it, the next
 // tile's first two stages load into ring slots 0 and 1 while the epilogue transposes
 // through slot 2, so a tile's start no longer waits on the tile table and row list.
-template <int MODE, int WM, int WN, int OCC, bool MX, int KH, int NS, bool PER>
+template <int MODE, int BM, int WM, int WN, int OCC, bool MX, int KH, int NS, bool PER>
 __global__ __launch_bounds__(WM * WN * 64, OCC) void grouped_gemm_wide_kernel(WideParams p) {
     constexpr int NTH = WM * WN * 64;
     static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
@@ -521,7 +521,7 @@ struct WideCfg {
     static constexpr int NTH = WM * WN * 64;
 };
 
-template <int MODE, bool MX>
+template <int MODE, bool MX, int BM>
 hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     using C = WideCfg<MODE, MX>;
     constexpr size_t rowb = 64 * C::KH;
@@ -529,7 +529,7 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
     static_assert(lds_max <= 160 * 1024 - 2048, "LDS ring too large");
     static bool attr_done = false;
-    auto kern = grouped_gemm_wide_kernel<MODE, C::WM, C::WN, C::OCC, MX, C::KH, C::NS, C::PER>;
+    auto kern = grouped_gemm_wide_kernel<MODE, BM, C::WM, C::WN, C::OCC, MX, C::KH, C::NS, C::PER>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_max);
@@ -555,14 +555,13 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
     return hipGetLastError();
 }
 
-int mt_max_wide(const moe_shape &s) {
+int mt_max_wide(const moe_shape &s, int rows) {
     const long P = (long)s.num_tokens * s.top_k;
-    return (int)(P / BM + std::min<long>(s.num_experts, P));
+    return (int)(P / rows + std::min<long>(s.num_experts, P));
 }
 
 }  // namespace
 
-static_assert(BM == kGroupedTileM, "m-tiles follow the grouping");
 
 // K must be a multiple of 64 and at least 128 (an even number of 32-deep steps, at least
 // 4: two stages of 64); MXFP4 also wants K a multiple of 512 (whole 16-byte chunks of
@@ -583,6 +582,17 @@ bool wide_down_supported(const moe_shape &s) {
            s.hidden % CBN == 0 && wide_k_ok(s, s.intermediate);
 }
 
+// m-tile height of the grouped GEMMs of moe_forward on `s`: 64 rows for bf16 experts on the
+// large-tile kernels while the pairs average at most 48 per expert, else 128.  Measured on
+// the bf16 decode shape (H=2048, E=128, k=8, I=768): 64-row tiles 3-6% faster at 2-32 pairs
+// per expert (T = 32..512), 4% slower at 64 (T = 1024); the results are the same bits (each
+// output's K order does not depend on the tile).
+int grouped_tile_rows(const moe_shape &s) {
+    const long P = (long)s.num_tokens * s.top_k;
+    const bool bf16_wide = s.weight_dtype == MOE_BF16 && wide_gateup_supported(s) && wide_down_supported(s);
+    return bf16_wide && P <= 48L * s.num_experts ? kWideSmallTileM : kGroupedTileM;
+}
+
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
                               const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
@@ -601,10 +611,15 @@ hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_exper
     prm.K = s.hidden;
     prm.topk = s.top_k;
     prm.E = s.num_experts;
-    prm.mt_max = mt_max_wide(s);
     prm.nt = s.intermediate / (CBN / 2);
-    if (s.weight_dtype == MOE_MXFP4) return wide_launch<WG_GATEUP, true>(prm, st, ev0, ev1);
-    return wide_launch<WG_GATEUP, false>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXFP4) {
+        prm.mt_max = mt_max_wide(s, kGroupedTileM);
+        return wide_launch<WG_GATEUP, true, kGroupedTileM>(prm, st, ev0, ev1);
+    }
+    const int rows = grouped_tile_rows(s);
+    prm.mt_max = mt_max_wide(s, rows);
+    if (rows == kWideSmallTileM) return wide_launch<WG_GATEUP, false, kWideSmallTileM>(prm, st, ev0, ev1);
+    return wide_launch<WG_GATEUP, false, kGroupedTileM>(prm, st, ev0, ev1);
 }
 
 hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, const int32_t *sorted,
@@ -622,10 +637,15 @@ hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, con
     prm.K = s.intermediate;
     prm.topk = s.top_k;
     prm.E = s.num_experts;
-    prm.mt_max = mt_max_wide(s);
     prm.nt = s.hidden / CBN;
-    if (s.weight_dtype == MOE_MXFP4) return wide_launch<WG_DOWN, true>(prm, st, ev0, ev1);
-    return wide_launch<WG_DOWN, false>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXFP4) {
+        prm.mt_max = mt_max_wide(s, kGroupedTileM);
+        return wide_launch<WG_DOWN, true, kGroupedTileM>(prm, st, ev0, ev1);
+    }
+    const int rows = grouped_tile_rows(s);
+    prm.mt_max = mt_max_wide(s, rows);
+    if (rows == kWideSmallTileM) return wide_launch<WG_DOWN, false, kWideSmallTileM>(prm, st, ev0, ev1);
+    return wide_launch<WG_DOWN, false, kGroupedTileM>(prm, st, ev0, ev1);
 }
 
 }  // namespace moe

@@ -170,9 +170,12 @@ moe_status moe_expert_ffn(const moe_shape *shape, const void *x, const moe_exper
     if (use_grouped(*shape)) {
         int32_t *mtile = at<int32_t>(ws, L.mtile);
         int32_t *tiles = at<int32_t>(ws, L.tiles);
-        MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, tiles, st));
+        const int rows = grouped_tile_rows(*shape);
+        MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, tiles, rows, st));
         MOE_TRY(launch_gateup_mfma(*shape, x, *w, expert_offsets, sorted_slots, mtile, tiles, nullptr,
                                    at<void>(ws, L.h), st, nullptr, nullptr));
+        // the fp32 sorted-order down projection runs on the register-staged kernel (128-row tiles)
+        if (rows != kGroupedTileM) MOE_TRY(launch_mtile_offsets(*shape, expert_offsets, mtile, tiles, kGroupedTileM, st));
         MOE_TRY(launch_down_mfma(*shape, *w, expert_offsets, sorted_slots, mtile, tiles, at<void>(ws, L.h),
                                  expert_out, true, st, nullptr, nullptr));
         return MOE_OK;
@@ -277,7 +280,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
             ++si;
             MOE_TRY(around(se, si++, st, [&] {
                 return launch_group_from_router(*shape, ids, counts, offsets, sorted, slot_pos, active, mtile, tiles,
-                                                kGroupedTileM, st);
+                                                grouped_tile_rows(*shape), st);
             }));
         } else {
             if (router_mfma_supported(*shape)) {
@@ -289,7 +292,7 @@ moe_status forward_impl(const moe_shape *shape, const void *x, const void *w_rou
             MOE_TRY(around(se, si++, st, [&] { return launch_topk(*shape, logits, ids, wts, st); }));
             MOE_TRY(around(se, si++, st, [&] {
                 return launch_group2(*shape, ids, offsets, sorted, slot_pos, active, at<int32_t>(ws, L.gcounts), mtile,
-                                     tiles, kGroupedTileM, err, st);
+                                     tiles, grouped_tile_rows(*shape), err, st);
             }));
         }
         MOE_TRY(launch_gateup_mfma(*shape, x, *w, offsets, sorted, mtile, tiles, wts, h, st, se.start(si),

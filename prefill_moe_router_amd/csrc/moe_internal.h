@@ -19,6 +19,8 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 #define MOE_TILE_M 128
 #endif
 constexpr int kGroupedTileM = MOE_TILE_M;
+// the smaller m-tile of the bf16 large-tile GEMMs for medium batches (grouped_tile_rows)
+constexpr int kWideSmallTileM = 64;
 
 // largest token count the fused single-kernel decode path takes
 constexpr int kFusedMaxTokens = 8;
@@ -32,9 +34,9 @@ inline int weight_chunk_elems(int dt) {
     return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 8 : dt == MOE_MXINT8 ? 16 : 32;
 }
 
-// upper bound of the number of m-tiles of P pairs over E experts:
+// upper bound of the number of m-tiles of P pairs over E experts, for either tile height:
 // sum over experts of ceil(count / tile) <= P / tile + (number of nonempty experts)
-inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kGroupedTileM + (P < E ? P : E); }
+inline size_t grouped_tile_bound(size_t P, size_t E) { return P / kWideSmallTileM + (P < E ? P : E); }
 
 // Byte offsets of the regions of one workspace.  Region 0 holds the control
 // words: [0] the sticky device error word; [8] the fused decode kernel's 64-bit
@@ -131,9 +133,9 @@ bool grouped_supported(const moe_shape &s);
 bool router_mfma_supported(const moe_shape &s);
 hipError_t launch_router_mfma(const moe_shape &s, const void *x, const void *wr, const float *bias, float *logits,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
-// m-tile offsets and the tile table from existing expert offsets
+// m-tile offsets and the tile table (tiles of `rows` rows) from existing expert offsets
 hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int32_t *mtile_off, int32_t *tiles,
-                                hipStream_t st);
+                                int rows, hipStream_t st);
 // h'[p][i] = (wts ? wts[slot] : 1) * silu(g) * u, bf16, sorted order
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
                               const int32_t *sorted, const int32_t *mtile_off, const int32_t *tiles, const float *wts,
@@ -146,6 +148,9 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
 // launchers above route to them when the shape allows
 bool wide_gateup_supported(const moe_shape &s);
 bool wide_down_supported(const moe_shape &s);
+// m-tile height the grouping must use for the grouped GEMMs of moe_forward on `s` (the bf16
+// large-tile kernels take 64 or 128; every other kernel takes 128)
+int grouped_tile_rows(const moe_shape &s);
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
                               const int32_t *mtile_off, const int32_t *tiles, const float *wts, void *h,
                               hipStream_t st, hipEvent_t ev0, hipEvent_t ev1);
