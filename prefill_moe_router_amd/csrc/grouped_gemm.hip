@@ -396,9 +396,11 @@ struct TileCfg {
     static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, BK = BK_, NS = NS_;
 };
 using CfgGU = TileCfg<MOE_GU_CFG>;
+using CfgGU64 = TileCfg<64, 128, 2, 4, 64>;   // gate/up with the medium batches' 64-row m-tiles
 using CfgDN = TileCfg<MOE_DN_CFG>;
 using CfgR = TileCfg<MOE_R_CFG>;
-static_assert(CfgGU::BM == kGroupedTileM && CfgDN::BM == kGroupedTileM, "m-tiles follow the grouping");
+static_assert(CfgGU::BM == kGroupedTileM && CfgDN::BM == kGroupedTileM && CfgGU64::BM == kWideSmallTileM,
+              "m-tiles follow the grouping");
 
 // m-tile offsets of the experts' groups: mtile_off[e] = sum over e' < e of ceil(cnt[e'] / rows),
 // and the tile table: tiles[t] = {first row, end row of the expert, expert, 0}
@@ -517,10 +519,10 @@ hipError_t launch_mtile_offsets(const moe_shape &s, const int32_t *offsets, int3
     return hipGetLastError();
 }
 
-static int mt_max_of(const moe_shape &s) {
+static int mt_max_of(const moe_shape &s, int rows = kGroupedTileM) {
     const long P = (long)s.num_tokens * s.top_k;
-    // sum over experts of ceil(cnt/BM) <= P/BM + (number of nonempty experts)
-    return (int)(P / kGroupedTileM + std::min<long>(s.num_experts, P));
+    // sum over experts of ceil(cnt/rows) <= P/rows + (number of nonempty experts)
+    return (int)(P / rows + std::min<long>(s.num_experts, P));
 }
 
 hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *offsets,
@@ -547,6 +549,10 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.E = s.num_experts;
     prm.mt_max = mt_max_of(s);
     prm.nt = s.intermediate / CfgGU::BN;
+    if (s.weight_dtype == MOE_MXFP4 && grouped_tile_rows(s) == kWideSmallTileM) {
+        prm.mt_max = mt_max_of(s, kWideSmallTileM);
+        return gemm_launch<GM_GATEUP, CfgGU64, true>(prm, st, ev0, ev1);
+    }
     if (s.weight_dtype == MOE_MXFP4) return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
     if (s.weight_dtype == MOE_NVFP4) return gemm_launch<GM_GATEUP, CfgGU, true, true>(prm, st, ev0, ev1);
     if (s.weight_dtype == MOE_MXINT8) return gemm_launch<GM_GATEUP, CfgGU, true, false, true>(prm, st, ev0, ev1);

@@ -525,8 +525,16 @@ template <int MODE, bool MX, int BM>
 hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     using C = WideCfg<MODE, MX>;
     constexpr size_t rowb = 64 * C::KH;
-    constexpr size_t ring = (size_t)C::NS * (BM * rowb + CBN * (MX ? BK / 2 : rowb));
-    constexpr size_t lds_max = ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0);
+    constexpr size_t stage = BM * rowb + CBN * (MX ? BK / 2 : rowb);
+    constexpr size_t ring = (size_t)C::NS * stage;
+    // the epilogue's transposes: per wave, its rows x (half) its columns (GATEUP) or passes of
+    // 16 / 32 rows (DOWN), padded by 8 bf16 per row; in ring slot 2 for persistent
+    // work-groups, else from the start of the dynamic LDS
+    constexpr size_t wrows = CBN / C::WN;
+    constexpr size_t epi = (size_t)C::WM * C::WN * 2 *
+                           (MODE == WG_GATEUP ? (size_t)(BM / C::WM) * (wrows / 2 + 8) : (C::PER ? 16 : 32) * (wrows + 8));
+    static_assert(!C::PER || epi <= stage, "the epilogue fits ring slot 2");
+    constexpr size_t lds_max = std::max(ring + (MX ? (size_t)CBN * MX_MAX_K / 32 : 0), C::PER ? 0 : epi);
     static_assert(lds_max <= 160 * 1024 - 2048, "LDS ring too large");
     static bool attr_done = false;
     auto kern = grouped_gemm_wide_kernel<MODE, BM, C::WM, C::WN, C::OCC, MX, C::KH, C::NS, C::PER>;
@@ -536,7 +544,7 @@ hipError_t wide_launch(const WideParams &prm, hipStream_t st, hipEvent_t ev0, hi
         if (r != hipSuccess) return r;
         attr_done = true;
     }
-    const size_t lds = ring + (MX ? (size_t)CBN * prm.K / 32 : 0);
+    const size_t lds = std::max(ring + (MX ? (size_t)CBN * prm.K / 32 : 0), C::PER ? (size_t)0 : epi);
     constexpr int GM = group_m(MODE, MX);
     int nblk = (prm.mt_max + GM - 1) / GM * GM * prm.nt;
     nblk = (nblk + NXCD - 1) / NXCD * NXCD;
@@ -582,15 +590,21 @@ bool wide_down_supported(const moe_shape &s) {
            s.hidden % CBN == 0 && wide_k_ok(s, s.intermediate);
 }
 
-// m-tile height of the grouped GEMMs of moe_forward on `s`: 64 rows for bf16 experts on the
-// large-tile kernels while the pairs average at most 48 per expert, else 128.  Measured on
-// the bf16 decode shape (H=2048, E=128, k=8, I=768): 64-row tiles 3-6% faster at 2-32 pairs
-// per expert (T = 32..512), 4% slower at 64 (T = 1024); the results are the same bits (each
-// output's K order does not depend on the tile).
+// m-tile height of the grouped GEMMs of moe_forward on `s`: 64 rows while the pairs average
+// at most 48 per expert for bf16 experts on the large-tile kernels, or at most 32 for MXFP4
+// experts (register-staged gate/up, large-tile down); else 128.  The results are the same
+// bits either way (an output's K order does not depend on the tile).  Measured, layer time
+// with the grouped path forced:
+//  - bf16 decode shape (H=2048, E=128, k=8, I=768): 3-6% faster at 2-32 pairs per expert
+//    (T = 32..512), 4% slower at 64 (T = 1024);
+//  - MXFP4 shape (H=4096, E=256, k=8, I=1024): 11-14% faster at 3-6 pairs per expert, 8% at
+//    12, 3.5% at 24, 9% slower at 48 (T = 1536).
 int grouped_tile_rows(const moe_shape &s) {
-    const long P = (long)s.num_tokens * s.top_k;
-    const bool bf16_wide = s.weight_dtype == MOE_BF16 && wide_gateup_supported(s) && wide_down_supported(s);
-    return bf16_wide && P <= 48L * s.num_experts ? kWideSmallTileM : kGroupedTileM;
+    const long P = (long)s.num_tokens * s.top_k, E = s.num_experts;
+    if (s.weight_dtype == MOE_BF16 && wide_gateup_supported(s) && wide_down_supported(s))
+        return P <= 48 * E ? kWideSmallTileM : kGroupedTileM;
+    if (s.weight_dtype == MOE_MXFP4 && wide_down_supported(s)) return P <= 32 * E ? kWideSmallTileM : kGroupedTileM;
+    return kGroupedTileM;
 }
 
 hipError_t launch_gateup_wide(const moe_shape &s, const void *x, const moe_expert_weights &w, const int32_t *sorted,
@@ -639,7 +653,9 @@ hipError_t launch_down_wide(const moe_shape &s, const moe_expert_weights &w, con
     prm.E = s.num_experts;
     prm.nt = s.hidden / CBN;
     if (s.weight_dtype == MOE_MXFP4) {
-        prm.mt_max = mt_max_wide(s, kGroupedTileM);
+        const int rows = grouped_tile_rows(s);
+        prm.mt_max = mt_max_wide(s, rows);
+        if (rows == kWideSmallTileM) return wide_launch<WG_DOWN, true, kWideSmallTileM>(prm, st, ev0, ev1);
         return wide_launch<WG_DOWN, true, kGroupedTileM>(prm, st, ev0, ev1);
     }
     const int rows = grouped_tile_rows(s);

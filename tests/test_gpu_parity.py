@@ -594,10 +594,12 @@ def test_forward_grouped_wide_persistent_tiles():
     np.testing.assert_array_equal(pos, rpos)
 
 
-@pytest.mark.parametrize("T,H,E,K,I", [(300, 1024, 32, 4, 512), (160, 2048, 16, 8, 1024)])
+@pytest.mark.parametrize("T,H,E,K,I", [(300, 1024, 32, 4, 512), (160, 2048, 16, 8, 1024), (200, 1024, 32, 4, 512),
+                                       (90, 4096, 256, 8, 1024)])
 def test_forward_grouped_wide_tiles_mxfp4(T, H, E, K, I):
     """MXFP4 experts on the large-tile kernels (codes and scales loaded straight into LDS,
-    decoded per operand read): skewed groups, partial m-tiles, several n-tiles."""
+    decoded per operand read): skewed groups, partial m-tiles, several n-tiles.  The last two
+    shapes average at most 32 pairs per expert, so they run on 64-row m-tiles."""
     note(f"grouped wide mxfp4 T={T} H={H} E={E} K={K} I={I}")
     sh_ = synth.Shape(T, H, E, K, I, "bf16", "mxfp4", bias="zipf")
     li = synth.make_layer(sh_, beta=1.0)
