@@ -82,13 +82,14 @@ moe_status check_path(const moe_shape *s) {
 bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 
 // AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
-// experts, three with MXFP4 and MXINT8 and four with NVFP4 (whose streaming kernels read a
-// quarter of the bytes); measured crossovers on the decode shapes: bf16 T = 24..32 (k = 8,
-// E = 128), MXFP4 T = 64..96 (k = 8, E = 256: 661 / 701 us streaming / grouped at 64, 802 /
-// 734 at 96)
+// and MXFP4 experts, three with MXINT8 and four with NVFP4 (whose streaming kernels read a
+// quarter of the bytes); measured crossovers on the decode shapes (streaming / grouped):
+// bf16 (k = 8, E = 128) 161 / 160 us at T = 24, 190 / 182 at 32; MXFP4 (k = 8, E = 256, the
+// grouped GEMMs on 64-row m-tiles) 563 / 620 us at T = 48, 661 / 633 at 64, 744 / 640 at 80
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    const long per_expert = s.weight_dtype == MOE_BF16 ? 2L : s.weight_dtype == MOE_NVFP4 ? 4L : 3L;
+    const long per_expert =
+        (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4) ? 2L : s.weight_dtype == MOE_NVFP4 ? 4L : 3L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
            (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
 }

@@ -171,8 +171,8 @@ def test_nvfp4_validation():
     for T, grouped in ((9, False), (63, False), (64, True), (4096, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.NVFP4, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
-    # MXFP4 switches at three pairs per expert: 48 tokens at E = 128, k = 8
-    for T, grouped in ((47, False), (48, True)):
+    # MXFP4 switches at two pairs per expert: 32 tokens at E = 128, k = 8
+    for T, grouped in ((31, False), (32, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.MXFP4, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     # with fp32 activations NVFP4 is not a supported pair
