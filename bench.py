@@ -51,9 +51,9 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 _SRC_DEVICE = ("prefill_moe_router_amd/csrc/moe_device.h", "83f51350610eff16eae366237d12db13d9a245a5")
 _SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "3ddbb79b7822226fd27b12ed468ee6c1c60046d4"),
                    _SRC_DEVICE])
-_SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "78c4ad8dfb756010e68bf2d5e73142906715bcfe"),
+_SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "c7eb78ac93dcde4c73a7e9c26c4bf552fa5d66c6"),
                   _SRC_DEVICE])
-_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "863535bad865fefccb824a8391ee98169b1cf5cd"),
+_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "23ce9cdb698051b0c0581e48ad647f9f8f469b1c"),
                      _SRC_DEVICE])
 
 
@@ -63,12 +63,12 @@ def _traffic(kernel, fetch_kib, write_kib, sources):
 
 
 COUNTED_TRAFFIC = {
-    "decode1": _traffic("decode_fused", 37511.6, 240.1, _SRC_FUSED),
-    "decode8": _traffic("decode_fused", 197361.4, 1640.5, _SRC_FUSED),
-    "mxfp4_decode1": _traffic("decode_fused", 27675.2, 344.1, _SRC_FUSED),
-    "mxfp4_decode8": _traffic("decode_fused", 188486.9, 2248.5, _SRC_FUSED),
-    "prefill8192": _traffic("gate_up", 1061248.8, 98308.7, _SRC_WIDE),
-    "mxfp4_prefill4096": _traffic("gate_up", 1089014.8, 65536.0, _SRC_GROUPED),
+    "decode1": _traffic("decode_fused", 37503.6, 240.1, _SRC_FUSED),
+    "decode8": _traffic("decode_fused", 197368.9, 1640.5, _SRC_FUSED),
+    "mxfp4_decode1": _traffic("decode_fused", 27674.3, 344.1, _SRC_FUSED),
+    "mxfp4_decode8": _traffic("decode_fused", 188486.6, 2248.5, _SRC_FUSED),
+    "prefill8192": _traffic("gate_up", 1064306.2, 98308.6, _SRC_WIDE),
+    "mxfp4_prefill4096": _traffic("gate_up", 1086083.1, 65536.0, _SRC_GROUPED),
 }
 
 
