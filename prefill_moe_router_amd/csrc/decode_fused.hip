@@ -49,8 +49,10 @@ constexpr int FMAX_T = kFusedMaxTokens;
 constexpr int FMAX_P = 256;             // T * k
 constexpr int FMAX_G = kFusedMaxGroups; // work-groups (one per CU)
 constexpr int FROUNDS_MAX_K = 12;       // top-k by arg-max rounds up to this k, radix walk above
-constexpr int FRANK_MAX_E = 128;        // one token: top-k by counted ranks up to this E (measured:
-                                        // 0.7 us faster at E = 128, 0.5 us slower at E = 256)
+constexpr int FRANK_MAX_E = 128;        // one token: top-k by counted ranks over all E up to this E
+                                        // (measured: 0.7 us faster at E = 128, 0.5 us slower at E = 256)
+constexpr int FRANK2_MAX_E = FWPB * 64; // one token above that: ranks in two levels (a wave's 64
+constexpr int FRANK2_MAX_K = 8;         // experts, then at most 64 candidates) up to this E and k
 constexpr int FMAX_C = 8;               // max 16-byte chunks per lane of one row
 constexpr int FMAX_WR = 32;             // output rows of one work-group (its tiles' rows)
 constexpr size_t FLDS_MAX = 140 * 1024; // staged x / h' bytes per work-group (static LDS ~16 KB)
@@ -316,35 +318,68 @@ __global__ __launch_bounds__(FTHREADS) void decode_fused_kernel(FusedParams p) {
         poll_words(p.logits, T * E, s_tag, s_lg, t0, p.err);
     }
     __syncthreads();
-    if (T == 1 && E <= FRANK_MAX_E) {
-        // One token: every expert's rank is the number of experts that beat it (a larger
-        // logit key, or the same key and a lower id), counted with the comparison range
-        // split over all the work-group's waves; ranks 0..K-1 are the kept experts.  The
-        // same selection as the per-wave top-k below, in a few dependent steps instead of K
-        // rounds in one wave (the counting is E*E comparisons, so only for small E).  One
-        // slot per kept expert, in ascending id, is the grouping.
-        uint32_t *s_rank = s_sel;   // zeroed at kernel start
-        for (int e = tid; e < E; e += FTHREADS)
-            s_pk[e] = ((uint64_t)f32_order_key(s_lg[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-        __syncthreads();
-        const int epad = (E + WAVE - 1) / WAVE * WAVE;
-        const int nparts = epad >= FTHREADS ? 1 : FTHREADS / epad;
-        const int span = (E + nparts - 1) / nparts;
-        for (int i = tid; i < epad * nparts; i += FTHREADS) {
-            const int e = i % epad, part = i / epad;   // part is the same in the whole wave
-            const int j0 = part * span, j1 = min(E, j0 + span);
-            const uint64_t mine = e < E ? s_pk[e] : ~0ull;
-            uint32_t r = 0;
+    const bool rank1 = T == 1 && E <= FRANK_MAX_E;
+    const bool rank2 = T == 1 && !rank1 && E <= FRANK2_MAX_E && K <= FRANK2_MAX_K;
+    if (rank1 || rank2) {
+        // One token: an expert's rank is the number of experts that beat it (a larger logit
+        // key, or the same key and a lower id); ranks 0..K-1 are the kept experts.  The same
+        // selection as the per-wave top-k below, in a few dependent steps instead of K
+        // rounds in one wave.  One slot per kept expert, in ascending id, is the grouping.
+        // The key (order key << 32 | ~e) is unique per expert, and the low word gives e back.
+        if (rank1) {
+            // the E*E comparisons split over all the work-group's waves
+            uint32_t *s_rank = s_sel;   // zeroed at kernel start
+            for (int e = tid; e < E; e += FTHREADS)
+                s_pk[e] = ((uint64_t)f32_order_key(s_lg[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+            __syncthreads();
+            const int epad = (E + WAVE - 1) / WAVE * WAVE;
+            const int nparts = epad >= FTHREADS ? 1 : FTHREADS / epad;
+            const int span = (E + nparts - 1) / nparts;
+            for (int i = tid; i < epad * nparts; i += FTHREADS) {
+                const int e = i % epad, part = i / epad;   // part is the same in the whole wave
+                const int j0 = part * span, j1 = min(E, j0 + span);
+                const uint64_t mine = e < E ? s_pk[e] : ~0ull;
+                uint32_t r = 0;
 #pragma unroll 8
-            for (int j = j0; j < j1; ++j) r += s_pk[j] > mine ? 1u : 0u;
-            if (e < E) atomicAdd(s_rank + e, r);
+                for (int j = j0; j < j1; ++j) r += s_pk[j] > mine ? 1u : 0u;
+                if (e < E) atomicAdd(s_rank + e, r);
+            }
+            __syncthreads();
+            for (int e = tid; e < E; e += FTHREADS) {
+                const uint32_t r = s_rank[e];
+                if (r < (uint32_t)K) s_ids[r] = e;   // s_ids by rank
+            }
+            __syncthreads();
+        } else {
+            // Two levels.  Wave w ranks its 64 experts 64w..64w+63 among themselves and keeps
+            // those of local rank < K as candidates (slot w*K + local rank; empty slots hold
+            // key 0, below every expert's).  An expert of global rank < K has local rank < K,
+            // and every expert that beats it beats it locally too, so its rank among the
+            // candidates is its global rank; any other candidate has at least K above it.
+            uint64_t *s_cand = reinterpret_cast<uint64_t *>(s_trash);   // [FWPB * K] keys
+            const int ng = (E + WAVE - 1) / WAVE;
+            if (wave < ng) {
+                const int e = wave * WAVE + lane;
+                const uint64_t mine =
+                    e < E ? ((uint64_t)f32_order_key(s_lg[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e) : 0ull;
+                if (e < E) s_pk[e] = mine;
+                if (lane < K) s_cand[wave * K + lane] = 0ull;
+                // the wave reads back its own lanes' keys (a wave's LDS accesses complete in order)
+                const int jn = min(WAVE, E - wave * WAVE);
+                uint32_t r = 0;
+#pragma unroll 8
+                for (int j = 0; j < jn; ++j) r += s_pk[wave * WAVE + j] > mine ? 1u : 0u;
+                if (e < E && r < (uint32_t)K) s_cand[wave * K + r] = mine;
+            }
+            __syncthreads();
+            if (wave == 0) {
+                const int nc = ng * K;   // at most 64
+                const uint64_t mine = lane < nc ? s_cand[lane] : 0ull;
+                uint32_t r = 0;
+                for (int j = 0; j < nc; ++j) r += s_cand[j] > mine ? 1u : 0u;
+                if (mine != 0ull && r < (uint32_t)K) s_ids[r] = (int)(0xffffffffu - (uint32_t)mine);
+            }
         }
-        __syncthreads();
-        for (int e = tid; e < E; e += FTHREADS) {
-            const uint32_t r = s_rank[e];
-            if (r < (uint32_t)K) s_ids[r] = e;   // s_ids by rank
-        }
-        __syncthreads();
         if (wave == 0) {
             // lane j < K: the expert of rank j, its place in ascending id, its weight
             const bool on = lane < K;

@@ -418,10 +418,12 @@ def test_forward_k_and_renorm_edges(K, renorm, E, I):
 
 
 @pytest.mark.parametrize("K,renorm,E", [(1, True, 8), (8, True, 8), (3, False, 16), (32, True, 64), (8, False, 128),
-                                         (8, True, 128), (8, False, 256)])
+                                         (8, True, 128), (8, False, 256), (8, True, 256), (1, True, 256),
+                                         (8, True, 130), (5, False, 512), (9, True, 256), (16, False, 200)])
 def test_forward_single_token_k_and_renorm(K, renorm, E):
-    """One decode token: the fused kernel's one-token selection (ranks counted over the work-group,
-    E <= 128) and its per-wave top-k (E = 256), with k = 1, k = E, renorm on and off."""
+    """One decode token: the fused kernel's one-token selections -- ranks counted over all E
+    (E <= 128), ranks in two levels (E <= 512, k <= 8; E = 130 leaves its last wave two experts,
+    fewer than k) and the per-wave top-k (k = 9 and 16) -- with k = 1, k = E, renorm on and off."""
     note(f"single token K={K} renorm={renorm} E={E}")
     li = layer_of(synth.Shape(1, 256, E, K, 128, "bf16", "bf16", bias="normal", renorm=renorm), batch=3)
     got = run_forward(DevLayer(li))
@@ -429,20 +431,23 @@ def test_forward_single_token_k_and_renorm(K, renorm, E):
     compare_forward(li, got, label=f"T=1 K={K} renorm={renorm} E={E}")
 
 
-@pytest.mark.parametrize("E", [12, 200])
-def test_forward_single_token_exact_ties(E):
+@pytest.mark.parametrize("E,K,tied", [(12, 3, (2, 5, 9, 11)), (200, 3, (2, 5, 9, 11)), (200, 3, (199, 70, 5, 130)),
+                                      (200, 12, (2, 5, 9, 11))])
+def test_forward_single_token_exact_ties(E, K, tied):
     """One token whose best logits tie exactly (identical router rows): the lower ids win, in the
-    fused kernel's one-token selection (E = 12) and its per-wave top-k (E = 200)."""
-    li = layer_of(synth.Shape(1, 256, E, 3, 128, "bf16", "bf16"))
+    fused kernel's one-token selections -- ranks over all E (E = 12), ranks in two levels with the
+    tied experts in one wave's group or spread over four (E = 200, k = 3) -- and its per-wave top-k
+    (k = 12)."""
+    li = layer_of(synth.Shape(1, 256, E, K, 128, "bf16", "bf16"))
     assert pm.forward_stages(lshape(li)) == ["decode_fused"]
     row = synth.bf16_bits_to_f32(li.wr[2])
     s = float(synth.bf16_bits_to_f32(li.x[0]).astype(np.float64) @ row.astype(np.float64))
     popular = synth.f32_to_bf16_bits(row * (64.0 if s > 0 else -64.0))   # exact: a power of two
-    for e in (2, 5, 9, 11):   # four equal, largest logits for three places
+    for e in tied:   # four equal, largest logits for the first three places
         li.wr[e] = popular
     got = run_forward(DevLayer(li))
     ref = oracle.router(oracle_layer(li))
-    assert ref["ids"][0].tolist() == [2, 5, 9]
+    assert ref["ids"][0].tolist()[:3] == sorted(tied)[:3]
     np.testing.assert_array_equal(got["ids"], ref["ids"])
     np.testing.assert_allclose(got["w"], ref["w"], rtol=0, atol=W_TOL)
 
