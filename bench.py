@@ -49,11 +49,11 @@ METRIC = "MoE layer tokens/s; decode HBM GB/s % peak; prefill MFMA TFLOP/s % pea
 # of known size (FETCH_SIZE x2.0, WRITE_SIZE x1.0).  Valid only for the kernel sources
 # the counters were taken on (sha1 of the listed files); otherwise traffic is null.
 _SRC_DEVICE = ("prefill_moe_router_amd/csrc/moe_device.h", "83f51350610eff16eae366237d12db13d9a245a5")
-_SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "3ddbb79b7822226fd27b12ed468ee6c1c60046d4"),
+_SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "5143c990fbab86e0a7a9bf0c177089fa1a3ead6b"),
                    _SRC_DEVICE])
 _SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "c7eb78ac93dcde4c73a7e9c26c4bf552fa5d66c6"),
                   _SRC_DEVICE])
-_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "23ce9cdb698051b0c0581e48ad647f9f8f469b1c"),
+_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "01ed6c8d006a9491d4dc70e0fe963afb7c711d25"),
                      _SRC_DEVICE])
 
 
@@ -63,12 +63,12 @@ def _traffic(kernel, fetch_kib, write_kib, sources):
 
 
 COUNTED_TRAFFIC = {
-    "decode1": _traffic("decode_fused", 37503.6, 240.1, _SRC_FUSED),
-    "decode8": _traffic("decode_fused", 197368.9, 1640.5, _SRC_FUSED),
-    "mxfp4_decode1": _traffic("decode_fused", 27674.3, 344.1, _SRC_FUSED),
-    "mxfp4_decode8": _traffic("decode_fused", 188486.6, 2248.5, _SRC_FUSED),
-    "prefill8192": _traffic("gate_up", 1064306.2, 98308.6, _SRC_WIDE),
-    "mxfp4_prefill4096": _traffic("gate_up", 1086083.1, 65536.0, _SRC_GROUPED),
+    "decode1": _traffic("decode_fused", 37534.6, 240.1, _SRC_FUSED),
+    "decode8": _traffic("decode_fused", 197283.1, 1640.5, _SRC_FUSED),
+    "mxfp4_decode1": _traffic("decode_fused", 27653.9, 344.1, _SRC_FUSED),
+    "mxfp4_decode8": _traffic("decode_fused", 188481.5, 2248.5, _SRC_FUSED),
+    "prefill8192": _traffic("gate_up", 1060291.8, 98308.3, _SRC_WIDE),
+    "mxfp4_prefill4096": _traffic("gate_up", 1088375.6, 65536.0, _SRC_GROUPED),
 }
 
 
