@@ -29,6 +29,9 @@ namespace moe {
 constexpr int NXCD = 8;
 
 enum { GM_ROUTER = 0, GM_GATEUP = 1, GM_DOWN = 2, GM_DOWN_F32 = 3 };
+// 16-byte scale-table pieces per thread of the MXFP4 gate/up (K <= 6144 with 256 weight rows
+// and 512 threads)
+constexpr int kScaleTableChunks = 6;
 
 #ifndef MOE_GEMM_GM
 #define MOE_GEMM_GM 8   // m-tiles per ordering group of the tile order
@@ -62,7 +65,8 @@ __device__ __forceinline__ int find_expert(const int32_t *mtile_off, int E, int 
 // BM x BN output tile per matrix (NB = 2 matrices, gate and up, for GATEUP), K steps
 // of BK, WM x WN waves, each wave MI x NJ blocks of 32x32 per matrix.  LDS rows are
 // padded by 16 bytes so 16 consecutive rows read at one k offset hit distinct banks.
-template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX, bool NV = false, bool I8 = false>
+template <int MODE, int BM, int BN, int WM, int WN, int BK, int NS, bool MX, bool NV = false, bool I8 = false,
+          bool ST = false>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p) {
     constexpr int NTH = WM * WN * 64;
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
@@ -138,6 +142,19 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
     constexpr int CQ = BK / QE;                                   // code chunks per row and K step
     constexpr int BQ = MX ? NB * BN * CQ / NTH : 1;               // code chunks staged per thread
     static_assert(!MX || BQ * NTH == NB * BN * CQ, "coded-weight staging must tile the block");
+    // ST (MXFP4): the tile's E8M0 scales for the whole K ([NB*BN rows][K/32] bytes) sit in
+    // LDS after the stages, loaded once per tile in 16-byte pieces (K % 512 == 0), instead of
+    // one scale byte per thread and step from global memory (each such load touches 32 rows'
+    // cache lines).  Step kt reads the bytes of the slice it writes to LDS at its start.
+    static_assert(!ST || (MX && !NV && !I8 && MODE == GM_GATEUP), "scale table: MXFP4 gate/up");
+    const int srow = p.K / 32;               // scale bytes per weight row
+    uint8_t *const sct = lds + NS * STAGE;   // the scale table
+    int sidx[BQ];                            // this thread's row of the table, plus its chunk
+#pragma unroll
+    for (int i = 0; i < BQ; ++i) {
+        const int idx = tid + NTH * i;
+        sidx[i] = (idx / CQ) * srow + idx % CQ;
+    }
     const uint8_t *bqrow[BQ], *bqsc[BQ];
     int bqlds[BQ];
 #pragma unroll
@@ -167,8 +184,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         if constexpr (MX) {                                                                               \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
                 RQ[i] = *reinterpret_cast<const u32x4_t *>(bqrow[i] + (size_t)(kt) * (I8 ? BK : BK / 2)); \
-                RS[i] = NV ? (uint32_t) * reinterpret_cast<const uint16_t *>(bqsc[i] + (kt) * CQ * 2)      \
-                           : (uint32_t)bqsc[i][(kt) * (BK / 32)];                                          \
+                RS[i] = NV   ? (uint32_t) * reinterpret_cast<const uint16_t *>(bqsc[i] + (kt) * CQ * 2)    \
+                        : ST ? 0u                                                                         \
+                             : (uint32_t)bqsc[i][(kt) * (BK / 32)];                                        \
             }                                                                                             \
         } else {                                                                                          \
             _Pragma("unroll") for (int b = 0; b < NB; ++b)                                                \
@@ -176,7 +194,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
                     *reinterpret_cast<const u32x4_t *>(brow[b][i] + ko_);                                  \
         }                                                                                                 \
     } while (0)
-#define GG_LSTORE(RA, RB, RQ, RS, stage)                                                                  \
+#define GG_LSTORE(RA, RB, RQ, RS, SX, stage)                                                              \
     do {                                                                                                  \
         uint8_t *base_ = lds + (stage) * STAGE;                                                           \
         _Pragma("unroll") for (int i = 0; i < AR; ++i)                                                    \
@@ -214,7 +232,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
             }                                                                                             \
         } else if constexpr (MX) {                                                                        \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
-                const float s_ = e8m0_to_f32(RS[i]);                                                      \
+                const float s_ = e8m0_to_f32(ST ? SX[i] : RS[i]);                                         \
                 _Pragma("unroll") for (int w = 0; w < 4; ++w) {                                           \
                     const uint32_t cw = RQ[i][w];                                                         \
                     u32x4_t o_;                                                                           \
@@ -266,6 +284,11 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
     } while (0)
 #define GG_STEP(kt_, DIST, RA_LOAD, RB_LOAD, RQ_LOAD, RS_LOAD, RA_STORE, RB_STORE, RQ_STORE, RS_STORE)      \
     do {                                                                                                  \
+        uint32_t sx_[BQ];                                                                                 \
+        if constexpr (ST) {                                                                               \
+            _Pragma("unroll") for (int i = 0; i < BQ; ++i) sx_[i] =                                       \
+                sct[sidx[i] + min((kt_) + 1, KT - 1) * (BK / 32)];                                        \
+        }                                                                                                 \
         GG_GLOAD(RA_LOAD, RB_LOAD, RQ_LOAD, RS_LOAD, min((kt_) + (DIST), KT - 1));                        \
         const uint8_t *base = lds + ((kt_) & 1) * STAGE;                                                  \
         if constexpr (ACT) {                                                                              \
@@ -283,7 +306,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
                 if (q < AR + (MX ? 2 * BQ : NB * BR)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  \
             }                                                                                             \
         }                                                                                                 \
-        GG_LSTORE(RA_STORE, RB_STORE, RQ_STORE, RS_STORE, ((kt_) + 1) & 1);                               \
+        GG_LSTORE(RA_STORE, RB_STORE, RQ_STORE, RS_STORE, sx_, ((kt_) + 1) & 1);                          \
         __syncthreads();                                                                                  \
         if constexpr (ACT) GG_OPLOAD(0, lds + (((kt_) + 1) & 1) * STAGE, 0);                              \
     } while (0)
@@ -296,7 +319,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         constexpr bool ACT = true;
         GG_GLOAD(ra0, rb0, rq0, rs0, 0);
         GG_GLOAD(ra1, rb1, rq1, rs1, min(1, KT - 1));
-        GG_LSTORE(ra0, rb0, rq0, rs0, 0);
+        GG_LSTORE(ra0, rb0, rq0, rs0, rs0, 0);
         __syncthreads();
         GG_OPLOAD(0, lds, 0);
         for (int kt = 0; kt < KT; kt += 2) {
@@ -306,13 +329,34 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
     } else {
         auto main_loop = [&](auto act_c) __attribute__((always_inline)) {
             constexpr bool ACT = decltype(act_c)::value;
+            // the scale table's loads go first, so writing it to LDS waits for them only
+            constexpr int TC = ST ? kScaleTableChunks : 1;
+            const int tcr = srow / 16, ntc = NB * BN * tcr;
+            u32x4_t tv[TC];
+            if constexpr (ST) {
+#pragma unroll
+                for (int j = 0; j < TC; ++j) {
+                    const int q = min(tid + NTH * j, ntc - 1), r = q / tcr, b = r / BN;
+                    tv[j] = *reinterpret_cast<const u32x4_t *>((b == 0 ? p.s0 : p.s1) +
+                                                               ((size_t)e * p.N + n0 + r % BN) * srow + (q % tcr) * 16);
+                }
+            }
             GG_GLOAD(ra0, rb0, rq0, rs0, 0);
             GG_GLOAD(ra1, rb1, rq1, rs1, min(1, KT - 1));
+            uint32_t sx0[BQ];
+            if constexpr (ST) {
+#pragma unroll
+                for (int j = 0; j < TC; ++j)
+                    if (tid + NTH * j < ntc) *reinterpret_cast<u32x4_t *>(sct + (tid + NTH * j) * 16) = tv[j];
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < BQ; ++i) sx0[i] = sct[sidx[i]];
+            }
             if constexpr (MODE == GM_ROUTER) {
                 // slice s sits in register set s % 3: step kt loads slice kt + 3 into the set
                 // that slice kt left (written to LDS the step before) and writes slice kt + 1
                 GG_GLOAD(ra2, rb2, rq2, rs2, min(2, KT - 1));
-                GG_LSTORE(ra0, rb0, rq0, rs0, 0);
+                GG_LSTORE(ra0, rb0, rq0, rs0, sx0, 0);
                 __syncthreads();
                 if constexpr (ACT) GG_OPLOAD(0, lds, 0);
                 for (int kt = 0; kt < KT; kt += 3) {
@@ -321,7 +365,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
                     if (kt + 2 < KT) GG_STEP(kt + 2, 3, ra2, rb2, rq2, rs2, ra0, rb0, rq0, rs0);
                 }
             } else {
-                GG_LSTORE(ra0, rb0, rq0, rs0, 0);
+                GG_LSTORE(ra0, rb0, rq0, rs0, sx0, 0);
                 __syncthreads();
                 if constexpr (ACT) GG_OPLOAD(0, lds, 0);
                 for (int kt = 0; kt < KT; kt += 2) {
@@ -492,18 +536,34 @@ bool router_mfma_supported(const moe_shape &s) {
     return s.act_dtype == MOE_BF16 && s.num_experts % CfgR::BN == 0 && s.hidden % CfgR::BK == 0;
 }
 
-template <int MODE, class C, bool MX = false, bool NV = false, bool I8 = false>
+constexpr size_t kGemmLdsMax = 158 * 1024;
+template <int MODE, class C>
+constexpr size_t gemm_stage_bytes() {
+    return C::NS * (size_t)(C::BM + (MODE == GM_GATEUP ? 2 : 1) * C::BN) * (C::BK * 2 + 16);
+}
+// the MXFP4 gate/up's scale table fits (whole 16-byte pieces, the LDS budget, the pieces per thread)
+template <class C>
+static bool scale_table_fits(int K) {
+    const size_t rows = 2 * (size_t)C::BN;
+    return K % 512 == 0 && gemm_stage_bytes<GM_GATEUP, C>() + rows * (K / 32) <= kGemmLdsMax &&
+           rows * (K / 512) <= (size_t)kScaleTableChunks * C::WM * C::WN * 64;
+}
+
+template <int MODE, class C, bool MX = false, bool NV = false, bool I8 = false, bool ST = false>
 static hipError_t gemm_launch(GemmParams prm, hipStream_t st, hipEvent_t ev0, hipEvent_t ev1) {
     constexpr int NB = MODE == GM_GATEUP ? 2 : 1;
-    constexpr size_t stage_bytes = C::NS * (size_t)(C::BM + NB * C::BN) * (C::BK * 2 + 16);
+    constexpr size_t stage_bytes = gemm_stage_bytes<MODE, C>();
     constexpr size_t epi_bytes = (size_t)C::WM * C::WN * (C::BM / C::WM) * (C::BN / C::WN + 8) * 2;
-    constexpr size_t lds = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
-    static_assert(lds <= 158 * 1024, "LDS budget");
+    constexpr size_t lds_fixed = stage_bytes > epi_bytes ? stage_bytes : epi_bytes;
+    static_assert(lds_fixed <= kGemmLdsMax, "LDS budget");
+    const size_t lds = ST ? std::max(stage_bytes + (size_t)NB * C::BN * (prm.K / 32), epi_bytes) : lds_fixed;
+    if (lds > kGemmLdsMax) return hipErrorInvalidValue;
     static bool attr_done = false;
-    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX, NV, I8>;
+    auto kern = grouped_gemm_kernel<MODE, C::BM, C::BN, C::WM, C::WN, C::BK, C::NS, MX, NV, I8, ST>;
     if (!attr_done) {
         hipError_t r = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           (int)(ST ? kGemmLdsMax : lds_fixed));
         if (r != hipSuccess) return r;
         attr_done = true;
     }
@@ -574,7 +634,11 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
         prm.mt_max = mt_max_of(s, kWideSmallTileM);
         return gemm_launch<GM_GATEUP, CfgGU64, true>(prm, st, ev0, ev1);
     }
-    if (s.weight_dtype == MOE_MXFP4) return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXFP4) {
+        if (scale_table_fits<CfgGU>(s.hidden))
+            return gemm_launch<GM_GATEUP, CfgGU, true, false, false, true>(prm, st, ev0, ev1);
+        return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
+    }
     if (s.weight_dtype == MOE_NVFP4) return gemm_launch<GM_GATEUP, CfgGU, true, true>(prm, st, ev0, ev1);
     if (s.weight_dtype == MOE_MXINT8) return gemm_launch<GM_GATEUP, CfgGU, true, false, true>(prm, st, ev0, ev1);
     return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
