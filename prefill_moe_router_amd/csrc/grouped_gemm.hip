@@ -142,18 +142,19 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
     constexpr int CQ = BK / QE;                                   // code chunks per row and K step
     constexpr int BQ = MX ? NB * BN * CQ / NTH : 1;               // code chunks staged per thread
     static_assert(!MX || BQ * NTH == NB * BN * CQ, "coded-weight staging must tile the block");
-    // ST (MXFP4): the tile's E8M0 scales for the whole K ([NB*BN rows][K/32] bytes) sit in
-    // LDS after the stages, loaded once per tile in 16-byte pieces (K % 512 == 0), instead of
-    // one scale byte per thread and step from global memory (each such load touches 32 rows'
-    // cache lines).  Step kt reads the bytes of the slice it writes to LDS at its start.
-    static_assert(!ST || (MX && !NV && !I8 && MODE == GM_GATEUP), "scale table: MXFP4 gate/up");
+    // ST (MXFP4, MXINT8): the tile's E8M0 scales for the whole K ([NB*BN rows][K/32] bytes)
+    // sit in LDS after the stages, loaded once per tile in 16-byte pieces (K % 512 == 0),
+    // instead of one scale byte per thread and step from global memory (each such load
+    // touches 32 rows' cache lines).  Step kt reads the bytes of the slice it writes to LDS
+    // at its start.
+    static_assert(!ST || (MX && !NV && (MODE == GM_GATEUP || MODE == GM_DOWN)), "scale table: E8M0 scales");
     const int srow = p.K / 32;               // scale bytes per weight row
     uint8_t *const sct = lds + NS * STAGE;   // the scale table
     int sidx[BQ];                            // this thread's row of the table, plus its chunk
 #pragma unroll
     for (int i = 0; i < BQ; ++i) {
         const int idx = tid + NTH * i;
-        sidx[i] = (idx / CQ) * srow + idx % CQ;
+        sidx[i] = (idx / CQ) * srow + (I8 ? idx % CQ / 2 : idx % CQ);   // MXINT8: two chunks a block
     }
     const uint8_t *bqrow[BQ], *bqsc[BQ];
     int bqlds[BQ];
@@ -220,7 +221,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmParams p
         } else if constexpr (I8) {                                                                        \
             /* MXINT8: each code times the block's power of two (exact in bf16) */                        \
             _Pragma("unroll") for (int i = 0; i < BQ; ++i) {                                              \
-                const float s_ = mxint8_scale(RS[i]);                                                     \
+                const float s_ = mxint8_scale(ST ? SX[i] : RS[i]);                                        \
                 _Pragma("unroll") for (int w = 0; w < 2; ++w) {                                           \
                     u32x4_t o_;                                                                           \
                     o_[0] = i8x2_to_bf16x2<0>(RQ[i][2 * w], s_);                                          \
@@ -541,11 +542,11 @@ template <int MODE, class C>
 constexpr size_t gemm_stage_bytes() {
     return C::NS * (size_t)(C::BM + (MODE == GM_GATEUP ? 2 : 1) * C::BN) * (C::BK * 2 + 16);
 }
-// the MXFP4 gate/up's scale table fits (whole 16-byte pieces, the LDS budget, the pieces per thread)
-template <class C>
+// an E8M0 scale table fits (whole 16-byte pieces, the LDS budget, the pieces per thread)
+template <int MODE, class C>
 static bool scale_table_fits(int K) {
-    const size_t rows = 2 * (size_t)C::BN;
-    return K % 512 == 0 && gemm_stage_bytes<GM_GATEUP, C>() + rows * (K / 32) <= kGemmLdsMax &&
+    const size_t rows = (MODE == GM_GATEUP ? 2 : 1) * (size_t)C::BN;
+    return K % 512 == 0 && gemm_stage_bytes<MODE, C>() + rows * (K / 32) <= kGemmLdsMax &&
            rows * (K / 512) <= (size_t)kScaleTableChunks * C::WM * C::WN * 64;
 }
 
@@ -632,15 +633,21 @@ hipError_t launch_gateup_mfma(const moe_shape &s, const void *x, const moe_exper
     prm.nt = s.intermediate / CfgGU::BN;
     if (s.weight_dtype == MOE_MXFP4 && grouped_tile_rows(s) == kWideSmallTileM) {
         prm.mt_max = mt_max_of(s, kWideSmallTileM);
+        if (scale_table_fits<GM_GATEUP, CfgGU64>(s.hidden))
+            return gemm_launch<GM_GATEUP, CfgGU64, true, false, false, true>(prm, st, ev0, ev1);
         return gemm_launch<GM_GATEUP, CfgGU64, true>(prm, st, ev0, ev1);
     }
     if (s.weight_dtype == MOE_MXFP4) {
-        if (scale_table_fits<CfgGU>(s.hidden))
+        if (scale_table_fits<GM_GATEUP, CfgGU>(s.hidden))
             return gemm_launch<GM_GATEUP, CfgGU, true, false, false, true>(prm, st, ev0, ev1);
         return gemm_launch<GM_GATEUP, CfgGU, true>(prm, st, ev0, ev1);
     }
     if (s.weight_dtype == MOE_NVFP4) return gemm_launch<GM_GATEUP, CfgGU, true, true>(prm, st, ev0, ev1);
-    if (s.weight_dtype == MOE_MXINT8) return gemm_launch<GM_GATEUP, CfgGU, true, false, true>(prm, st, ev0, ev1);
+    if (s.weight_dtype == MOE_MXINT8) {
+        if (scale_table_fits<GM_GATEUP, CfgGU>(s.hidden))
+            return gemm_launch<GM_GATEUP, CfgGU, true, false, true, true>(prm, st, ev0, ev1);
+        return gemm_launch<GM_GATEUP, CfgGU, true, false, true>(prm, st, ev0, ev1);
+    }
     return gemm_launch<GM_GATEUP, CfgGU>(prm, st, ev0, ev1);
 }
 
@@ -670,8 +677,12 @@ hipError_t launch_down_mfma(const moe_shape &s, const moe_expert_weights &w, con
                          : mx ? gemm_launch<GM_DOWN_F32, CfgDN, true>(prm, st, ev0, ev1)
                               : gemm_launch<GM_DOWN_F32, CfgDN>(prm, st, ev0, ev1);
     if (nv) return gemm_launch<GM_DOWN, CfgDN, true, true>(prm, st, ev0, ev1);
-    if (i8) return gemm_launch<GM_DOWN, CfgDN, true, false, true>(prm, st, ev0, ev1);
-    return mx ? gemm_launch<GM_DOWN, CfgDN, true>(prm, st, ev0, ev1) : gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
+    const bool table = scale_table_fits<GM_DOWN, CfgDN>(s.intermediate);
+    if (i8) return table ? gemm_launch<GM_DOWN, CfgDN, true, false, true, true>(prm, st, ev0, ev1)
+                         : gemm_launch<GM_DOWN, CfgDN, true, false, true>(prm, st, ev0, ev1);
+    if (mx) return table ? gemm_launch<GM_DOWN, CfgDN, true, false, false, true>(prm, st, ev0, ev1)
+                         : gemm_launch<GM_DOWN, CfgDN, true>(prm, st, ev0, ev1);
+    return gemm_launch<GM_DOWN, CfgDN>(prm, st, ev0, ev1);
 }
 
 hipError_t launch_combine_rows(const moe_shape &s, const void *o, void *y, hipStream_t st) {
