@@ -72,8 +72,8 @@ enum {
 enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2, MOE_NVFP4 = 3, MOE_MXINT8 = 4 };
 
 /* expert-FFN kernel family; AUTO picks DECODE for T <= 8 and while T * top_k < 2 * E (bf16
-   and MXFP4 experts), < 3 * E (MXINT8) or < 4 * E (NVFP4), GROUPED above (bf16, MXFP4, NVFP4
-   and MXINT8 experts with bf16 activations) */
+   experts), < 1.5 * E (MXFP4), < 1.25 * E (MXINT8) or < 4 * E (NVFP4), GROUPED above (bf16,
+   MXFP4, NVFP4 and MXINT8 experts with bf16 activations) */
 enum { MOE_PATH_AUTO = 0, MOE_PATH_DECODE = 1, MOE_PATH_GROUPED = 2 };
 
 /* device error bits reported by moe_check_device_error */

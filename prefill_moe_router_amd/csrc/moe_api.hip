@@ -81,17 +81,20 @@ moe_status check_path(const moe_shape *s) {
 // work-group per 32 tokens leaves most of the chip idle.
 bool fused_router(const moe_shape &s) { return router_topk_mfma_supported(s); }
 
-// AUTO: the grouped GEMMs from two (token, expert) pairs per expert on average with bf16
-// and MXFP4 experts, three with MXINT8 and four with NVFP4 (whose streaming kernels read a
+// AUTO: the grouped GEMMs from 2 (token, expert) pairs per expert on average with bf16
+// experts, 1.5 with MXFP4, 1.25 with MXINT8 and 4 with NVFP4 (whose streaming kernels read a
 // quarter of the bytes); measured crossovers on the decode shapes (streaming / grouped):
-// bf16 (k = 8, E = 128) 161 / 160 us at T = 24, 190 / 182 at 32; MXFP4 (k = 8, E = 256, the
-// grouped GEMMs on 64-row m-tiles) 563 / 620 us at T = 48, 661 / 633 at 64, 744 / 640 at 80
+// bf16 (k = 8, E = 128) 161 / 160 us at T = 24, 190 / 182 at 32; MXFP4 (k = 8, E = 256)
+// 513 / 520 us at T = 40, 564 / 533 at 48, 660 / 546 at 64; MXINT8 (same shape) 842 / 943 us
+// at T = 32, 1094 / 952 at 48, 1282 / 958 at 64
 bool use_grouped(const moe_shape &s) {
     if (s.path == MOE_PATH_GROUPED) return true;
-    const long per_expert =
-        (s.weight_dtype == MOE_BF16 || s.weight_dtype == MOE_MXFP4) ? 2L : s.weight_dtype == MOE_NVFP4 ? 4L : 3L;
+    const long quarters = s.weight_dtype == MOE_BF16     ? 8L    // pairs per expert x 4
+                          : s.weight_dtype == MOE_MXFP4  ? 6L
+                          : s.weight_dtype == MOE_MXINT8 ? 5L
+                                                         : 16L;
     return s.path == MOE_PATH_AUTO && s.num_tokens > 8 &&
-           (long)s.num_tokens * s.top_k >= per_expert * s.num_experts && grouped_supported(s);
+           4L * s.num_tokens * s.top_k >= quarters * s.num_experts && grouped_supported(s);
 }
 
 template <class T>

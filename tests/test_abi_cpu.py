@@ -156,7 +156,7 @@ def test_noalloc_refuses_shapes_beyond_its_scratch_before_any_device_call():
 
 def test_nvfp4_validation():
     """NVFP4 experts: scale arrays required and 16-byte aligned, finite tensor scales; AUTO
-    takes the grouped GEMMs from four pairs per expert (MXFP4: three)."""
+    takes the grouped GEMMs from four pairs per expert (MXFP4: 1.5)."""
     L = pm.lib()
     shp = _shape(weight_dtype=pm.NVFP4)
     s = shp.c()
@@ -171,8 +171,8 @@ def test_nvfp4_validation():
     for T, grouped in ((9, False), (63, False), (64, True), (4096, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.NVFP4, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
-    # MXFP4 switches at two pairs per expert: 32 tokens at E = 128, k = 8
-    for T, grouped in ((31, False), (32, True)):
+    # MXFP4 switches at 1.5 pairs per expert: 24 tokens at E = 128, k = 8
+    for T, grouped in ((23, False), (24, True)):
         stages = pm.forward_stages(_shape(weight_dtype=pm.MXFP4, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     # with fp32 activations NVFP4 is not a supported pair
@@ -181,7 +181,7 @@ def test_nvfp4_validation():
 
 def test_mxint8_validation():
     """MXINT8 experts: bf16 activations only, H and I multiples of the 32-element scale
-    block, scale arrays required; AUTO takes the grouped GEMMs from three pairs per expert."""
+    block, scale arrays required; AUTO takes the grouped GEMMs from 1.25 pairs per expert."""
     assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8)) > 0
     assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8, hidden=2048 + 16)) == 0
     assert pm.workspace_size(_shape(weight_dtype=pm.MXINT8, intermediate=768 + 8)) == 0
@@ -192,7 +192,7 @@ def test_mxint8_validation():
     w = pm.ExpertWeights(FAKE, FAKE, FAKE, None, FAKE, FAKE)
     assert L.moe_forward(ctypes.byref(s), FAKE, FAKE, None, ctypes.byref(w), FAKE, None, None, FAKE,
                          pm.workspace_size(shp), None) == pm.ERR_INVALID_ARG
-    for T, grouped in ((47, False), (48, True)):
+    for T, grouped in ((19, False), (20, True)):   # 1.25 pairs per expert at E = 128, k = 8
         stages = pm.forward_stages(_shape(weight_dtype=pm.MXINT8, num_tokens=T))
         assert ("router_topk" in stages) == grouped and "gate_up" in stages, (T, stages)
     assert pm.forward_stages(_shape(weight_dtype=pm.MXINT8, num_tokens=8, hidden=4096, num_experts=256,
