@@ -53,7 +53,7 @@ _SRC_FUSED = dict([("prefill_moe_router_amd/csrc/decode_fused.hip", "5143c990fba
                    _SRC_DEVICE])
 _SRC_WIDE = dict([("prefill_moe_router_amd/csrc/grouped_gemm_wide.hip", "c7eb78ac93dcde4c73a7e9c26c4bf552fa5d66c6"),
                   _SRC_DEVICE])
-_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "01ed6c8d006a9491d4dc70e0fe963afb7c711d25"),
+_SRC_GROUPED = dict([("prefill_moe_router_amd/csrc/grouped_gemm.hip", "0d538576ed40adb102c1759b5c9614421265dea6"),
                      _SRC_DEVICE])
 
 
@@ -63,12 +63,12 @@ def _traffic(kernel, fetch_kib, write_kib, sources):
 
 
 COUNTED_TRAFFIC = {
-    "decode1": _traffic("decode_fused", 37534.6, 240.1, _SRC_FUSED),
-    "decode8": _traffic("decode_fused", 197283.1, 1640.5, _SRC_FUSED),
+    "decode1": _traffic("decode_fused", 37527.0, 240.1, _SRC_FUSED),
+    "decode8": _traffic("decode_fused", 197231.2, 1640.5, _SRC_FUSED),
     "mxfp4_decode1": _traffic("decode_fused", 27653.9, 344.1, _SRC_FUSED),
-    "mxfp4_decode8": _traffic("decode_fused", 188481.5, 2248.5, _SRC_FUSED),
-    "prefill8192": _traffic("gate_up", 1060291.8, 98308.3, _SRC_WIDE),
-    "mxfp4_prefill4096": _traffic("gate_up", 1088375.6, 65536.0, _SRC_GROUPED),
+    "mxfp4_decode8": _traffic("decode_fused", 188483.6, 2248.5, _SRC_FUSED),
+    "prefill8192": _traffic("gate_up", 1062886.1, 98309.1, _SRC_WIDE),
+    "mxfp4_prefill4096": _traffic("gate_up", 993020.4, 65536.0, _SRC_GROUPED),
 }
 
 
