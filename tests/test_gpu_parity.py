@@ -389,10 +389,13 @@ def test_forward_mxint8_streaming(T, path):
 
 @pytest.mark.parametrize("T,H,E,K,I,path", [(130, 1024, 32, 4, 256, pm.PATH_GROUPED),
                                             (333, 512, 16, 6, 512, pm.PATH_GROUPED),
+                                            (150, 1280, 16, 4, 768, pm.PATH_GROUPED),
                                             (512, 4096, 256, 8, 1024, pm.PATH_AUTO)])
 def test_forward_mxint8_grouped(T, H, E, K, I, path):
     """MXINT8 on the grouped MFMA GEMMs (codes dequantised into LDS with the block's power
-    of two): ragged m-tiles, skewed groups, and AUTO's choice at 512 tokens."""
+    of two): ragged m-tiles, skewed groups, and AUTO's choice at 512 tokens.  H and I that
+    are multiples of 512 take the tile's scales from an LDS table; H = 1280 and I = 256 or
+    768 load them step by step."""
     note(f"mxint8 grouped T={T} H={H} E={E}")
     li = layer_of(synth.Shape(T, H, E, K, I, "bf16", "mxint8", bias="zipf" if T == 333 else "normal"), seed=11)
     sh = lshape(li, path)
